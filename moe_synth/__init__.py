@@ -1,0 +1,316 @@
+"""Seeded synthetic inputs for the MoE FFN layer, shared by the tests, the bench
+and the oracle checks.
+
+This module holds input generation only: counter-based random numbers, the
+workload shapes, and the routing tables the workloads prescribe.  It contains
+none of the layer's arithmetic (no routing scores, no sorting, no FFN), so it
+can feed both the HIP library and the CPU oracle without coupling them.
+
+Random numbers
+--------------
+Every value is a function of (seed, tag, block, index) only, so a tensor, or
+any slab of it, can be regenerated on the host or on a GPU with identical
+bits.  The 32-bit hash is a Weyl step followed by two rounds of the MurmurHash3
+32-bit finaliser ("fmix32", Austin Appleby, public domain):
+
+    h = fmix32(fmix32(index * 0x9E3779B1 + k1) ^ k2)          (mod 2^32)
+
+where k1, k2 are derived from (seed, tag, block, stream) on the host.  All
+arithmetic is exact integer arithmetic on int64 tensors (products are split so
+they never exceed 2^49), so CPU and GPU agree bit for bit.
+
+* uniform U(a,b): u = (h >> 8) * 2^-24 in [0,1), then a + (b - a) * u in fp32.
+* normal N(0, sigma): Irwin-Hall sum of four 16-bit uniforms taken from two
+  hashes (streams 0 and 1): z = (S - 131070) * sqrt(3)/65536, i.e. mean 0,
+  variance 1, bounded at +-3.46; the integer S - 131070 is exact in fp32 and
+  the scaling is one fp32 multiply by fp32(sigma * sqrt(3) / 65536).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+M32 = 0xFFFFFFFF
+_PHI = 0x9E3779B1
+_C1, _C2 = 0x85EBCA6B, 0xC2B2AE35
+
+# tags: one per input tensor
+TAG_X, TAG_W13, TAG_W2, TAG_WR, TAG_BIAS, TAG_IDS, TAG_LOGIT_NOISE, TAG_PERM = 1, 2, 3, 4, 5, 6, 7, 8
+
+
+# ------------------------------------------------------------------ hashing --
+def _fmix32_int(h: int) -> int:
+    h &= M32
+    h ^= h >> 16
+    h = (h * _C1) & M32
+    h ^= h >> 13
+    h = (h * _C2) & M32
+    h ^= h >> 16
+    return h
+
+
+def _mul32(x: torch.Tensor, c: int) -> torch.Tensor:
+    """(x * c) mod 2^32 for int64 x in [0, 2^32) without exceeding 2^49."""
+    lo = x * (c & 0xFFFF)
+    hi = torch.bitwise_and(x * (c >> 16), 0xFFFF)
+    return torch.bitwise_and(lo + torch.bitwise_left_shift(hi, 16), M32)
+
+
+def _fmix32(h: torch.Tensor) -> torch.Tensor:
+    h = torch.bitwise_xor(h, torch.bitwise_right_shift(h, 16))
+    h = _mul32(h, _C1)
+    h = torch.bitwise_xor(h, torch.bitwise_right_shift(h, 13))
+    h = _mul32(h, _C2)
+    h = torch.bitwise_xor(h, torch.bitwise_right_shift(h, 16))
+    return h
+
+
+def _keys(seed: int, tag: int, block: int, stream: int):
+    k = _fmix32_int(_fmix32_int(seed * 0x27D4EB2F + 0x165667B1) ^ (tag * 0x9E3779B1))
+    k = _fmix32_int(k ^ (block * 0x85EBCA77 & M32))
+    k1 = _fmix32_int(k ^ (stream + 1) * 0xC2B2AE3D)
+    k2 = _fmix32_int(k1 ^ 0x27D4EB2F)
+    return k1, k2
+
+
+def hash_u32(seed: int, tag: int, block: int, start: int, n: int, device="cpu", stream: int = 0):
+    """u32 hashes of counters start..start+n-1 (int64 tensor, values in [0, 2^32))."""
+    if start < 0 or start + n > (1 << 32):
+        raise ValueError("counter range must stay inside [0, 2^32)")
+    k1, k2 = _keys(seed, tag, block, stream)
+    idx = torch.arange(start, start + n, dtype=torch.int64, device=device)
+    h = torch.bitwise_and(_mul32(idx, _PHI) + k1, M32)
+    h = _fmix32(h)
+    h = torch.bitwise_xor(h, k2)
+    return _fmix32(h)
+
+
+def hash_u32_reference(seed: int, tag: int, block: int, i: int, stream: int = 0) -> int:
+    """Pure-Python form of hash_u32 for one counter (used to pin the tensor version)."""
+    k1, k2 = _keys(seed, tag, block, stream)
+    return _fmix32_int(_fmix32_int((i * _PHI + k1) & M32) ^ k2)
+
+
+# ------------------------------------------------------------ distributions --
+def _normal_flat(seed, tag, block, start, n, sigma, device):
+    h0 = hash_u32(seed, tag, block, start, n, device, stream=0)
+    h1 = hash_u32(seed, tag, block, start, n, device, stream=1)
+    s = (torch.bitwise_and(h0, 0xFFFF) + torch.bitwise_right_shift(h0, 16)
+         + torch.bitwise_and(h1, 0xFFFF) + torch.bitwise_right_shift(h1, 16))
+    del h0, h1
+    z = (s - 131070).to(torch.float32)
+    c = torch.tensor(float(np.float32(sigma * math.sqrt(3.0) / 65536.0)), dtype=torch.float32,
+                     device=device)
+    return z * c
+
+
+def _uniform_flat(seed, tag, block, start, n, lo, hi, device):
+    h = hash_u32(seed, tag, block, start, n, device)
+    u = torch.bitwise_right_shift(h, 8).to(torch.float32) * (2.0 ** -24)
+    lo_t = torch.tensor(lo, dtype=torch.float32, device=device)
+    span = torch.tensor(float(np.float32(hi) - np.float32(lo)), dtype=torch.float32, device=device)
+    return lo_t + span * u
+
+
+_CHUNK = 1 << 25
+
+
+def normal(seed, tag, shape, sigma, device="cpu", dtype=torch.float32, blocked=False):
+    """N(0, sigma) approximation (see module doc) of the given shape.
+
+    blocked=True keys the counter by the leading index (one block per expert
+    slab), so any slab can be regenerated alone with ``normal_slab``.
+    """
+    shape = tuple(int(s) for s in shape)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    if blocked:
+        for b in range(shape[0]):
+            out[b].copy_(normal_slab(seed, tag, b, shape[1:], sigma, device, dtype))
+        return out
+    flat = out.view(-1)
+    n = flat.numel()
+    for s0 in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s0)
+        flat[s0:s0 + m] = _normal_flat(seed, tag, 0, s0, m, sigma, device).to(dtype)
+    return out
+
+
+def normal_slab(seed, tag, block, shape, sigma, device="cpu", dtype=torch.float32):
+    shape = tuple(int(s) for s in shape)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s0 in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s0)
+        flat[s0:s0 + m] = _normal_flat(seed, tag, block, s0, m, sigma, device).to(dtype)
+    return out
+
+
+def uniform(seed, tag, shape, lo, hi, device="cpu"):
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape)) if shape else 1
+    return _uniform_flat(seed, tag, 0, 0, n, lo, hi, device).view(shape)
+
+
+def permutation(seed, tag, n) -> np.ndarray:
+    """A seeded permutation of range(n): the stable argsort of n hashes."""
+    h = hash_u32(seed, tag, 0, 0, n).numpy()
+    return np.argsort(h, kind="stable").astype(np.int64)
+
+
+def zipf_topk_ids(seed, tag, T, K, E, s, chunk=65536) -> np.ndarray:
+    """[T,K] int32 expert ids, K distinct per token, drawn one after another
+    without replacement from Zipf(s) over ranks 1..E (p ∝ r^-s) by the inverse
+    CDF of the remaining mass (host double); rank r maps to expert perm[r-1]
+    through a seeded permutation."""
+    perm = permutation(seed, TAG_PERM + 100 * tag, E)
+    p = np.arange(1, E + 1, dtype=np.float64) ** (-float(s))
+    out = np.empty((T, K), np.int32)
+    for t0 in range(0, T, chunk):
+        tn = min(chunk, T - t0)
+        u = hash_u32(seed, tag, 0, t0 * K, tn * K).numpy().astype(np.float64) * 2.0 ** -32
+        u = u.reshape(tn, K)
+        W = np.broadcast_to(p, (tn, E)).copy()
+        for k in range(K):
+            cs = np.cumsum(W, axis=1)
+            target = u[:, k] * cs[:, -1]
+            r = (cs <= target[:, None]).sum(axis=1)
+            r = np.minimum(r, E - 1)
+            # never land on a rank already taken (zero mass): step to the next live one
+            dead = W[np.arange(tn), r] == 0.0
+            while dead.any():
+                r[dead] = (r[dead] + 1) % E
+                dead = W[np.arange(tn), r] == 0.0
+            W[np.arange(tn), r] = 0.0
+            out[t0:t0 + tn, k] = perm[r]
+    return out
+
+
+# ------------------------------------------------------------------ codecs --
+def to_bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 numpy bit patterns (host)."""
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def to_e4m3_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+
+
+# ----------------------------------------------------------------- configs --
+CONFIGS = {
+    # Tiny MoE FFN in fp32, softmax top-2 renormalised, router logits from W_r.
+    "tiny_fp32": dict(T=64, H=128, I=256, E=8, K=2, dtype="f32", score="softmax", bias=False,
+                      n_group=1, topk_group=1, renormalize=True, routing="router", B=16),
+    # Align & Sort alone: 16384 tokens x top-8 of 256 experts, Zipf(1.1), no repeats.
+    "align_16k": dict(T=16384, K=8, E=256, B=64, zipf_s=1.1),
+    # DeepSeek-V3-shaped decode in bf16: sigmoid + bias, 8 groups keep 4, top-8 of 256.
+    "decode_bf16": dict(T=64, H=7168, I=2048, E=256, K=8, dtype="bf16", score="sigmoid", bias=True,
+                        n_group=8, topk_group=4, renormalize=True, routing="router", B=16),
+    # One-GPU expert-parallel prefill share in bf16: 2048 tokens, 64 per local expert.
+    "prefill_bf16": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="bf16", score="softmax",
+                         bias=False, n_group=1, topk_group=1, renormalize=False,
+                         routing="uniform", B=64),
+    # The a8w8 variant: Zipf(1.2) over 32 experts plus one always-on shared expert.
+    "prefill_fp8": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e4m3", score="softmax",
+                        bias=False, n_group=1, topk_group=1, renormalize=False,
+                        routing="zipf", zipf_s=1.2, shared=True, B=64),
+}
+
+ROUTER_SIGMA = 0.02
+WEIGHT_SIGMA = 0.02
+ASSIGN_MARGIN = 8.0
+
+
+def assigned_experts(cfg, seed=0) -> np.ndarray:
+    """For routing 'uniform' / 'zipf': the expert each token must route to."""
+    T, E = cfg["T"], cfg["E"]
+    if cfg["routing"] == "uniform":
+        perm = permutation(seed, TAG_PERM, T)
+        a = np.empty(T, np.int64)
+        a[perm] = (np.arange(T) * E) // T          # token perm[j] -> expert floor(j*E/T)
+        return a
+    if cfg["routing"] == "zipf":
+        return zipf_topk_ids(seed, TAG_IDS, T, 1, E, cfg["zipf_s"])[:, 0].astype(np.int64)
+    raise ValueError(cfg["routing"])
+
+
+def make_layer(cfg, device="cpu", seed=0, weights=True):
+    """All inputs of one MoE layer for a config dict (see CONFIGS).
+
+    Returns a dict of torch tensors on ``device``:
+      x [T,H] (f32 or bf16), logits [T,E] f32, bias [E] f32 or None,
+      w13 [Ew,2I,H], w2 [Ew,H,I] (f32, bf16, or float8_e4m3fn with fp32
+      per-row scales w13_scale [Ew,2I], w2_scale [Ew,H]); Ew = E (+1 shared).
+    Router logits for routing='router' are the caller's projection x.W_r^T,
+    formed on the host in double from the exact x and W_r values and rounded
+    to fp32.  For 'uniform' / 'zipf' they are N(0,1) noise plus a margin of 8
+    on the prescribed expert, which makes that expert the top-1 choice.
+    """
+    T, H, I, E = cfg["T"], cfg["H"], cfg["I"], cfg["E"]
+    Ew = E + (1 if cfg.get("shared") else 0)
+    dt = cfg["dtype"]
+    out = {}
+    xdt = torch.float32 if dt == "f32" else torch.bfloat16
+    x = normal(seed, TAG_X, (T, H), 1.0, device, xdt)
+    out["x"] = x
+    if cfg["routing"] == "router":
+        wr = normal(seed, TAG_WR, (E, H), ROUTER_SIGMA, "cpu", torch.float32)
+        xd = x.to("cpu").to(torch.float64)
+        logits = (xd @ wr.to(torch.float64).T).to(torch.float32)
+    else:
+        a = assigned_experts(cfg, seed)
+        logits = normal(seed, TAG_LOGIT_NOISE, (T, E), 1.0, "cpu", torch.float32)
+        logits[torch.arange(T), torch.from_numpy(a)] += ASSIGN_MARGIN
+    out["logits"] = logits.to(device)
+    out["bias"] = uniform(seed, TAG_BIAS, (E,), -0.1, 0.1, device) if cfg.get("bias") else None
+    if weights:
+        out.update(make_weights(cfg, device, seed))
+    return out
+
+
+def make_weights(cfg, device="cpu", seed=0, experts=None):
+    """Expert weights; ``experts`` (a list of slab indices) generates only those slabs."""
+    H, I, E = cfg["H"], cfg["I"], cfg["E"]
+    Ew = E + (1 if cfg.get("shared") else 0)
+    sel = list(range(Ew)) if experts is None else list(experts)
+    dt = cfg["dtype"]
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}[dt]
+    w13 = torch.empty((len(sel), 2 * I, H), dtype=wdt, device=device)
+    w2 = torch.empty((len(sel), H, I), dtype=wdt, device=device)
+    res = {"w13": w13, "w2": w2}
+    if dt == "e4m3":
+        res["w13_scale"] = torch.empty((len(sel), 2 * I), dtype=torch.float32, device=device)
+        res["w2_scale"] = torch.empty((len(sel), H), dtype=torch.float32, device=device)
+    for n, e in enumerate(sel):
+        a = normal_slab(seed, TAG_W13, e, (2 * I, H), WEIGHT_SIGMA, device)
+        b = normal_slab(seed, TAG_W2, e, (H, I), WEIGHT_SIGMA, device)
+        if dt == "e4m3":
+            for src, dst, sc in ((a, w13, "w13_scale"), (b, w2, "w2_scale")):
+                q, s = _quantise_rows_e4m3_input(src)
+                dst[n].copy_(q)
+                res[sc][n].copy_(s)
+        else:
+            w13[n].copy_(a.to(wdt))
+            w2[n].copy_(b.to(wdt))
+        del a, b
+    return res
+
+
+def _quantise_rows_e4m3_input(w: torch.Tensor):
+    """Input preparation for the fp8 workload's weights: per output row, scale =
+    amax/448 and codes = torch's own fp32 -> float8_e4m3fn cast of w * (448/amax).
+    (The library receives the weights already in this form.)"""
+    amax = w.abs().amax(dim=1)
+    amax = torch.where(amax > 0, amax, torch.ones_like(amax))
+    inv = torch.tensor(448.0, dtype=torch.float32, device=w.device) / amax
+    q = (w * inv[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q, amax / 448.0
+
+
+def scaled(cfg_name, **over):
+    """A copy of a named config with some sizes overridden (for small tests)."""
+    c = dict(CONFIGS[cfg_name])
+    c.update(over)
+    return c

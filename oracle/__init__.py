@@ -1,0 +1,245 @@
+"""CPU oracle for the single-GPU MoE FFN layer.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only code allowed to import this
+package.  The product library (``routing_align_sort_amd``) never imports it and
+shares no code with it: the arithmetic lives in ``moe_oracle.c`` (plain C,
+double precision), which this module compiles with gcc and calls through
+ctypes.  Everything here is argument marshalling between numpy arrays and that
+C code.
+
+Each function names the passage of the pages it follows in ``moe_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+SCORE_SOFTMAX = 0
+SCORE_SIGMOID = 1
+W_F32, W_BF16, W_E4M3 = 0, 1, 2
+X_F32, X_BF16 = 0, 1
+INTER_F64, INTER_F32, INTER_BF16, INTER_E4M3 = 0, 1, 2, 3
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c into libmoe_oracle.so (gcc, OpenMP, no FMA contraction)."""
+    global _lib
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+           "-Wall", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_bf16_encode_array.argtypes = [P, i64, P]
+    lib.oracle_bf16_decode_array.argtypes = [P, i64, P]
+    lib.oracle_e4m3_encode_array.argtypes = [P, i64, P]
+    lib.oracle_e4m3_decode_array.argtypes = [P, i64, P]
+    for f in (lib.oracle_bf16_encode_array, lib.oracle_bf16_decode_array,
+              lib.oracle_e4m3_encode_array, lib.oracle_e4m3_decode_array):
+        f.restype = None
+    lib.oracle_route_topk.argtypes = [i32, i32, i32, i32, i32, i32, i32, f64, i32, P, P, P, P]
+    lib.oracle_route_topk.restype = i32
+    lib.oracle_align_capacity.argtypes = [i64, i64, i64]
+    lib.oracle_align_capacity.restype = i64
+    lib.oracle_align_sort.argtypes = [P, i32, i32, i32, i32, P, P, P, P]
+    lib.oracle_align_sort.restype = i32
+    lib.oracle_quant_tokens_e4m3.argtypes = [P, i32, i32, P, P]
+    lib.oracle_quant_tokens_e4m3.restype = None
+    lib.oracle_quant_row_e4m3.argtypes = [P, i64, P, P]
+    lib.oracle_quant_row_e4m3.restype = None
+    lib.oracle_expert_ffn.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
+                                      P, P, P, P, P, P, P]
+    lib.oracle_expert_ffn.restype = i32
+    lib.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
+    lib.oracle_combine.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---------------------------------------------------------------- codecs ----
+def bf16_encode(v) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint16)
+    _load().oracle_bf16_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def bf16_decode(b) -> np.ndarray:
+    b = _c(b, np.uint16)
+    out = np.empty(b.shape, np.float64)
+    _load().oracle_bf16_decode_array(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """fp32 -> OCP E4M3 codes (uint8), nearest even, saturating at +-448."""
+    v = _c(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_e4m3_encode_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(c) -> np.ndarray:
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------- routing ----
+def route_topk(logits, K, *, score="softmax", bias=None, n_group=1, topk_group=1,
+               renormalize=True, routed_scaling=1.0, append_shared=False):
+    """Top-K routing of each token (row of ``logits``); returns (ids, weights).
+
+    ids int32 [T, K(+1)], weights float32 [T, K(+1)]; see moe_oracle.c.
+    """
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    b = None if bias is None else _c(bias, np.float32)
+    KO = K + (1 if append_shared else 0)
+    ids = np.empty((T, KO), np.int32)
+    w = np.empty((T, KO), np.float32)
+    mode = {"softmax": SCORE_SOFTMAX, "sigmoid": SCORE_SIGMOID}[score]
+    rc = _load().oracle_route_topk(T, E, K, mode, n_group, topk_group, int(bool(renormalize)),
+                                   float(routed_scaling), int(bool(append_shared)),
+                                   _ptr(logits), _ptr(b), _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_route_topk: invalid arguments")
+    return ids, w
+
+
+# ----------------------------------------------------------- align&sort ----
+def align_capacity(S: int, E: int, B: int) -> int:
+    return int(_load().oracle_align_capacity(S, E, B))
+
+
+def align_sort(topk_ids, E: int, B: int):
+    """Stable counting sort of the token slots by expert with per-expert padding.
+
+    Returns dict(sorted_token_ids [C], expert_ids [C/B], num_tokens_post_padded,
+    expert_offsets [E+1]).
+    """
+    ids = _c(topk_ids, np.int32)
+    if ids.ndim == 1:
+        ids = ids.reshape(-1, 1)
+    T, K = ids.shape
+    C = align_capacity(T * K, E, B)
+    sorted_ids = np.empty(C, np.int32)
+    expert_ids = np.empty(C // B, np.int32)
+    P = np.zeros(1, np.int32)
+    off = np.empty(E + 1, np.int32)
+    rc = _load().oracle_align_sort(_ptr(ids), T, K, E, B, _ptr(sorted_ids), _ptr(expert_ids),
+                                   _ptr(P), _ptr(off))
+    if rc != 0:
+        raise ValueError("oracle_align_sort: invalid arguments")
+    return {"sorted_token_ids": sorted_ids, "expert_ids": expert_ids,
+            "num_tokens_post_padded": int(P[0]), "expert_offsets": off}
+
+
+# ----------------------------------------------------------- fp8 quant ----
+def quant_tokens_e4m3(x_bf16):
+    """Per-token E4M3 quantisation of bf16 rows; returns (codes uint8, scales f32)."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    q = np.empty((T, H), np.uint8)
+    s = np.empty(T, np.float32)
+    _load().oracle_quant_tokens_e4m3(_ptr(x), T, H, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_row_e4m3(v):
+    """E4M3 quantisation of one fp32 row with a per-row scale; returns (codes, scale)."""
+    v = _c(v, np.float32).ravel()
+    q = np.empty(v.size, np.uint8)
+    s = np.empty(1, np.float32)
+    _load().oracle_quant_row_e4m3(_ptr(v), v.size, _ptr(q), _ptr(s))
+    return q, float(s[0])
+
+
+# ------------------------------------------------------------ FFN, combine ----
+_WDT = {"f32": (W_F32, np.float32), "bf16": (W_BF16, np.uint16), "e4m3": (W_E4M3, np.uint8)}
+_XDT = {"f32": (X_F32, np.float32), "bf16": (X_BF16, np.uint16)}
+_INTER = {"f64": INTER_F64, "f32": INTER_F32, "bf16": INTER_BF16, "e4m3": INTER_E4M3}
+
+
+def expert_ffn(x, w13, w2, topk_ids, *, w_dtype, x_dtype, inter, w13_scale=None, w2_scale=None):
+    """y_slots[t*K+k] = FFN_{ids[t,k]}(x[t]) as float32 [T*K, H].
+
+    x: [T,H] fp32 or bf16 bit patterns; w13 [E,2I,H], w2 [E,H,I] in fp32, bf16 bits
+    or E4M3 codes (with w13_scale [E,2I], w2_scale [E,H]).  Slots with ids out of
+    range are left at zero.
+    """
+    wcode, wnp = _WDT[w_dtype]
+    xcode, xnp = _XDT[x_dtype]
+    x = _c(x, xnp)
+    w13 = _c(w13, wnp)
+    w2 = _c(w2, wnp)
+    ids = _c(topk_ids, np.int32)
+    T, H = x.shape
+    K = ids.shape[1]
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    assert H2 == H and w2.shape == (E, H, I) and ids.shape[0] == T
+    s13 = None if w13_scale is None else _c(w13_scale, np.float32)
+    s2 = None if w2_scale is None else _c(w2_scale, np.float32)
+    y = np.zeros((T * K, H), np.float32)
+    rc = _load().oracle_expert_ffn(T, K, E, H, I, wcode, xcode, _INTER[inter], _ptr(x), _ptr(w13),
+                                   _ptr(s13), _ptr(w2), _ptr(s2), _ptr(ids), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle_expert_ffn: invalid arguments")
+    return y
+
+
+def combine(y_slots, topk_weights, topk_ids, E: int):
+    """out[t] = sum_k w[t,k] * y_slots[t*K+k] (double, ascending k, ids out of range skipped)."""
+    y = _c(y_slots, np.float32)
+    w = _c(topk_weights, np.float32)
+    ids = _c(topk_ids, np.int32)
+    T, K = ids.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.float64)
+    rc = _load().oracle_combine(T, K, E, H, _ptr(y), _ptr(w), _ptr(ids), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_combine: invalid arguments")
+    return out
+
+
+def moe_layer(x, w13, w2, topk_ids, topk_weights, *, w_dtype, x_dtype, inter,
+              w13_scale=None, w2_scale=None, E=None):
+    """The expert FFN of every slot followed by the combine: (out f64 [T,H], y_slots)."""
+    E = w13.shape[0] if E is None else E
+    y = expert_ffn(x, w13, w2, topk_ids, w_dtype=w_dtype, x_dtype=x_dtype, inter=inter,
+                   w13_scale=w13_scale, w2_scale=w2_scale)
+    return combine(y, topk_weights, topk_ids, E), y
