@@ -1,0 +1,205 @@
+/*
+ * moe_mi355x.h -- C ABI of the single-GPU Mixture-of-Experts FFN layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer runs as four calls, in order, on one HIP stream:
+ *
+ *   moe_route_topk   logits [T,E]            -> topk_ids, topk_weights [T,K(+1)]
+ *   moe_align_sort   topk_ids                -> sorted_token_ids, expert_ids,
+ *                                               num_tokens_post_padded
+ *   moe_grouped_ffn  x, expert weights, the sorted layout -> y_slots [T*K, H]
+ *   moe_combine      y_slots, topk weights   -> out [T,H]
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers named as device pointers must point to device memory of the
+ *   current HIP device; tensors are dense and row-major; int32 and fp32
+ *   arrays are 4-byte aligned, bf16 arrays 2-byte aligned; x, the weights and
+ *   y_slots must be 16-byte aligned with H and I multiples of the tile widths
+ *   stated at moe_grouped_ffn.
+ * - The caller allocates and owns every buffer.  The library never allocates,
+ *   frees or synchronises, and never reads device memory from the host, so a
+ *   sequence of calls can be captured into a HIP graph.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *   work is enqueued asynchronously on it.  The library keeps no mutable
+ *   global state; calls are thread-safe.
+ * - Errors: arguments are validated on the host before anything is enqueued;
+ *   an invalid call returns a status != MOE_OK and enqueues nothing.  A launch
+ *   that fails returns MOE_ERR_HIP.  Data are never an error: expert ids
+ *   outside [0,E) are skipped by every step.
+ *
+ * Notation: T tokens, K experts per token (including an appended shared
+ * expert), E experts (weight slabs, including the shared one), H hidden
+ * size, I expert intermediate size, B block_size_m (rows per grouped-GEMM
+ * block), S = T*K token slots, slot i = t*K + k.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size  */
+    MOE_ERR_UNSUPPORTED = 2,   /* valid but not built: block size, dtype, E>1024 */
+    MOE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required   */
+    MOE_ERR_HIP = 4            /* a HIP launch failed (no device, bad pointer)  */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_t;
+
+int32_t moe_abi_version(void);
+const char *moe_status_string(int32_t status);
+
+/* ------------------------------------------------------------------------ */
+/* Top-k routing                                                             */
+/* ------------------------------------------------------------------------ */
+/*
+ * Defined by "AMD GPU ... 7x faster ... efficient MoE with any number of
+ * experts" (dignews.cc), opening paragraphs: the gating function sends each
+ * token to the experts with the top-K gating scores, DeepSeek V3/R1 adding a
+ * per-expert bias to balance load; and its FasterTransformer section (top-k
+ * gating softmax and the biased variant).
+ *
+ * For each token t (row of logits):
+ *   score_e = softmax(logits[t])_e  or  1/(1+exp(-logits[t,e]))   (computed in
+ *             double, rounded once to fp32)
+ *   key_e   = score_e + bias[e]      (fp32; bias may be NULL = 0)
+ *   if n_group > 1: experts form n_group equal consecutive groups; a group's
+ *             score is the sum of its two largest keys; only the topk_group
+ *             best groups stay eligible (ties: lower group index)
+ *   the K eligible experts with the largest keys are chosen (ties: lower id),
+ *   written in descending key order;
+ *   weight  = unbiased score; divided by the sum over the K chosen when
+ *             renormalize != 0; times routed_scaling; rounded to fp32.
+ *   append_shared != 0 writes one more column (id E, weight 1.0).
+ *
+ * logits   device fp32 [T,E]        bias device fp32 [E] or NULL
+ * topk_ids device int32 [T,K+append_shared]  (row-major, out)
+ * topk_weights device fp32 [T,K+append_shared] (out)
+ * Limits: 1 <= E <= 1024, 1 <= K <= topk_group*E/n_group, n_group divides E,
+ * n_group <= 64.  T = 0 is a no-op.
+ */
+typedef struct {
+    int32_t T, E, K;
+    int32_t score;             /* moe_score_t                                  */
+    int32_t n_group;           /* 1 = no group limit                           */
+    int32_t topk_group;
+    int32_t renormalize;
+    float routed_scaling;      /* 1.0f for none                                */
+    int32_t append_shared;
+} moe_route_params_t;
+
+moe_status_t moe_route_topk(const moe_route_params_t *p, const float *logits, const float *bias,
+                            int32_t *topk_ids, float *topk_weights, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Align & Sort                                                              */
+/* ------------------------------------------------------------------------ */
+/*
+ * Defined by the same dignews.cc page: opening paragraphs (sort token slots
+ * by expert id, with each expert's run aligned to whole blocks so that the
+ * grouped GEMM takes an expert's tokens block by block) and the section on
+ * the three-part algorithm (distributed concurrent counting, cumsum, parallel
+ * placement).
+ *
+ * Result (identical to a stable counting sort):
+ *   cnt[e]  = number of slots i with topk_ids[i] == e  (ids outside [0,E) skipped)
+ *   off[0] = 0, off[e+1] = off[e] + ceil(cnt[e]/B)*B,  P = off[E]
+ *   sorted_token_ids[off[e] + r] = the r-th slot (ascending i) with id e;
+ *   padding inside each expert's run and the tail [P, C) hold S = T*K;
+ *   expert_ids[j] = e for block j in [off[e]/B, off[e+1]/B), -1 for j >= P/B;
+ *   num_tokens_post_padded[0] = P; expert_offsets[0..E] = off (if not NULL).
+ * Capacity C = moe_align_sort_capacity(T,K,E,B) = B*floor((S + min(E,S)*(B-1))/B),
+ * the largest P any id table can produce.
+ *
+ * topk_ids device int32 [T*K]; sorted_token_ids device int32 [C] (out);
+ * expert_ids device int32 [C/B] (out); num_tokens_post_padded device int32 [1]
+ * (out); expert_offsets device int32 [E+1] (out) or NULL; workspace device,
+ * at least moe_align_sort_workspace_bytes(T,K,E,B) bytes, 256-byte aligned,
+ * contents need not be initialised and are clobbered.
+ * Limits: 1 <= E <= 1024; 1 <= B <= 1024; S + C < 2^31.
+ */
+int64_t moe_align_sort_capacity(int32_t T, int32_t K, int32_t E, int32_t B);
+int64_t moe_align_sort_workspace_bytes(int32_t T, int32_t K, int32_t E, int32_t B);
+moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32_t E, int32_t B,
+                            int32_t *sorted_token_ids, int32_t *expert_ids,
+                            int32_t *num_tokens_post_padded, int32_t *expert_offsets,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Grouped expert FFN                                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * Defined by "[Feature]: Add more configuration options for MoE assembly
+ * kernels" (ROCm/aiter issue 1248), "Suggestion Description" (gate and up
+ * projections with SiLU, the a8w8 mode with per-token fp8 activations, fp8
+ * weights and bf16 output, block_size_m rows per block) and the GC-MoE
+ * abstract (zhuanzhiai.com: fused SwiGLU, requantisation of the intermediate
+ * for the second fp8 GEMM, shared experts).
+ *
+ * For each block j < P/B with e = expert_ids[j] and each of its rows with
+ * slot r = sorted_token_ids[j*B + m] < S, token t = r / K:
+ *   a  = SiLU(x[t] . W13[e, 0:I]^T) * (x[t] . W13[e, I:2I]^T)     [I]
+ *   y_slots[r] = a . W2[e]^T                                       [H], fp32
+ * Rows holding the sentinel and blocks j >= P/B are skipped; rows of y_slots
+ * whose slot is never placed are not written.
+ *   w_dtype = x_dtype = MOE_F32 : fp32 throughout (a kept in fp32)
+ *   w_dtype = x_dtype = MOE_BF16: bf16 inputs, fp32 accumulation, a rounded
+ *                                 to bf16 between the two GEMMs
+ *   w_dtype = MOE_FP8_E4M3, x_dtype = MOE_BF16 (a8w8): x is quantised per
+ *     token to OCP E4M3 inside the call (scale = amax/448, code = RNE of
+ *     x*(448/amax), saturating); weights are E4M3 codes with one fp32 scale
+ *     per output row (w13_scale [E,2I], w2_scale [E,H]); products accumulate
+ *     in fp32 and are scaled by the two scales; a is requantised per row the
+ *     same way before the down projection.
+ * x device [T,H] (fp32 or bf16); w13 device [E,2I,H]; w2 device [E,H,I];
+ * sorted_token_ids / expert_ids / num_tokens_post_padded as produced by
+ * moe_align_sort with the same T,K,E,B; y_slots device fp32 [T*K,H] (out);
+ * workspace device, at least moe_grouped_ffn_workspace_bytes(p), 256-byte
+ * aligned, clobbered.
+ * Limits: B in {16,32,64,128}; H a multiple of 256 and I a multiple of 128
+ * (fp32: multiples of 64); E <= 1024.
+ */
+typedef struct {
+    int32_t T, K, E, H, I, B;
+    int32_t w_dtype;           /* moe_dtype_t */
+    int32_t x_dtype;           /* moe_dtype_t */
+} moe_ffn_params_t;
+
+int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);
+moe_status_t moe_grouped_ffn(const moe_ffn_params_t *p, const void *x, const void *w13,
+                             const float *w13_scale, const void *w2, const float *w2_scale,
+                             const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                             const int32_t *num_tokens_post_padded, float *y_slots,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Top-k weighted combine                                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * Defined by the dignews.cc page, opening paragraphs (a token's output is the
+ * gate-weighted result of its chosen experts) and the GC-MoE abstract (the
+ * shared expert joins the sum; here it is the appended column of weight 1).
+ *   out[t,h] = sum over k = 0..K-1 in ascending order, skipping ids outside
+ *              [0,E), of topk_weights[t,k] * y_slots[t*K+k, h]   (fp32)
+ * y_slots device fp32 [T*K,H]; topk_weights device fp32 [T,K]; topk_ids
+ * device int32 [T,K]; out device [T,H] in out_dtype (MOE_F32 or MOE_BF16,
+ * bf16 rounded to nearest even).  Limits: H a multiple of 4.
+ */
+moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float *y_slots,
+                         const float *topk_weights, const int32_t *topk_ids, int32_t out_dtype,
+                         void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -75,16 +75,21 @@ def _keys(seed: int, tag: int, block: int, stream: int):
     return k1, k2
 
 
-def hash_u32(seed: int, tag: int, block: int, start: int, n: int, device="cpu", stream: int = 0):
-    """u32 hashes of counters start..start+n-1 (int64 tensor, values in [0, 2^32))."""
-    if start < 0 or start + n > (1 << 32):
-        raise ValueError("counter range must stay inside [0, 2^32)")
+def hash_u32_at(seed: int, tag: int, block: int, idx: torch.Tensor, stream: int = 0):
+    """u32 hashes of the int64 counters in ``idx`` (values in [0, 2^32))."""
     k1, k2 = _keys(seed, tag, block, stream)
-    idx = torch.arange(start, start + n, dtype=torch.int64, device=device)
     h = torch.bitwise_and(_mul32(idx, _PHI) + k1, M32)
     h = _fmix32(h)
     h = torch.bitwise_xor(h, k2)
     return _fmix32(h)
+
+
+def hash_u32(seed: int, tag: int, block: int, start: int, n: int, device="cpu", stream: int = 0):
+    """u32 hashes of counters start..start+n-1 (int64 tensor, values in [0, 2^32))."""
+    if start < 0 or start + n > (1 << 32):
+        raise ValueError("counter range must stay inside [0, 2^32)")
+    idx = torch.arange(start, start + n, dtype=torch.int64, device=device)
+    return hash_u32_at(seed, tag, block, idx, stream)
 
 
 def hash_u32_reference(seed: int, tag: int, block: int, i: int, stream: int = 0) -> int:
@@ -160,32 +165,31 @@ def permutation(seed, tag, n) -> np.ndarray:
     return np.argsort(h, kind="stable").astype(np.int64)
 
 
-def zipf_topk_ids(seed, tag, T, K, E, s, chunk=65536) -> np.ndarray:
-    """[T,K] int32 expert ids, K distinct per token, drawn one after another
-    without replacement from Zipf(s) over ranks 1..E (p ∝ r^-s) by the inverse
-    CDF of the remaining mass (host double); rank r maps to expert perm[r-1]
-    through a seeded permutation."""
+def zipf_topk_ids(seed, tag, T, K, E, s) -> np.ndarray:
+    """[T,K] int32 expert ids, K distinct per token: each pick is a Zipf(s)
+    rank over 1..E (p ∝ r^-s, inverse CDF in host double) drawn again while it
+    repeats an earlier pick of the token -- which samples the remaining ranks
+    in proportion to their mass, i.e. sequential sampling without
+    replacement.  Rank r maps to expert perm[r-1] through a seeded
+    permutation.  Attempt a of pick k of token t uses counter t*K+k of block a."""
+    if K > E:
+        raise ValueError("K distinct experts need K <= E")
     perm = permutation(seed, TAG_PERM + 100 * tag, E)
-    p = np.arange(1, E + 1, dtype=np.float64) ** (-float(s))
-    out = np.empty((T, K), np.int32)
-    for t0 in range(0, T, chunk):
-        tn = min(chunk, T - t0)
-        u = hash_u32(seed, tag, 0, t0 * K, tn * K).numpy().astype(np.float64) * 2.0 ** -32
-        u = u.reshape(tn, K)
-        W = np.broadcast_to(p, (tn, E)).copy()
-        for k in range(K):
-            cs = np.cumsum(W, axis=1)
-            target = u[:, k] * cs[:, -1]
-            r = (cs <= target[:, None]).sum(axis=1)
-            r = np.minimum(r, E - 1)
-            # never land on a rank already taken (zero mass): step to the next live one
-            dead = W[np.arange(tn), r] == 0.0
-            while dead.any():
-                r[dead] = (r[dead] + 1) % E
-                dead = W[np.arange(tn), r] == 0.0
-            W[np.arange(tn), r] = 0.0
-            out[t0:t0 + tn, k] = perm[r]
-    return out
+    cdf = np.cumsum(np.arange(1, E + 1, dtype=np.float64) ** (-float(s)))
+    cdf /= cdf[-1]
+    ranks = np.full((T, K), -1, np.int64)
+    for k in range(K):
+        pending = np.arange(T, dtype=np.int64)
+        attempt = 0
+        while pending.size:
+            h = hash_u32_at(seed, tag, attempt, torch.from_numpy(pending * K + k)).numpy()
+            u = h.astype(np.float64) * 2.0 ** -32
+            r = np.minimum(np.searchsorted(cdf, u, side="right"), E - 1)
+            dup = (ranks[pending, :k] == r[:, None]).any(axis=1) if k else np.zeros(r.size, bool)
+            ranks[pending[~dup], k] = r[~dup]
+            pending = pending[dup]
+            attempt += 1
+    return perm[ranks].astype(np.int32)
 
 
 # ------------------------------------------------------------------ codecs --

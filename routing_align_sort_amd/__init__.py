@@ -1,0 +1,310 @@
+"""Python binding of the MI355X MoE FFN layer library (libmoe_mi355x.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the C-ABI library declared in include/moe_mi355x.h.  Tensors are torch CUDA
+(HIP) tensors; calls are enqueued on torch's current stream.  If the library
+has not been built this module raises on first use -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class _RouteParams(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("score", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("routed_scaling", ctypes.c_float), ("append_shared", ctypes.c_int32)]
+
+
+class _FfnParams(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32)]
+
+
+EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
+            "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
+            "moe_grouped_ffn", "moe_combine")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load and type the C-ABI library (no GPU needed to load it)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m routing_align_sort_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_abi_version.restype = i32
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_route_topk.argtypes = [ctypes.POINTER(_RouteParams), P, P, P, P, P]
+    lib.moe_route_topk.restype = i32
+    lib.moe_align_sort_capacity.argtypes = [i32, i32, i32, i32]
+    lib.moe_align_sort_capacity.restype = i64
+    lib.moe_align_sort_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.moe_align_sort_workspace_bytes.restype = i64
+    lib.moe_align_sort.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    lib.moe_align_sort.restype = i32
+    lib.moe_grouped_ffn_workspace_bytes.argtypes = [ctypes.POINTER(_FfnParams)]
+    lib.moe_grouped_ffn_workspace_bytes.restype = i64
+    lib.moe_grouped_ffn.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_grouped_ffn.restype = i32
+    lib.moe_combine.argtypes = [i32, i32, i32, i32, P, P, P, i32, P, P]
+    lib.moe_combine.restype = i32
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().moe_abi_version())
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(int(status)).decode()
+
+
+def _check(fn, st):
+    if st != MOE_OK:
+        raise MoEError(fn, st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name, numel=None):
+    if t.device.type != "cuda" or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor on the GPU, got "
+                         f"{t.dtype} on {t.device} (contiguous={t.is_contiguous()})")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+
+
+# ------------------------------------------------------------------ routing --
+def moe_route_topk(logits, K, *, score="softmax", bias=None, n_group=1, topk_group=1,
+                   renormalize=True, routed_scaling=1.0, append_shared=False,
+                   topk_ids=None, topk_weights=None, stream=None):
+    """Top-K routing of each row of fp32 ``logits`` [T,E]; returns (topk_ids, topk_weights)."""
+    lib = load_library()
+    T, E = logits.shape
+    _need(logits, torch.float32, "logits")
+    if bias is not None:
+        _need(bias, torch.float32, "bias", E)
+    KO = K + (1 if append_shared else 0)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, KO), dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, KO), dtype=torch.float32, device=logits.device)
+    _need(topk_ids, torch.int32, "topk_ids", T * KO)
+    _need(topk_weights, torch.float32, "topk_weights", T * KO)
+    p = _RouteParams(T, E, K, {"softmax": 0, "sigmoid": 1}[score], n_group, topk_group,
+                     int(bool(renormalize)), float(routed_scaling), int(bool(append_shared)))
+    _check("moe_route_topk", lib.moe_route_topk(ctypes.byref(p), _ptr(logits), _ptr(bias),
+                                                _ptr(topk_ids), _ptr(topk_weights), _stream(stream)))
+    return topk_ids, topk_weights
+
+
+# -------------------------------------------------------------- align&sort --
+def moe_align_sort_capacity(T, K, E, B) -> int:
+    c = int(load_library().moe_align_sort_capacity(T, K, E, B))
+    if c < 0:
+        raise MoEError("moe_align_sort_capacity", MOE_ERR_INVALID_ARG)
+    return c
+
+
+def moe_align_sort_workspace_bytes(T, K, E, B) -> int:
+    c = int(load_library().moe_align_sort_workspace_bytes(T, K, E, B))
+    if c < 0:
+        raise MoEError("moe_align_sort_workspace_bytes", MOE_ERR_INVALID_ARG)
+    return c
+
+
+def moe_align_sort(topk_ids, E, B, *, sorted_token_ids=None, expert_ids=None,
+                   num_tokens_post_padded=None, expert_offsets=None, workspace=None, stream=None):
+    """Align & Sort of int32 ``topk_ids`` [T,K]; returns a dict of device tensors."""
+    lib = load_library()
+    ids = topk_ids if topk_ids.dim() == 2 else topk_ids.view(-1, 1)
+    T, K = ids.shape
+    _need(ids, torch.int32, "topk_ids")
+    dev = ids.device
+    C = moe_align_sort_capacity(T, K, E, B)
+    if sorted_token_ids is None:
+        sorted_token_ids = torch.empty(C, dtype=torch.int32, device=dev)
+    if expert_ids is None:
+        expert_ids = torch.empty(C // B, dtype=torch.int32, device=dev)
+    if num_tokens_post_padded is None:
+        num_tokens_post_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    if expert_offsets is None:
+        expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ws_need = moe_align_sort_workspace_bytes(T, K, E, B)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _need(sorted_token_ids, torch.int32, "sorted_token_ids", C)
+    _need(expert_ids, torch.int32, "expert_ids", C // B)
+    _need(num_tokens_post_padded, torch.int32, "num_tokens_post_padded", 1)
+    _need(expert_offsets, torch.int32, "expert_offsets", E + 1)
+    _check("moe_align_sort", lib.moe_align_sort(
+        _ptr(ids), T, K, E, B, _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(expert_offsets), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return {"sorted_token_ids": sorted_token_ids, "expert_ids": expert_ids,
+            "num_tokens_post_padded": num_tokens_post_padded, "expert_offsets": expert_offsets}
+
+
+# -------------------------------------------------------------- grouped FFN --
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
+
+
+def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype):
+    return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype])
+
+
+def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype) -> int:
+    p = _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype)
+    c = int(load_library().moe_grouped_ffn_workspace_bytes(ctypes.byref(p)))
+    if c < 0:
+        raise MoEError("moe_grouped_ffn_workspace_bytes", MOE_ERR_UNSUPPORTED)
+    return c
+
+
+def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, *, K, B,
+                    w13_scale=None, w2_scale=None, y_slots=None, workspace=None, stream=None):
+    """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots fp32 [T*K, H]."""
+    lib = load_library()
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    if H2 != H or tuple(w2.shape) != (E, H, I):
+        raise ValueError("weight shapes do not match x")
+    _need(x, x.dtype, "x")
+    _need(w13, w13.dtype, "w13")
+    _need(w2, w13.dtype, "w2")
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (num_tokens_post_padded, "num_tokens_post_padded")):
+        _need(t, torch.int32, n)
+    if w13.dtype == torch.float8_e4m3fn:
+        _need(w13_scale, torch.float32, "w13_scale", E * 2 * I)
+        _need(w2_scale, torch.float32, "w2_scale", E * H)
+    if y_slots is None:
+        y_slots = torch.empty((T * K, H), dtype=torch.float32, device=x.device)
+    _need(y_slots, torch.float32, "y_slots", T * K * H)
+    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype)
+    need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("moe_grouped_ffn", lib.moe_grouped_ffn(
+        ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(y_slots),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return y_slots
+
+
+# ------------------------------------------------------------------ combine --
+def moe_combine(y_slots, topk_weights, topk_ids, E, *, out_dtype=torch.bfloat16, out=None,
+                stream=None):
+    """out[t] = sum_k w[t,k] * y_slots[t*K+k] (ascending k, ids outside [0,E) skipped)."""
+    lib = load_library()
+    T, K = topk_ids.shape
+    H = y_slots.shape[1]
+    _need(y_slots, torch.float32, "y_slots", T * K * H)
+    _need(topk_weights, torch.float32, "topk_weights", T * K)
+    _need(topk_ids, torch.int32, "topk_ids", T * K)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y_slots.device)
+    _need(out, out_dtype, "out", T * H)
+    _check("moe_combine", lib.moe_combine(T, K, E, H, _ptr(y_slots), _ptr(topk_weights),
+                                          _ptr(topk_ids), _DT[out_dtype], _ptr(out),
+                                          _stream(stream)))
+    return out
+
+
+# -------------------------------------------------------------- the layer --
+class MoELayer:
+    """The four calls of one MoE layer over preallocated buffers.
+
+    Holds the weights and every intermediate buffer so that ``forward`` only
+    enqueues the four library calls (route -> align -> grouped FFN -> combine).
+    """
+
+    def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
+                 renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
+                 w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16):
+        dev = w13.device
+        self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
+        self.E_slabs = w13.shape[0]
+        self.E_routed = self.E_slabs - (1 if shared else 0)
+        self.T, self.K, self.B, self.shared = T, K, B, shared
+        self.KO = K + (1 if shared else 0)
+        self.H, self.I = w13.shape[2], w13.shape[1] // 2
+        self.route_kw = dict(score=score, n_group=n_group, topk_group=topk_group,
+                             renormalize=renormalize, routed_scaling=routed_scaling,
+                             append_shared=shared)
+        self.out_dtype = out_dtype
+        C = moe_align_sort_capacity(T, self.KO, self.E_slabs, B)
+        self.C = C
+        self.topk_ids = torch.empty((T, self.KO), dtype=torch.int32, device=dev)
+        self.topk_weights = torch.empty((T, self.KO), dtype=torch.float32, device=dev)
+        self.sorted = torch.empty(C, dtype=torch.int32, device=dev)
+        self.expert_ids = torch.empty(C // B, dtype=torch.int32, device=dev)
+        self.ntpp = torch.empty(1, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(self.E_slabs + 1, dtype=torch.int32, device=dev)
+        ws_a = moe_align_sort_workspace_bytes(T, self.KO, self.E_slabs, B)
+        ws_f = moe_grouped_ffn_workspace_bytes(T, self.KO, self.E_slabs, self.H, self.I, B,
+                                               w13.dtype, x_dtype)
+        self.ws_align = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
+        self.ws_ffn = torch.empty(max(ws_f, 1), dtype=torch.uint8, device=dev)
+        self.y_slots = torch.empty((T * self.KO, self.H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, self.H), dtype=out_dtype, device=dev)
+
+    def route(self, logits, bias=None):
+        return moe_route_topk(logits, self.K, bias=bias, topk_ids=self.topk_ids,
+                              topk_weights=self.topk_weights, **self.route_kw)
+
+    def align(self):
+        return moe_align_sort(self.topk_ids, self.E_slabs, self.B, sorted_token_ids=self.sorted,
+                              expert_ids=self.expert_ids, num_tokens_post_padded=self.ntpp,
+                              expert_offsets=self.offsets, workspace=self.ws_align)
+
+    def ffn(self, x):
+        return moe_grouped_ffn(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
+                               K=self.KO, B=self.B, w13_scale=self.w13_scale,
+                               w2_scale=self.w2_scale, y_slots=self.y_slots, workspace=self.ws_ffn)
+
+    def combine(self):
+        return moe_combine(self.y_slots, self.topk_weights, self.topk_ids, self.E_slabs,
+                           out_dtype=self.out_dtype, out=self.out)
+
+    def forward(self, x, logits, bias=None):
+        self.route(logits, bias)
+        self.align()
+        self.ffn(x)
+        return self.combine()

@@ -1,0 +1,149 @@
+// The C ABI (include/moe_mi355x.h): host-side validation, sizing and launch.
+// Nothing here allocates, synchronises or reads device memory.
+#include "../../include/moe_mi355x.h"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int64_t capacity(int64_t S, int64_t E, int64_t B) {
+    const int64_t n = S < E ? S : E;
+    return B * ((S + n * (B - 1)) / B);
+}
+
+bool align_args_ok(int32_t T, int32_t K, int32_t E, int32_t B) {
+    if (T < 0 || K < 1 || E < 1 || B < 1) return false;
+    const int64_t S = (int64_t)T * K;
+    return S + capacity(S, E, B) < ((int64_t)1 << 31);
+}
+
+bool ffn_block_ok(int32_t B) { return B == 16 || B == 32 || B == 64 || B == 128; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int32_t s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+moe_status_t moe_route_topk(const moe_route_params_t* p, const float* logits, const float* bias,
+                            int32_t* topk_ids, float* topk_weights, void* stream) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 0 || p->E < 1 || p->K < 1 || p->n_group < 1 || p->topk_group < 1 ||
+        p->topk_group > p->n_group || p->E % p->n_group != 0 ||
+        p->K > p->topk_group * (p->E / p->n_group) || (p->score != MOE_SCORE_SOFTMAX && p->score != MOE_SCORE_SIGMOID))
+        return MOE_ERR_INVALID_ARG;
+    if (p->E > kRouteMaxExperts || p->K > kRouteMaxK || p->n_group > kRouteMaxGroups) return MOE_ERR_UNSUPPORTED;
+    if (p->T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+    RouteArgs a;
+    a.T = p->T; a.E = p->E; a.K = p->K; a.score = p->score;
+    a.n_group = p->n_group; a.topk_group = p->topk_group;
+    a.renormalize = p->renormalize != 0; a.append_shared = p->append_shared != 0;
+    a.routed_scaling = p->routed_scaling;
+    a.logits = logits; a.bias = bias; a.topk_ids = topk_ids; a.topk_weights = topk_weights;
+    return from_hip(launch_route_topk(a, as_stream(stream)));
+}
+
+int64_t moe_align_sort_capacity(int32_t T, int32_t K, int32_t E, int32_t B) {
+    if (!align_args_ok(T, K, E, B)) return -1;
+    return capacity((int64_t)T * K, E, B);
+}
+
+int64_t moe_align_sort_workspace_bytes(int32_t T, int32_t K, int32_t E, int32_t B) {
+    if (!align_args_ok(T, K, E, B)) return -1;
+    return align_plan((int64_t)T * K, E).workspace_bytes;
+}
+
+moe_status_t moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t K, int32_t E, int32_t B,
+                            int32_t* sorted_token_ids, int32_t* expert_ids,
+                            int32_t* num_tokens_post_padded, int32_t* expert_offsets,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (!align_args_ok(T, K, E, B)) return MOE_ERR_INVALID_ARG;
+    if (E > kAlignMaxExperts || B > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t S = (int64_t)T * K;
+    const int64_t C = capacity(S, E, B);
+    if (!num_tokens_post_padded || (S > 0 && !topk_ids) || (C > 0 && (!sorted_token_ids || !expert_ids)))
+        return MOE_ERR_INVALID_ARG;
+    const int64_t need = align_plan(S, E).workspace_bytes;
+    if (need > 0 && (!workspace || (int64_t)workspace_bytes < need)) return MOE_ERR_WORKSPACE;
+    return from_hip(launch_align_sort(topk_ids, S, E, B, C, sorted_token_ids, expert_ids,
+                                      num_tokens_post_padded, expert_offsets, workspace, as_stream(stream)));
+}
+
+static moe_status_t ffn_check(const moe_ffn_params_t* p) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 0 || p->K < 1 || p->E < 1 || p->H < 1 || p->I < 1 || !align_args_ok(p->T, p->K, p->E, p->B))
+        return MOE_ERR_INVALID_ARG;
+    const bool f32 = p->w_dtype == MOE_F32 && p->x_dtype == MOE_F32;
+    const bool bf16 = p->w_dtype == MOE_BF16 && p->x_dtype == MOE_BF16;
+    const bool fp8 = p->w_dtype == MOE_FP8_E4M3 && p->x_dtype == MOE_BF16;
+    if (!(f32 || bf16 || fp8)) return MOE_ERR_UNSUPPORTED;
+    if (!ffn_block_ok(p->B) || p->E > kAlignMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (f32 && (p->H % 64 || p->I % 64)) return MOE_ERR_UNSUPPORTED;
+    if (!f32 && (p->H % 256 || p->I % 128)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
+    if (ffn_check(p) != MOE_OK) return -1;
+    const int64_t C = capacity((int64_t)p->T * p->K, p->E, p->B);
+    return ffn_workspace_bytes(p->w_dtype, p->T, p->H, p->I, C);
+}
+
+moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
+                             const float* w13_scale, const void* w2, const float* w2_scale,
+                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                             const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    const moe_status_t st = ffn_check(p);
+    if (st != MOE_OK) return st;
+    const int64_t S = (int64_t)p->T * p->K;
+    const int64_t C = capacity(S, p->E, p->B);
+    if (S == 0) return MOE_OK;
+    if (!x || !w13 || !w2 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !y_slots)
+        return MOE_ERR_INVALID_ARG;
+    if (p->w_dtype == MOE_FP8_E4M3 && (!w13_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+    const int64_t need = ffn_workspace_bytes(p->w_dtype, p->T, p->H, p->I, C);
+    if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    FfnArgs a;
+    a.T = p->T; a.K = p->K; a.E = p->E; a.H = p->H; a.I = p->I; a.B = p->B;
+    a.S = S; a.C = C;
+    a.x = x; a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
+    a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.post_padded = num_tokens_post_padded;
+    a.y_slots = y_slots;
+    hipError_t e;
+    if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream));
+    else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream));
+    else e = launch_ffn_fp8(a, workspace, as_stream(stream));
+    return from_hip(e);
+}
+
+moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float* y_slots,
+                         const float* topk_weights, const int32_t* topk_ids, int32_t out_dtype, void* out,
+                         void* stream) {
+    if (T < 0 || K < 1 || E < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (H % 4) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!y_slots || !topk_weights || !topk_ids || !out) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_combine(T, K, E, H, y_slots, topk_weights, topk_ids, out_dtype == MOE_BF16, out,
+                                   as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Top-k weighted combine for gfx950.
+//
+// What it computes: "AMD GPU ... 7x faster ... efficient MoE with any number
+// of experts" (dignews.cc), opening paragraphs -- a token's output is the sum
+// of its chosen experts' FFN outputs weighted by their gate values; the
+// GC-MoE abstract (zhuanzhiai.com) adds the shared expert, which here is the
+// appended column with weight 1.  The sum runs in ascending k in fp32.
+//
+// A streaming kernel: each thread owns 4 consecutive hidden units of one
+// token, reads the K slot rows with 16-byte non-temporal loads (each y_slots
+// row is read exactly once) and writes fp32 or bf16.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kCombineThreads = 256;
+
+template <bool kBf16>
+__global__ void __launch_bounds__(kCombineThreads)
+combine_kernel(int T, int K, int E, int H, int nchunk, const float* __restrict__ y,
+               const float* __restrict__ w, const int32_t* __restrict__ ids, void* __restrict__ out) {
+    const int t = blockIdx.x / nchunk;
+    const int h = ((blockIdx.x % nchunk) * kCombineThreads + threadIdx.x) * 4;
+    if (h >= H) return;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+        const int64_t i = (int64_t)t * K + k;
+        const int e = ids[i];
+        if (e < 0 || e >= E) continue;
+        const float wk = w[i];
+        const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)(y + i * H + h));
+        acc[0] += wk * v[0];
+        acc[1] += wk * v[1];
+        acc[2] += wk * v[2];
+        acc[3] += wk * v[3];
+    }
+    if (kBf16) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+        uint2* o = (uint2*)((uint16_t*)out + (int64_t)t * H + h);
+        *o = make_uint2(lo, hi);
+    } else {
+        *(f32x4_t*)((float*)out + (int64_t)t * H + h) = acc;
+    }
+}
+
+hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,
+                          const int32_t* ids, int out_bf16, void* out, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int nchunk = (H / 4 + kCombineThreads - 1) / kCombineThreads;
+    const dim3 grid((unsigned)((int64_t)T * nchunk));
+    if (out_bf16)
+        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kCombineThreads), 0, stream, T, K, E, H,
+                           nchunk, y_slots, w, ids, out);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kCombineThreads), 0, stream, T, K, E, H,
+                           nchunk, y_slots, w, ids, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,486 @@
+// Block-aligned grouped expert FFN on gfx950 matrix cores: bf16 and a8w8 fp8.
+//
+// What it computes: "[Feature]: Add more configuration options for MoE
+// assembly kernels" (ROCm/aiter issue 1248), "Suggestion Description" -- per
+// block of block_size_m rows of one expert, the gate and up projections,
+// SiLU(gate) * up, then the down projection; the a8w8 mode with per-token fp8
+// activations, fp8 weights and bf16 output; "Estimated Performance Scaling" --
+// the block size trades weight reloads against padding rows.  The GC-MoE
+// abstract (zhuanzhiai.com) adds the requantisation of the intermediate before
+// the second fp8 GEMM.
+//
+// Design on MI355X
+// ----------------
+// * Two GEMM launches.  Stage 1 (gate/up + SiLU*up) writes the intermediate in
+//   sorted-row order; stage 2 (down) reads it and scatters fp32 rows to
+//   y_slots by slot index.  Grids are sized by capacity (C/B blocks); blocks
+//   past num_tokens_post_padded exit at once, so nothing is read back to the
+//   host and the sequence is graph-capturable.
+// * 256-thread workgroups (4 waves, one per SIMD).  bf16 uses
+//   v_mfma_f32_32x32x16_bf16, fp8 v_mfma_scale_f32_32x32x64_f8f6f4 (OCP E4M3
+//   operands, unit block scales; per-token and per-channel scales are applied
+//   in the epilogue).  Stage 1: a wave owns 32 intermediate columns (its 32 gate
+//   rows and 32 up rows of W13), a workgroup 128.  Stage 2: a wave owns 64
+//   output columns, a workgroup 256.  The M tile is block_size_m rows (at
+//   least one 32-row MFMA tile; rows past the block are zero).
+// * A K-step is 128 bytes of every row (64 bf16 or 128 fp8 values).  Expert
+//   weights stream straight from HBM into MFMA operand registers: each lane
+//   reads 64 contiguous bytes of one weight row per K-step, and the
+//   contraction index inside a K-step is permuted identically for the A and B
+//   operands so those bytes feed the MFMAs as they are.  Loads run PF K-steps
+//   ahead in a register ring, keeping enough bytes in flight per CU to stream
+//   HBM.  Each weight element is used by exactly one wave, so it never passes
+//   through LDS.
+// * Activations (the A operand shared by the 4 waves) go through a
+//   double-buffered, row-padded LDS tile (144-byte pitch: conflict-free 16-byte
+//   MFMA reads), gathered through sorted_token_ids in stage 1.
+// * Tiles are dealt so that each XCD gets a contiguous tile range, walked with
+//   the N tile fastest: the workgroups of one XCD share the activation rows of
+//   a few M blocks in that XCD's L2, and M blocks of one expert stay close in
+//   time so repeated weight tiles hit L2 (the pid remapping idea of the AITER
+//   section of the dignews.cc page, "AMD GPU ... 7x faster ...").
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kFfnThreads = 256;
+constexpr int kStepBytes = 128;                 // bytes of a row per K-step
+constexpr int kLdsPitch = kStepBytes + 16;      // padded LDS row, bytes
+
+template <int BM>
+struct Tile {
+    static constexpr int MT = (BM < 32 ? 32 : BM) / 32;         // 32-row MFMA tiles
+    static constexpr int ROWS = MT * 32;
+    static constexpr int ACH = BM * (kStepBytes / 16);           // 16-byte A chunks per K-step
+    static constexpr int APT = (ACH + kFfnThreads - 1) / kFfnThreads;
+    static constexpr int LDS_BYTES = 2 * ROWS * kLdsPitch;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ i32x8_t as_i32x8(uint4 lo, uint4 hi) {
+    i32x8_t r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+}
+
+// The shared K loop.  arow[m] points at row m of A (nullptr = zero row);
+// brow[ns] is this lane's weight row for B subtile ns, already offset by the
+// lane's half (64 bytes); nk K-steps of 128 bytes; acc[MT][NSUB] accumulates.
+template <bool kFp8, int BM, int NSUB, int PF>
+__device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t* const (&brow)[NSUB], int nk,
+                                      uint8_t* lds, f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
+    using TL = Tile<BM>;
+    constexpr int MT = TL::MT;
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+
+    uint4 areg[PF + 1][TL::APT];
+    uint4 breg[PF + 1][NSUB][4];
+
+    auto load_a = [&](uint4 (&dst)[TL::APT], int k) {
+#pragma unroll
+        for (int r = 0; r < TL::APT; ++r) {
+            const int c = tid + r * kFfnThreads;
+            dst[r] = make_uint4(0, 0, 0, 0);
+            if (c < TL::ACH) {
+                const uint8_t* src = arow[c >> 3];
+                if (src) dst[r] = *(const uint4*)(src + (int64_t)k * kStepBytes + (c & 7) * 16);
+            }
+        }
+    };
+    auto store_a = [&](const uint4 (&src)[TL::APT], int buf) {
+#pragma unroll
+        for (int r = 0; r < TL::APT; ++r) {
+            const int c = tid + r * kFfnThreads;
+            if (c < TL::ACH)
+                *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = src[r];
+        }
+    };
+    auto load_b = [&](uint4 (&dst)[NSUB][4], int k) {
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                dst[ns][q] = *(const uint4*)(brow[ns] + (int64_t)k * kStepBytes + q * 16);
+    };
+    auto compute = [&](const uint4 (&b)[NSUB][4], int buf) {
+        const uint8_t* base = lds + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * 64;
+        if constexpr (!kFp8) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint4 af = *(const uint4*)(base + mt * 32 * kLdsPitch + kk * 16);
+#pragma unroll
+                    for (int ns = 0; ns < NSUB; ++ns)
+                        acc[mt][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            as_bf16x8(af), as_bf16x8(b[ns][kk]), acc[mt][ns], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint4 a0 = *(const uint4*)(base + mt * 32 * kLdsPitch + kk * 32);
+                    const uint4 a1 = *(const uint4*)(base + mt * 32 * kLdsPitch + kk * 32 + 16);
+#pragma unroll
+                    for (int ns = 0; ns < NSUB; ++ns)
+                        acc[mt][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            as_i32x8(a0, a1), as_i32x8(b[ns][2 * kk], b[ns][2 * kk + 1]), acc[mt][ns],
+                            0, 0, 0, 127, 0, 127);
+                }
+            }
+        }
+    };
+
+    // prologue: K-steps 0..PF-1 in flight, step 0 of A in LDS
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        if (s < nk) {
+            load_a(areg[s], s);
+            load_b(breg[s], s);
+        }
+    }
+    store_a(areg[0], 0);
+    __syncthreads();
+
+    for (int k0 = 0; k0 < nk; k0 += PF + 1) {
+#pragma unroll
+        for (int u = 0; u <= PF; ++u) {
+            const int k = k0 + u;
+            if (k < nk) {
+                const int nxt = (u + PF) % (PF + 1);
+                if (k + PF < nk) {
+                    load_a(areg[nxt], k + PF);
+                    load_b(breg[nxt], k + PF);
+                }
+                compute(breg[u], k & 1);
+                if (k + 1 < nk) store_a(areg[(u + 1) % (PF + 1)], (k + 1) & 1);
+                __syncthreads();
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+// Row of the 32x32 MFMA accumulator held by this lane in register i.
+__device__ __forceinline__ int acc_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
+
+template <int MT, int NSUB>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[MT][NSUB]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ++ns)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mt][ns][i] = 0.f;
+}
+
+struct Fp8Ws {
+    uint8_t* xq;        // [T,H] E4M3 codes of x
+    float* sx;          // [T]   per-token scales
+    float* a;           // [C,I] fp32 intermediate
+    uint32_t* amax;     // [C]   per-row max |a| (fp32 bits)
+    uint8_t* aq;        // [C,I] E4M3 codes of the intermediate
+    float* sa;          // [C]   per-row scales
+};
+
+// ------------------------------------------------------------------ stage 1 --
+// bf16: h_out is bf16 [C,I].  fp8: writes fp32 a and the row amax.
+// Workgroups per CU the register budget is sized for: the 128-row tile keeps
+// 4x2 accumulator tiles per wave and takes the whole register file.
+template <int BM>
+constexpr int ffn_min_blocks() { return BM >= 128 ? 1 : 2; }
+
+template <bool kFp8, int BM, int PF>
+__global__ void __launch_bounds__(kFfnThreads, ffn_min_blocks<BM>())
+ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN, int ntiles) {
+    using TL = Tile<BM>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
+    __shared__ const uint8_t* arow[BM];
+    __shared__ float rowscale[BM];
+    const int tile = xcd_contiguous_tile(blockIdx.x, ntiles);
+    const int mb = tile / nN, nt = tile % nN;
+    const int P = a.post_padded[0];
+    if (mb * BM >= P) return;
+    const int e = a.expert_ids[mb];
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int H = a.H, I = a.I;
+    constexpr int esz = kFp8 ? 1 : 2;
+    if (tid < BM) {
+        const int slot = a.sorted_ids[(int64_t)mb * BM + tid];
+        const bool ok = slot < a.S;
+        const int t = ok ? slot / a.K : 0;
+        const uint8_t* xs = kFp8 ? q.xq : (const uint8_t*)a.x;
+        arow[tid] = ok ? xs + (int64_t)t * H * esz : nullptr;
+        if (kFp8) rowscale[tid] = ok ? q.sx[t] : 0.f;
+    }
+    if (BM < TL::ROWS)
+        for (int i = tid; i < TL::LDS_BYTES / 16; i += kFfnThreads) ((uint4*)lds)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    const int n0 = nt * 128 + w * 32;                       // this wave's intermediate columns
+    const int r32 = lane & 31, half = lane >> 5;
+    const uint8_t* wbase = (const uint8_t*)a.w13 + (int64_t)e * 2 * I * H * esz;
+    const uint8_t* const brow[2] = {wbase + ((int64_t)(n0 + r32) * H) * esz + half * 64,
+                                    wbase + ((int64_t)(I + n0 + r32) * H) * esz + half * 64};
+    f32x16_t acc[TL::MT][2];
+    zero_acc(acc);
+    kloop<kFp8, BM, 2, PF>(arow, brow, H * esz / kStepBytes, lds, acc);
+
+    const int col = n0 + r32;
+    float sg = 1.f, su = 1.f;
+    if (kFp8) {
+        sg = a.w13_scale[(int64_t)e * 2 * I + col];
+        su = a.w13_scale[(int64_t)e * 2 * I + I + col];
+    }
+#pragma unroll
+    for (int mt = 0; mt < TL::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = mt * 32 + acc_row(i, lane);
+            float g = acc[mt][0][i], u = acc[mt][1][i];
+            if (kFp8) {
+                const float s = (m < BM) ? rowscale[m] : 0.f;
+                g = g * s * sg;
+                u = u * s * su;
+            }
+            const float hval = silu_f32(g) * u;
+            if constexpr (kFp8) {
+                // row max over this wave's 32 columns, then one atomic per row
+                float mx = fabsf(hval);
+#pragma unroll
+                for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+                if (m < BM) {
+                    q.a[((int64_t)mb * BM + m) * I + col] = hval;
+                    if (r32 == 0 && mx > 0.f) atomicMax(q.amax + (int64_t)mb * BM + m, __float_as_uint(mx));
+                }
+            } else {
+                if (m < BM) h_out[((int64_t)mb * BM + m) * I + col] = f32_to_bf16_bits(hval);
+            }
+        }
+}
+
+// ------------------------------------------------------------------ stage 2 --
+template <bool kFp8, int BM, int PF>
+__global__ void __launch_bounds__(kFfnThreads, ffn_min_blocks<BM>())
+ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN,
+           int ntiles) {
+    using TL = Tile<BM>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
+    __shared__ const uint8_t* arow[BM];
+    __shared__ int slots[BM];
+    __shared__ float rowscale[BM];
+    const int tile = xcd_contiguous_tile(blockIdx.x, ntiles);
+    const int mb = tile / nN, nt = tile % nN;
+    const int P = a.post_padded[0];
+    if (mb * BM >= P) return;
+    const int e = a.expert_ids[mb];
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+    const int H = a.H, I = a.I;
+    constexpr int esz = kFp8 ? 1 : 2;
+    if (tid < BM) {
+        arow[tid] = h_in + ((int64_t)mb * BM + tid) * I * esz;
+        slots[tid] = a.sorted_ids[(int64_t)mb * BM + tid];
+        if (kFp8) rowscale[tid] = sa[(int64_t)mb * BM + tid];
+    }
+    if (BM < TL::ROWS)
+        for (int i = tid; i < TL::LDS_BYTES / 16; i += kFfnThreads) ((uint4*)lds)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    const int n0 = nt * 256 + w * 64;                       // this wave's output columns
+    const int r32 = lane & 31, half = lane >> 5;
+    const uint8_t* wbase = (const uint8_t*)a.w2 + (int64_t)e * H * I * esz;
+    const uint8_t* const brow[2] = {wbase + ((int64_t)(n0 + r32) * I) * esz + half * 64,
+                                    wbase + ((int64_t)(n0 + 32 + r32) * I) * esz + half * 64};
+    f32x16_t acc[TL::MT][2];
+    zero_acc(acc);
+    kloop<kFp8, BM, 2, PF>(arow, brow, I * esz / kStepBytes, lds, acc);
+
+    float s0 = 1.f, s1 = 1.f;
+    if (kFp8) {
+        s0 = a.w2_scale[(int64_t)e * H + n0 + r32];
+        s1 = a.w2_scale[(int64_t)e * H + n0 + 32 + r32];
+    }
+#pragma unroll
+    for (int mt = 0; mt < TL::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = mt * 32 + acc_row(i, lane);
+            if (m < BM) {
+                const int slot = slots[m];
+                if (slot < a.S) {
+                    float y0 = acc[mt][0][i], y1 = acc[mt][1][i];
+                    if (kFp8) {
+                        const float rs = rowscale[m];
+                        y0 = y0 * rs * s0;
+                        y1 = y1 * rs * s1;
+                    }
+                    float* dst = a.y_slots + (int64_t)slot * H + n0 + r32;
+                    dst[0] = y0;
+                    dst[32] = y1;
+                }
+            }
+        }
+}
+
+// --------------------------------------------------------- fp8 quantisation --
+// E4M3 code of v (OCP, nearest even); |v| <= 448 by construction (clamped).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    a = fminf(fmaxf(a, -448.f), 448.f);
+    b = fminf(fmaxf(b, -448.f), 448.f);
+    c = fminf(fmaxf(c, -448.f), 448.f);
+    d = fminf(fmaxf(d, -448.f), 448.f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
+constexpr int kQuantThreads = 256;
+
+__device__ __forceinline__ float block_max(float v, float* lds4) {
+    v = wave_max_f32(v);
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) lds4[w] = v;
+    __syncthreads();
+    float m = lds4[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / kWave; ++i) m = fmaxf(m, lds4[i]);
+    return m;
+}
+
+// One workgroup per token: x bf16 row -> E4M3 codes + scale.  Also clears the
+// per-row amax of the intermediate for stage 1.
+__global__ void __launch_bounds__(kQuantThreads)
+quant_tokens_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq, float* __restrict__ sx,
+                    uint32_t* __restrict__ amax_rows, int64_t C) {
+    __shared__ float red[kQuantThreads / kWave];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    for (int64_t r = (int64_t)t * kQuantThreads + tid; r < C; r += (int64_t)gridDim.x * kQuantThreads)
+        amax_rows[r] = 0u;
+    const uint16_t* row = x + (int64_t)t * H;
+    float m = 0.f;
+    for (int h = tid * 8; h < H; h += kQuantThreads * 8) {
+        const uint4 v = *(const uint4*)(row + h);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(wv[j] & 0xFFFF))));
+            m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(wv[j] >> 16))));
+        }
+    }
+    m = block_max(m, red);
+    const float inv = (m > 0.f) ? 448.0f / m : 0.f;
+    if (tid == 0) sx[t] = (m > 0.f) ? m / 448.0f : 1.0f;
+    for (int h = tid * 8; h < H; h += kQuantThreads * 8) {
+        const uint4 v = *(const uint4*)(row + h);
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[2 * j] = bf16_bits_to_f32((uint16_t)(wv[j] & 0xFFFF)) * inv;
+            f[2 * j + 1] = bf16_bits_to_f32((uint16_t)(wv[j] >> 16)) * inv;
+        }
+        uint2 o;
+        o.x = e4m3_pack4(f[0], f[1], f[2], f[3]);
+        o.y = e4m3_pack4(f[4], f[5], f[6], f[7]);
+        *(uint2*)(xq + (int64_t)t * H + h) = o;
+    }
+}
+
+// One workgroup per sorted row of the intermediate: fp32 a -> E4M3 + scale.
+__global__ void __launch_bounds__(kQuantThreads)
+requant_rows_kernel(const float* __restrict__ a, const uint32_t* __restrict__ amax_rows,
+                    const int32_t* __restrict__ post_padded, int I, uint8_t* __restrict__ aq,
+                    float* __restrict__ sa) {
+    const int64_t r = blockIdx.x;
+    if (r >= post_padded[0]) return;
+    const float m = __uint_as_float(amax_rows[r]);
+    const float inv = (m > 0.f) ? 448.0f / m : 0.f;
+    if (threadIdx.x == 0) sa[r] = (m > 0.f) ? m / 448.0f : 1.0f;
+    const float* row = a + r * I;
+    for (int j = threadIdx.x * 8; j < I; j += kQuantThreads * 8) {
+        const f32x4_t v0 = *(const f32x4_t*)(row + j);
+        const f32x4_t v1 = *(const f32x4_t*)(row + j + 4);
+        uint2 o;
+        o.x = e4m3_pack4(v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv);
+        o.y = e4m3_pack4(v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv);
+        *(uint2*)(aq + r * I + j) = o;
+    }
+}
+
+// -------------------------------------------------------------------- host --
+static inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+
+int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C) {
+    if (w_dtype == 0) return align256(C * I * 4);
+    if (w_dtype == 1) return align256(C * I * 2);
+    return align256(T * H) + align256(T * 4) + align256(C * I * 4) + align256(C * 4) + align256(C * I) +
+           align256(C * 4);
+}
+
+static Fp8Ws fp8_ws(void* ws, int64_t T, int64_t H, int64_t I, int64_t C) {
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    Fp8Ws q;
+    q.xq = p; p += align256(T * H);
+    q.sx = (float*)p; p += align256(T * 4);
+    q.a = (float*)p; p += align256(C * I * 4);
+    q.amax = (uint32_t*)p; p += align256(C * 4);
+    q.aq = p; p += align256(C * I);
+    q.sa = (float*)p;
+    return q;
+}
+
+template <bool kFp8, int BM>
+static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream) {
+    constexpr int PF = 2;
+    const int nMB = (int)(a.C / BM);
+    const int nN1 = a.I / 128, nN2 = a.H / 256;
+    const int t1 = nMB * nN1, t2 = nMB * nN2;
+    hipError_t err;
+    Fp8Ws q{};
+    const uint8_t* h_in = static_cast<const uint8_t*>(ws);
+    if (kFp8) {
+        q = fp8_ws(ws, a.T, a.H, a.I, a.C);
+        if (a.T > 0)
+            hipLaunchKernelGGL(quant_tokens_kernel, dim3(a.T), dim3(kQuantThreads), 0, stream,
+                               (const uint16_t*)a.x, a.H, q.xq, q.sx, q.amax, a.C);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        h_in = q.aq;
+    }
+    if (t1 > 0)
+        hipLaunchKernelGGL((ffn_stage1<kFp8, BM, PF>), dim3(t1), dim3(kFfnThreads), 0, stream, a,
+                           (uint16_t*)ws, q, nN1, t1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (kFp8 && a.C > 0) {
+        hipLaunchKernelGGL(requant_rows_kernel, dim3((unsigned)a.C), dim3(kQuantThreads), 0, stream,
+                           (const float*)q.a, (const uint32_t*)q.amax, a.post_padded, a.I, q.aq, q.sa);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (t2 > 0)
+        hipLaunchKernelGGL((ffn_stage2<kFp8, BM, PF>), dim3(t2), dim3(kFfnThreads), 0, stream, a, h_in,
+                           (const float*)q.sa, nN2, t2);
+    return hipGetLastError();
+}
+
+template <bool kFp8>
+static hipError_t launch_mfma(const FfnArgs& a, void* ws, hipStream_t stream) {
+    switch (a.B) {
+        case 16: return launch_mfma_bm<kFp8, 16>(a, ws, stream);
+        case 32: return launch_mfma_bm<kFp8, 32>(a, ws, stream);
+        case 64: return launch_mfma_bm<kFp8, 64>(a, ws, stream);
+        case 128: return launch_mfma_bm<kFp8, 128>(a, ws, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream) { return launch_mfma<false>(a, ws, stream); }
+hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream) { return launch_mfma<true>(a, ws, stream); }
+
+}  // namespace moe

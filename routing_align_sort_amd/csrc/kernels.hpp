@@ -1,0 +1,65 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ----------------------------------------------------------------- routing --
+constexpr int kRouteMaxExperts = 1024;
+constexpr int kRouteMaxK = 64;
+constexpr int kRouteMaxGroups = 64;
+
+struct RouteArgs {
+    int T, E, K, score, n_group, topk_group, renormalize, append_shared;
+    float routed_scaling;
+    const float* logits;
+    const float* bias;
+    int32_t* topk_ids;
+    float* topk_weights;
+};
+hipError_t launch_route_topk(const RouteArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------- align&sort --
+constexpr int kAlignMaxExperts = 1024;
+constexpr int64_t kAlignSingleMaxSlots = 4096;   // one workgroup, one launch, up to here
+constexpr int64_t kAlignSlotsPerWg = 2048;       // target chunk of the multi-block path
+constexpr int kAlignMaxWg = 256;
+
+struct AlignPlan {
+    bool single;
+    int G;
+    int64_t chunk;
+    int64_t workspace_bytes;
+};
+AlignPlan align_plan(int64_t S, int E);
+hipError_t launch_align_sort(const int32_t* ids, int64_t S, int E, int B, int64_t C, int32_t* sorted,
+                             int32_t* expert_ids, int32_t* post_padded, int32_t* offsets,
+                             void* workspace, hipStream_t stream);
+
+// -------------------------------------------------------------- grouped FFN --
+struct FfnArgs {
+    int T, K, E, H, I, B;
+    int64_t S, C;              // slots, capacity (rows of the sorted layout)
+    const void* x;
+    const void* w13;
+    const float* w13_scale;
+    const void* w2;
+    const float* w2_scale;
+    const int32_t* sorted_ids;
+    const int32_t* expert_ids;
+    const int32_t* post_padded;
+    float* y_slots;
+};
+// Workspace layout per dtype path (bytes, each region 256-byte aligned).
+int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C);
+hipError_t launch_ffn_f32(const FfnArgs& a, void* ws, hipStream_t stream);
+hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream);
+hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream);
+
+// ----------------------------------------------------------------- combine --
+hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,
+                          const int32_t* ids, int out_bf16, void* out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,87 @@
+"""Shared helpers of the GPU parity tests (all comparisons are against the CPU oracle)."""
+import numpy as np
+import torch
+
+import moe_synth as ms
+import oracle
+import routing_align_sort_amd as moe
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 6e-2}
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    moe.load_library()              # fails loudly if the HIP library is not built
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """Bit patterns / values of a device tensor as the oracle takes them."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+ODT = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "e4m3"}
+INTER = {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3"}
+
+
+def oracle_tokens(x, w13, w2, ids, w, toks, w13_scale=None, w2_scale=None):
+    """Oracle FFN + combine for the tokens ``toks`` only.
+
+    Copies to the host just the expert slabs those tokens use (the inputs, as
+    the generator made them) and renumbers their ids.  Returns (out [n,H] f64,
+    y_slots [n*K,H] f32)."""
+    toks = np.asarray(toks)
+    E = w13.shape[0]
+    sub_ids = ids[toks]
+    used = sorted({int(e) for e in sub_ids.ravel() if 0 <= e < E})
+    remap = {e: i for i, e in enumerate(used)}
+    rid = np.array([[remap.get(int(e), -1) for e in row] for row in sub_ids], np.int32)
+    sel = torch.tensor(used, dtype=torch.long, device=w13.device)
+    w13h = host_bits(w13.index_select(0, sel)) if used else None
+    w2h = host_bits(w2.index_select(0, sel)) if used else None
+    s13 = s2 = None
+    if w13_scale is not None and used:
+        s13 = w13_scale.index_select(0, sel).cpu().numpy()
+        s2 = w2_scale.index_select(0, sel).cpu().numpy()
+    wdt = ODT[w13.dtype]
+    xdt = ODT[x.dtype]
+    xh = host_bits(x[torch.as_tensor(toks, device=x.device)])
+    if not used:
+        H = x.shape[1]
+        return np.zeros((len(toks), H)), np.zeros((len(toks) * ids.shape[1], H), np.float32)
+    out, y = oracle.moe_layer(xh, w13h, w2h, rid, w[toks], w_dtype=wdt, x_dtype=xdt,
+                              inter=INTER[wdt], w13_scale=s13, w2_scale=s2, E=len(used))
+    return out, y
+
+
+def route_oracle(cfg, L, K=None):
+    """The oracle's routing of a generated layer's logits."""
+    ids, w = oracle.route_topk(L["logits"].cpu().numpy(), K or cfg["K"], score=cfg["score"],
+                               bias=None if L["bias"] is None else L["bias"].cpu().numpy(),
+                               n_group=cfg["n_group"], topk_group=cfg["topk_group"],
+                               renormalize=cfg["renormalize"], append_shared=bool(cfg.get("shared")))
+    return ids, w
+
+
+def make_gpu_layer(cfg, L, B=None):
+    return moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B or cfg["B"],
+                        score=cfg["score"], n_group=cfg["n_group"], topk_group=cfg["topk_group"],
+                        renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
+                        w13_scale=L.get("w13_scale"), w2_scale=L.get("w2_scale"),
+                        x_dtype=L["x"].dtype,
+                        out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16)

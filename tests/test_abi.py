@@ -1,0 +1,109 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every function
+include/moe_mi355x.h declares, and its host-side validation and sizing work
+(none of these calls touches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routing_align_sort_amd as moe
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from routing_align_sort_amd import build
+        build.build()
+    return moe.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    assert set(names) == set(moe.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert moe.abi_version() == 1
+    assert moe.status_string(0) == "ok"
+    assert "workspace" in moe.status_string(3)
+    assert moe.status_string(99) == "unknown status"
+
+
+def test_capacity_matches_oracle_closed_form(lib):
+    for T, K, E, B in [(0, 1, 1, 1), (1, 1, 1, 16), (16384, 8, 256, 64), (64, 8, 256, 16),
+                       (2048, 2, 33, 32), (5, 3, 1024, 128), (3, 2, 7, 5)]:
+        assert moe.moe_align_sort_capacity(T, K, E, B) == oracle.align_capacity(T * K, E, B)
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    P = ctypes.c_void_p
+    assert lib.moe_align_sort_capacity(-1, 1, 1, 1) == -1
+    assert lib.moe_align_sort_capacity(1, 0, 1, 1) == -1
+    assert lib.moe_align_sort_workspace_bytes(1, 1, 0, 1) == -1
+    # E beyond the built limit
+    st = lib.moe_align_sort(None, 1, 1, 2000, 1, None, None, P(8), None, None, 0, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
+    # null output pointer
+    st = lib.moe_align_sort(P(8), 4, 2, 8, 16, None, P(8), P(8), None, None, 0, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    # the multi-block path needs a workspace
+    need = lib.moe_align_sort_workspace_bytes(16384, 8, 256, 64)
+    assert need > 0
+    st = lib.moe_align_sort(P(8), 16384, 8, 256, 64, P(8), P(8), P(8), None, None, need - 1, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_align_sort_workspace_bytes(64, 8, 256, 16) == 0     # one workgroup, no workspace
+
+
+def test_route_validation(lib):
+    p = moe._RouteParams(4, 256, 8, 1, 8, 4, 1, 1.0, 0)
+    P = ctypes.c_void_p
+    p.K = 0
+    assert lib.moe_route_topk(ctypes.byref(p), P(8), None, P(8), P(8), None) == moe.MOE_ERR_INVALID_ARG
+    p.K = 8; p.n_group = 7
+    assert lib.moe_route_topk(ctypes.byref(p), P(8), None, P(8), P(8), None) == moe.MOE_ERR_INVALID_ARG
+    p.n_group = 8; p.topk_group = 1; p.K = 33                # only 32 experts eligible
+    assert lib.moe_route_topk(ctypes.byref(p), P(8), None, P(8), P(8), None) == moe.MOE_ERR_INVALID_ARG
+    p.topk_group = 4; p.K = 8; p.E = 2048; p.n_group = 8
+    assert lib.moe_route_topk(ctypes.byref(p), P(8), None, P(8), P(8), None) == moe.MOE_ERR_UNSUPPORTED
+    p.E = 256; p.T = 0
+    assert lib.moe_route_topk(ctypes.byref(p), None, None, None, None, None) == moe.MOE_OK
+
+
+def test_ffn_validation_and_workspace(lib):
+    import torch
+    ws = moe.moe_grouped_ffn_workspace_bytes(2048, 1, 32, 7168, 2048, 64, torch.bfloat16, torch.bfloat16)
+    C = oracle.align_capacity(2048, 32, 64)
+    assert ws >= C * 2048 * 2
+    with pytest.raises(moe.MoEError):
+        moe.moe_grouped_ffn_workspace_bytes(64, 2, 8, 128, 256, 48, torch.bfloat16, torch.bfloat16)
+    with pytest.raises(moe.MoEError):       # H not a multiple of the tile
+        moe.moe_grouped_ffn_workspace_bytes(64, 2, 8, 100, 256, 16, torch.bfloat16, torch.bfloat16)
+    with pytest.raises(moe.MoEError):       # fp8 activations are not a built combination
+        moe.moe_grouped_ffn_workspace_bytes(64, 2, 8, 256, 256, 16, torch.float8_e4m3fn,
+                                            torch.float8_e4m3fn)
+    p = moe._FfnParams(64, 2, 8, 256, 256, 16, 1, 1)
+    P = ctypes.c_void_p
+    st = lib.moe_grouped_ffn(ctypes.byref(p), P(8), P(8), None, P(8), None, P(8), P(8), P(8), P(8),
+                             P(8), 10, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    p.w_dtype = 2
+    st = lib.moe_grouped_ffn(ctypes.byref(p), P(8), P(8), None, P(8), None, P(8), P(8), P(8), P(8),
+                             P(8), 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG        # fp8 needs its scales
+    assert lib.moe_combine(4, 2, 8, 6, P(8), P(8), P(8), 1, P(8), None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(4, 2, 8, 8, P(8), P(8), P(8), 7, P(8), None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(0, 2, 8, 8, None, None, None, 1, None, None) == moe.MOE_OK

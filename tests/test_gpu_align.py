@@ -1,0 +1,80 @@
+"""Align & Sort on the GPU, bit-exact against the oracle's stable counting sort
+(full buffers: sorted_token_ids, expert_ids, num_tokens_post_padded, offsets)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+import routing_align_sort_amd as moe
+from gpu_helpers import device, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_compare(ids_np, E, B, label=""):
+    dev = device()
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).to(dev)
+    say(f"align {label}: T,K={ids_np.shape} E={E} B={B}")
+    r = moe.moe_align_sort(ids, E, B)
+    torch.cuda.synchronize()
+    ref = oracle.align_sort(ids_np, E, B)
+    assert int(r["num_tokens_post_padded"].item()) == ref["num_tokens_post_padded"], label
+    assert np.array_equal(r["expert_offsets"].cpu().numpy(), ref["expert_offsets"]), label
+    assert np.array_equal(r["expert_ids"].cpu().numpy(), ref["expert_ids"]), label
+    got = r["sorted_token_ids"].cpu().numpy()
+    want = ref["sorted_token_ids"]
+    if not np.array_equal(got, want):
+        bad = np.flatnonzero(got != want)
+        raise AssertionError(f"{label}: {bad.size} positions differ, first {bad[:8]} "
+                             f"got {got[bad[:8]]} want {want[bad[:8]]}")
+    return r
+
+
+def test_align_16k_top8_of_256_block64():
+    cfg = ms.CONFIGS["align_16k"]
+    ids = ms.zipf_topk_ids(0, ms.TAG_IDS, cfg["T"], cfg["K"], cfg["E"], cfg["zipf_s"])
+    run_and_compare(ids, cfg["E"], cfg["B"], "16384x8/256 Zipf1.1")
+
+
+@pytest.mark.parametrize("T", [64, 1024, 131072, 1048576])
+def test_align_size_sweep(T):
+    ids = ms.zipf_topk_ids(0, ms.TAG_IDS, T, 8, 256, 1.1)
+    run_and_compare(ids, 256, 64, f"sweep T={T}")
+
+
+@pytest.mark.parametrize("B", [1, 16, 32, 64, 128])
+def test_align_decode_and_prefill_shapes(B):
+    rng = np.random.default_rng(B)
+    run_and_compare(rng.integers(0, 256, size=(64, 8)).astype(np.int32), 256, B, "decode 64x8")
+    run_and_compare(rng.integers(0, 33, size=(2048, 2)).astype(np.int32), 33, B, "prefill 2048x2/33")
+
+
+def test_align_random_shapes_and_edges():
+    rng = np.random.default_rng(7)
+    cases = []
+    for T in (0, 1, 2, 3, 17, 511, 512, 513, 4095, 4097, 20000):
+        for K in (1, 2, 8):
+            E = int(rng.choice([1, 2, 8, 33, 256, 1024]))
+            B = int(rng.choice([1, 2, 16, 64, 128, 3]))
+            ids = rng.integers(-2, E + 3, size=(T, K)).astype(np.int32)      # some out of range
+            cases.append((ids, E, B))
+    # single- / multi-workgroup threshold: S = 4096 and 4097 slots
+    cases.append((rng.integers(0, 64, size=(4096, 1)).astype(np.int32), 64, 16))
+    cases.append((rng.integers(0, 64, size=(4097, 1)).astype(np.int32), 64, 16))
+    # every id out of range; one expert takes everything; max experts
+    cases.append((np.full((300, 4), 9, np.int32), 8, 16))
+    cases.append((np.zeros((50000, 2), np.int32), 4, 64))
+    cases.append((rng.integers(0, 1024, size=(30000, 8)).astype(np.int32), 1024, 32))
+    for n, (ids, E, B) in enumerate(cases):
+        run_and_compare(ids, E, B, f"case {n}")
+
+
+def test_align_is_deterministic():
+    ids_np = ms.zipf_topk_ids(1, ms.TAG_IDS, 16384, 8, 256, 1.1)
+    dev = device()
+    ids = torch.from_numpy(ids_np).to(dev)
+    first = moe.moe_align_sort(ids, 256, 64)["sorted_token_ids"].clone()
+    for _ in range(10):
+        again = moe.moe_align_sort(ids, 256, 64)["sorted_token_ids"]
+        assert torch.equal(first, again)

@@ -1,0 +1,151 @@
+"""The grouped FFN and the whole layer (route -> align -> FFN -> combine) on the
+GPU against the oracle: max|gpu - oracle| <= tol * max|oracle| with tol 1e-4
+(fp32), 2e-2 (bf16), 6e-2 (fp8); full-size workloads are compared on a seeded
+sample of tokens, small ones on every token."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+import routing_align_sort_amd as moe
+from gpu_helpers import (TOL, device, make_gpu_layer, oracle_tokens, rel_err, route_oracle, say,
+                         host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_layer(cfg, L, B=None):
+    layer = make_gpu_layer(cfg, L, B)
+    out = layer.forward(L["x"], L["logits"], L["bias"])
+    torch.cuda.synchronize()
+    return layer, out
+
+
+def check_layer(cfg, L, toks, B=None, label=""):
+    dev = device()
+    layer, out = run_layer(cfg, L, B)
+    ids, w = route_oracle(cfg, L)
+    gid = layer.topk_ids.cpu().numpy()
+    assert np.array_equal(gid, ids), f"{label}: routing differs"
+    assert np.allclose(layer.topk_weights.cpu().numpy(), w, rtol=1e-6, atol=0)
+    al = oracle.align_sort(ids, layer.E_slabs, layer.B)
+    assert np.array_equal(layer.sorted.cpu().numpy(), al["sorted_token_ids"]), f"{label}: align"
+    assert int(layer.ntpp.item()) == al["num_tokens_post_padded"]
+    ref, yref = oracle_tokens(L["x"], L["w13"], L["w2"], ids, w, toks, L.get("w13_scale"),
+                              L.get("w2_scale"))
+    got = out[torch.as_tensor(toks, device=dev)].float().cpu().numpy()
+    err = rel_err(got, ref)
+    K = ids.shape[1]
+    slots = (np.asarray(toks)[:, None] * K + np.arange(K)[None]).ravel()
+    valid = (ids[toks].ravel() >= 0)
+    yerr = rel_err(layer.y_slots[torch.as_tensor(slots, device=dev)].cpu().numpy()[valid], yref[valid])
+    say(f"{label}: out rel err {err:.3e}  y_slots rel err {yerr:.3e}  (tol {TOL[cfg['dtype']]})")
+    assert err <= TOL[cfg["dtype"]], err
+    return layer, out
+
+
+def test_layer_tiny_fp32():
+    dev = device()
+    cfg = ms.CONFIGS["tiny_fp32"]
+    L = ms.make_layer(cfg, device=dev)
+    check_layer(cfg, L, np.arange(cfg["T"]), label="tiny fp32 B=16")
+
+
+@pytest.mark.parametrize("B", [16, 32, 64, 128])
+def test_layer_small_bf16_all_tokens(B):
+    dev = device()
+    cfg = ms.scaled("decode_bf16", T=300, H=512, I=384, E=16, K=4, n_group=4, topk_group=2)
+    L = ms.make_layer(cfg, device=dev)
+    check_layer(cfg, L, np.arange(cfg["T"]), B=B, label=f"small bf16 B={B}")
+
+
+@pytest.mark.parametrize("B", [16, 32, 64, 128])
+def test_layer_small_fp8_all_tokens(B):
+    dev = device()
+    cfg = ms.scaled("prefill_fp8", T=333, H=768, I=256, E=12)
+    L = ms.make_layer(cfg, device=dev)
+    check_layer(cfg, L, np.arange(cfg["T"]), B=B, label=f"small fp8 B={B}")
+
+
+def test_ffn_output_is_block_size_invariant():
+    dev = device()
+    for name in ("decode_bf16", "prefill_fp8"):
+        cfg = ms.scaled(name, T=200, H=256, I=256, E=8, K=2, n_group=2, topk_group=2)
+        if name == "prefill_fp8":
+            cfg = ms.scaled(name, T=200, H=256, I=256, E=8)
+        L = ms.make_layer(cfg, device=dev)
+        ys = []
+        for B in (16, 32, 64, 128):
+            layer, _ = run_layer(cfg, L, B)
+            ys.append(layer.y_slots.clone())
+        for y in ys[1:]:
+            assert torch.equal(y, ys[0]), name
+
+
+def test_fp8_token_quantisation_codes_match_oracle():
+    dev = device()
+    cfg = ms.scaled("prefill_fp8", T=257, H=1024, I=256, E=4)
+    L = ms.make_layer(cfg, device=dev)
+    layer, _ = run_layer(cfg, L)
+    T, H = cfg["T"], cfg["H"]
+    ws = layer.ws_ffn.cpu().numpy()
+    codes = ws[:T * H].reshape(T, H)                         # workspace region 0: x codes
+    off = (T * H + 255) // 256 * 256
+    scales = ws[off:off + 4 * T].view(np.float32)             # region 1: per-token scales
+    q, s = oracle.quant_tokens_e4m3(host_bits(L["x"]))
+    assert np.array_equal(scales, s)
+    same = (codes == q) | (((codes & 0x7F) == 0) & ((q & 0x7F) == 0))   # +0 / -0 alike
+    assert same.all(), f"{(~same).sum()} codes differ"
+
+
+def test_generator_device_matches_host():
+    dev = device()
+    cfg = ms.scaled("prefill_fp8", H=256, I=128, E=3)
+    g = ms.make_weights(cfg, device=dev)
+    h = ms.make_weights(cfg, device="cpu")
+    for k in ("w13", "w2"):
+        assert np.array_equal(host_bits(g[k]), host_bits(h[k]))
+    for k in ("w13_scale", "w2_scale"):
+        assert torch.equal(g[k].cpu(), h[k])
+    cfg = ms.scaled("decode_bf16", H=256, I=128, E=2)
+    assert torch.equal(ms.make_layer(cfg, device=dev)["x"].cpu().view(torch.int16),
+                       ms.make_layer(cfg, device="cpu")["x"].view(torch.int16))
+
+
+# ----------------------------------------------------------- full-size shapes --
+def sample_tokens(T, n, seed=0):
+    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+
+
+def test_layer_decode_bf16_full_size():
+    dev = device()
+    cfg = ms.CONFIGS["decode_bf16"]
+    say("generating DeepSeek-V3-shaped decode weights (256 experts, 22.5 GB bf16)")
+    L = ms.make_layer(cfg, device=dev)
+    for B in (16, 32):
+        check_layer(cfg, L, sample_tokens(cfg["T"], 8, B), B=B, label=f"decode bf16 B={B}")
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_layer_prefill_bf16_full_size():
+    dev = device()
+    cfg = ms.CONFIGS["prefill_bf16"]
+    say("generating prefill bf16 weights (32 experts, 2.8 GB)")
+    L = ms.make_layer(cfg, device=dev)
+    for B in (32, 64, 128):
+        check_layer(cfg, L, sample_tokens(cfg["T"], 48, B), B=B, label=f"prefill bf16 B={B}")
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_layer_prefill_fp8_full_size():
+    dev = device()
+    cfg = ms.CONFIGS["prefill_fp8"]
+    say("generating prefill fp8 weights (32 + 1 shared experts, 1.45 GB)")
+    L = ms.make_layer(cfg, device=dev)
+    for B in (32, 64, 128):
+        check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill fp8 B={B}")
+    del L
+    torch.cuda.empty_cache()
