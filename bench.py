@@ -1,4 +1,37 @@
-"""MoE layer benchmark on one MI355X (filled in with the HIP path)."""
+#!/usr/bin/env python3
+"""MoE FFN layer benchmark on one MI355X.
+
+A step is one pass of the whole layer -- top-k routing, Align & Sort, the
+grouped SwiGLU FFN (gate/up, down) and the weighted combine -- over one batch
+of seeded synthetic input already resident in HBM.  The default workload is the
+one-GPU expert-parallel prefill share: 2048 tokens, each routed to one of 32
+local experts (64 per expert), hidden 7168, expert intermediate 2048, bf16,
+block_size_m 64.
+
+Prints ONE JSON line.  `value` is layer tokens/s; per-kernel durations come
+from HIP events recorded on the launch stream around every kernel inside the
+timed steps; `roofline` is for the dominant kernel (the gate/up GEMM);
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload prefill_bf16] [--B 64]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                                   # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
+ESZ = {"f32": 4, "bf16": 2, "e4m3": 1}
+DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "e4m3": "fp8_e4m3"}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def layer_flops(slots: int, hidden: int, inter: int) -> int:
@@ -6,3 +39,321 @@ def layer_flops(slots: int, hidden: int, inter: int) -> int:
     gate+up is a [slots,H]x[H,2I] GEMM (2*H*2I flops per slot) and down a
     [slots,I]x[I,H] GEMM (2*I*H per slot): 6*H*I per slot."""
     return 6 * slots * hidden * inter
+
+
+def algorithmic_bytes(cfg, ids_np, E_slabs):
+    """Bytes the method itself must move per kernel (each counted once):
+    gate/up: W13 of every expert hit (+ its fp32 row scales) and x;
+    down: W2 of every expert hit (+ scales) and the fp32 y_slots rows written;
+    combine: y_slots read, out written (bf16 / fp32)."""
+    import numpy as np
+    T, H, I = cfg["T"], cfg["H"], cfg["I"]
+    dt = cfg["dtype"]
+    e = ESZ[dt]
+    flat = ids_np.ravel()
+    hit = np.unique(flat[(flat >= 0) & (flat < E_slabs)])
+    D = int(hit.size)
+    S_valid = int(((flat >= 0) & (flat < E_slabs)).sum())
+    xb = T * H * (4 if dt == "f32" else 2)
+    sc = 4 if dt == "e4m3" else 0
+    out_b = T * H * (4 if dt == "f32" else 2)
+    return {
+        "experts_hit": D,
+        "stage1": D * 2 * I * H * e + D * 2 * I * sc + xb,
+        "stage2": D * H * I * e + D * H * sc + S_valid * H * 4,
+        "combine": S_valid * H * 4 + out_b,
+        "weights": D * 3 * I * H * e,
+        "slots": S_valid,
+    }
+
+
+def _mean(v):
+    return sum(v) / len(v) if v else 0.0
+
+
+def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
+    """Generate one workload, run `warmup` + `steps` layer passes with events
+    around every kernel; return timings and what the roofline needs."""
+    import torch
+
+    import moe_synth as ms
+    import routing_align_sort_amd as moe
+
+    L = ms.make_layer(cfg, device=dev, seed=seed)
+    layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"],
+                         n_group=cfg["n_group"], topk_group=cfg["topk_group"],
+                         renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
+                         w13_scale=L.get("w13_scale"), w2_scale=L.get("w2_scale"),
+                         x_dtype=L["x"].dtype,
+                         out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16)
+    x, logits, bias = L["x"], L["logits"], L["bias"]
+    NE = 9
+    ev = moe.HipEvents(NE * max(steps, 1))
+    for _ in range(warmup):
+        layer.forward(x, logits, bias)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        b = NE * s
+        ev.record(b + 0)
+        layer.route(logits, bias)
+        ev.record(b + 1)
+        layer.align()
+        ev.record(b + 2)
+        layer.ffn(x, stage_events=ev.handles[b + 3:b + 8])
+        layer.combine()
+        ev.record(b + 8)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["route", "align", None, "quant", "gate_up", "requant", "down", "combine"]
+    per = {n: [] for n in names if n}
+    total = []
+    for s in range(steps):
+        b = NE * s
+        for i, n in enumerate(names):
+            if n:
+                per[n].append(ev.elapsed_ms(b + i, b + i + 1) * 1e3)
+        total.append(ev.elapsed_ms(b, b + 8) * 1e3)
+    ev.close()
+    ids_np = layer.topk_ids.cpu().numpy()
+    res = {
+        "wall_s": wall,
+        "us": {n: _mean(v) for n, v in per.items()},
+        "us_step_events": _mean(total),
+        "P": int(layer.ntpp.item()),
+        "ids": ids_np,
+        "weights_np": layer.topk_weights.cpu().numpy(),
+        "E_slabs": layer.E_slabs,
+        "L": L,
+        "layer": layer,
+    }
+    return res
+
+
+def summarize(cfg, B, r):
+    ab = algorithmic_bytes(cfg, r["ids"], r["E_slabs"])
+    us = r["us"]
+    flops = layer_flops(ab["slots"], cfg["H"], cfg["I"])
+    gemm_us = us["gate_up"] + us["down"]
+    dt = cfg["dtype"]
+    return {
+        "block_size_m": B,
+        "tokens_per_s": cfg["T"] / (r["us_step_events"] * 1e-6),
+        "us_per_step": r["us_step_events"],
+        "us": {k: round(v, 2) for k, v in us.items()},
+        "experts_hit": ab["experts_hit"],
+        "num_tokens_post_padded": r["P"],
+        "grouped_gemm_tflops": flops / (gemm_us * 1e-6) / 1e12,
+        "grouped_gemm_mfma_frac": flops / (gemm_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[dt],
+        "gate_up_hbm_gbs": ab["stage1"] / (us["gate_up"] * 1e-6) / 1e9,
+        "down_hbm_gbs": ab["stage2"] / (us["down"] * 1e-6) / 1e9,
+        "weights_gb": ab["weights"] / 1e9,
+        "layer_weight_stream_frac": ab["weights"] / (r["us_step_events"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+    }
+
+
+def align_only(dev, iters=200):
+    """Align & Sort alone on 16384 tokens x top-8 of 256 experts (Zipf 1.1), block 64."""
+    import numpy as np
+    import torch
+
+    import moe_synth as ms
+    import routing_align_sort_amd as moe
+
+    cfg = ms.CONFIGS["align_16k"]
+    ids_np = ms.zipf_topk_ids(0, ms.TAG_IDS, cfg["T"], cfg["K"], cfg["E"], cfg["zipf_s"])
+    ids = torch.from_numpy(ids_np).to(dev)
+    E, B = cfg["E"], cfg["B"]
+    ws_b = moe.moe_align_sort_workspace_bytes(cfg["T"], cfg["K"], E, B)
+    ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=dev)
+    out = moe.moe_align_sort(ids, E, B, workspace=ws)            # allocates the outputs once
+    ev = moe.HipEvents(2 * iters)
+    for _ in range(20):
+        moe.moe_align_sort(ids, E, B, workspace=ws, **out)
+    torch.cuda.synchronize()
+    for i in range(iters):
+        ev.record(2 * i)
+        moe.moe_align_sort(ids, E, B, workspace=ws, **out)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    t = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(iters))
+    ev.close()
+    P = int(out["num_tokens_post_padded"].item())
+    S = ids_np.size
+    C = out["sorted_token_ids"].numel()
+    # algorithmic bytes: ids read, sorted_token_ids written up to capacity, expert_ids written
+    nbytes = 4 * S + 4 * C + 4 * (C // B)
+    med = t[len(t) // 2]
+    return {"workload": "16384 tokens x top-8 of 256 experts, Zipf(1.1), block_size_m 64",
+            "us_median": round(med, 2), "us_p10": round(t[len(t) // 10], 2),
+            "us_p90": round(t[9 * len(t) // 10], 2), "num_tokens_post_padded": P,
+            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (med * 1e-6) / 1e9, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--B", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the align-only and secondary-workload figures")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); multi-GPU sharding is described in DESIGN.md, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_synth as ms
+    import routing_align_sort_amd as moe
+    if not os.path.exists(moe.LIB_PATH):
+        from routing_align_sort_amd import build as hip_build
+        hip_build.build()
+    moe.load_library()
+    dev = torch.device("cuda:0")
+    cfg = ms.CONFIGS[args.workload]
+    B = args.B or cfg["B"]
+
+    r = run_layer_timed(cfg, B, args.steps, args.warmup, dev)
+    summ = summarize(cfg, B, r)
+    ab = algorithmic_bytes(cfg, r["ids"], r["E_slabs"])
+    ms_per_step = r["wall_s"] / args.steps * 1e3
+    value = cfg["T"] * args.steps / r["wall_s"]
+    st1_us = r["us"]["gate_up"]
+    achieved = ab["stage1"] / (st1_us * 1e-6) / 1e9
+    roofline = {"kernel": "ffn_stage1 (gate/up GEMM + SiLU*up)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload, B),
+                "algorithmic_bytes_per_launch": ab["stage1"], "avg_launch_us": round(st1_us, 2)}
+    line = {
+        "metric": "MoE layer tokens/s + grouped-GEMM TFLOPS (% MFMA peak); align-sort us",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[cfg["dtype"]],
+        "data": "synthetic (seeded counter-based generator; random-init expert weights)",
+        "config": {"workload": describe(args.workload, cfg, B), "tokens": cfg["T"],
+                   "experts": cfg["E"], "top_k": cfg["K"], "hidden": cfg["H"], "inter": cfg["I"],
+                   "block_size_m": B, "shared_expert": bool(cfg.get("shared"))},
+        "layer": summ,
+        "roofline": roofline,
+    }
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        line["align_sort_16k"] = align_only(dev)
+        extra = {}
+        for name in ("prefill_fp8", "decode_bf16"):
+            if name == args.workload:
+                continue
+            c2 = ms.CONFIGS[name]
+            r2 = run_layer_timed(c2, c2["B"], 10, 3, dev)
+            extra[name] = {"workload": describe(name, c2, c2["B"]), **summarize(c2, c2["B"], r2)}
+            del r2
+            torch.cuda.empty_cache()
+        line["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(cfg, B, dev)
+    print(json.dumps(line), flush=True)
+
+
+def describe(name, cfg, B):
+    if name == "align_16k":
+        return "align-sort 16384x8 over 256 experts"
+    s = f"{name}: {cfg['T']} tokens x top-{cfg['K']} of {cfg['E']} experts"
+    if cfg.get("shared"):
+        s += " + 1 shared expert"
+    s += f", hidden {cfg['H']}, inter {cfg['I']}, SwiGLU, {cfg['dtype']}, block_size_m {B}"
+    return s
+
+
+def measured_traffic(workload, B):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(PROFILE_DIR, f"ffn_stage1_{workload}_B{B}_counters.json")
+    src = os.path.join(ROOT, "routing_align_sort_amd", "csrc", "ffn_mfma.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_cpu_baseline(cfg, B, dev, budget_s=12.0):
+    """The CPU oracle as it stands, on a bounded sample of the same workload:
+    routing and Align & Sort over all tokens, then the expert FFN + combine of
+    a seeded sample of tokens sized to ~budget_s of CPU time; tokens/s is the
+    per-token cost extrapolated to the whole batch."""
+    import numpy as np
+    import torch
+
+    import moe_synth as ms
+    import oracle
+
+    L = ms.make_layer(cfg, device="cpu", weights=False)
+    logits = L["logits"].numpy()
+    bias = None if L["bias"] is None else L["bias"].numpy()
+    T = cfg["T"]
+    t0 = time.perf_counter()
+    ids, w = oracle.route_topk(logits, cfg["K"], score=cfg["score"], bias=bias,
+                               n_group=cfg["n_group"], topk_group=cfg["topk_group"],
+                               renormalize=cfg["renormalize"],
+                               append_shared=bool(cfg.get("shared")))
+    E_slabs = cfg["E"] + (1 if cfg.get("shared") else 0)
+    oracle.align_sort(ids, E_slabs, B)
+    t_ra = time.perf_counter() - t0
+
+    # host copies of the inputs (generated on the GPU, bit-identical to the host generator)
+    G = ms.make_weights(cfg, device=dev)
+    hb = lambda t: (t.cpu().view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16
+                    else t.cpu().view(torch.uint8).numpy() if t.dtype == torch.float8_e4m3fn
+                    else t.cpu().numpy())
+    w13, w2 = hb(G["w13"]), hb(G["w2"])
+    s13 = G["w13_scale"].cpu().numpy() if "w13_scale" in G else None
+    s2 = G["w2_scale"].cpu().numpy() if "w2_scale" in G else None
+    del G
+    torch.cuda.empty_cache()
+    x = L["x"]
+    xh = hb(x)
+    wdt = cfg["dtype"]
+    xdt = "f32" if wdt == "f32" else "bf16"
+    rng = np.random.default_rng(0)
+    order = rng.permutation(T)
+
+    def ffn(toks):
+        t1 = time.perf_counter()
+        oracle.moe_layer(xh[toks], w13, w2, ids[toks], w[toks], w_dtype=wdt, x_dtype=xdt,
+                         inter=wdt, w13_scale=s13, w2_scale=s2, E=E_slabs)
+        return time.perf_counter() - t1
+
+    n0 = 2
+    t_probe = ffn(np.sort(order[:n0]))
+    n = int(min(T, max(n0, budget_s / max(t_probe / n0, 1e-9))))
+    t_ffn = ffn(np.sort(order[:n]))
+    per_token = t_ra / T + t_ffn / n
+    return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"routing + Align & Sort over all {T} tokens ({t_ra:.3f} s), expert FFN + "
+                      f"combine for {n} seeded tokens ({t_ffn:.2f} s), double precision; "
+                      f"tokens/s extrapolated per token"}
+
+
+if __name__ == "__main__":
+    main()

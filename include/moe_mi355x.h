@@ -166,13 +166,18 @@ moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32
  * moe_align_sort with the same T,K,E,B; y_slots device fp32 [T*K,H] (out);
  * workspace device, at least moe_grouped_ffn_workspace_bytes(p), 256-byte
  * aligned, clobbered.
+ * weight_layout MOE_LAYOUT_PACKED means w13 and w2 were rewritten by
+ * moe_prepack_weights (below); the scales stay in their canonical layout.
  * Limits: B in {16,32,64,128}; H a multiple of 256 and I a multiple of 128
- * (fp32: multiples of 64); E <= 1024.
+ * (fp32: multiples of 64, canonical layout only); E <= 1024.
  */
+typedef enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layout_t;
+
 typedef struct {
     int32_t T, K, E, H, I, B;
     int32_t w_dtype;           /* moe_dtype_t */
     int32_t x_dtype;           /* moe_dtype_t */
+    int32_t weight_layout;     /* moe_weight_layout_t of w13 and w2 */
 } moe_ffn_params_t;
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);
@@ -181,6 +186,34 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t *p, const void *x, const voi
                              const int32_t *sorted_token_ids, const int32_t *expert_ids,
                              const int32_t *num_tokens_post_padded, float *y_slots,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One-time weight preparation, off the per-token path: rewrites canonical
+ * w13 [E,2I,H] and w2 [E,H,I] (bf16 or E4M3, per p->w_dtype; uses p->E, H, I)
+ * into the packed layout (same byte sizes) that moe_grouped_ffn streams with
+ * one contiguous 1 KB read per load instruction.  The packed layout is a
+ * permutation of the bytes, private to this library: produce it only with
+ * this call.  Outputs must not alias the inputs.  MOE_ERR_UNSUPPORTED for fp32.
+ */
+moe_status_t moe_prepack_weights(const moe_ffn_params_t *p, const void *w13, const void *w2,
+                                 void *w13_packed, void *w2_packed, void *stream);
+
+/*
+ * Profiling form of moe_grouped_ffn: the same work and results, plus five
+ * caller-created hipEvent_t handles (events[0..4], passed as void*) recorded on
+ * the stream at the stage boundaries -- [0] before the per-token activation
+ * quantisation, [1] before the gate/up GEMM, [2] after it, [3] before the down
+ * GEMM (after the intermediate's requantisation), [4] after the down GEMM.
+ * Stages a dtype path does not have take no time.  For callers that time the
+ * stages; the events are only recorded, never created or destroyed here.
+ * A NULL array or handle is MOE_ERR_INVALID_ARG.
+ */
+moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t *p, const void *x, const void *w13,
+                                      const float *w13_scale, const void *w2, const float *w2_scale,
+                                      const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                                      const int32_t *num_tokens_post_padded, float *y_slots,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      void *const *events);
 
 /* ------------------------------------------------------------------------ */
 /* Top-k weighted combine                                                    */

@@ -308,9 +308,13 @@ def _quantise_rows_e4m3_input(w: torch.Tensor):
     (The library receives the weights already in this form.)"""
     amax = w.abs().amax(dim=1)
     amax = torch.where(amax > 0, amax, torch.ones_like(amax))
-    inv = torch.tensor(448.0, dtype=torch.float32, device=w.device) / amax
+    # tensor / tensor divisions: torch turns a division by a Python scalar into
+    # a multiply by its reciprocal on the GPU, which would break host/device
+    # bit-identity
+    c448 = torch.tensor(448.0, dtype=torch.float32, device=w.device)
+    inv = c448 / amax
     q = (w * inv[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-    return q, amax / 448.0
+    return q, amax / c448
 
 
 def scaled(cfg_name, **over):

@@ -75,6 +75,7 @@ def _load():
     lib.oracle_expert_ffn.restype = i32
     lib.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
     lib.oracle_combine.restype = i32
+    lib.oracle_num_threads.restype = i32
     _lib = lib
     return lib
 
@@ -85,6 +86,11 @@ def _ptr(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    """Threads of the oracle's OpenMP loop over token slots."""
+    return int(_load().oracle_num_threads())
 
 
 # ---------------------------------------------------------------- codecs ----

@@ -26,9 +26,13 @@
  * operation), so both sides see the same bits.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the oracle's parallel loop uses (reported with its timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */

@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+# MOE_LIB_PATH selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
@@ -38,12 +39,13 @@ class _RouteParams(ctypes.Structure):
 class _FfnParams(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("B", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
-            "moe_grouped_ffn", "moe_combine")
+            "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_prepack_weights", "moe_combine")
 
 
 def load_library(path: str = LIB_PATH):
@@ -70,6 +72,11 @@ def load_library(path: str = LIB_PATH):
     lib.moe_grouped_ffn_workspace_bytes.restype = i64
     lib.moe_grouped_ffn.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P, P, P, P, P, P, sz, P]
     lib.moe_grouped_ffn.restype = i32
+    lib.moe_grouped_ffn_profiled.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P, P, P, P, P, P,
+                                             sz, P, P]
+    lib.moe_grouped_ffn_profiled.restype = i32
+    lib.moe_prepack_weights.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P]
+    lib.moe_prepack_weights.restype = i32
     lib.moe_combine.argtypes = [i32, i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_combine.restype = i32
     _lib = lib
@@ -183,8 +190,27 @@ def moe_align_sort(topk_ids, E, B, *, sorted_token_ids=None, expert_ids=None,
 _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
 
 
-def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype):
-    return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype])
+MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PACKED = 0, 1
+
+
+def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False):
+    return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype],
+                      MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_CANONICAL)
+
+
+def moe_prepack_weights(w13, w2, *, stream=None):
+    """One-time rewrite of canonical expert weights into the packed streaming
+    layout; returns (w13_packed, w2_packed), same shapes and dtype (opaque)."""
+    lib = load_library()
+    E, I2, H = w13.shape
+    _need(w13, w13.dtype, "w13")
+    _need(w2, w13.dtype, "w2", E * H * (I2 // 2))
+    p13 = torch.empty_like(w13)
+    p2 = torch.empty_like(w2)
+    p = _ffn_params(1, 1, E, H, I2 // 2, 16, w13.dtype, torch.bfloat16)
+    _check("moe_prepack_weights", lib.moe_prepack_weights(ctypes.byref(p), _ptr(w13), _ptr(w2),
+                                                          _ptr(p13), _ptr(p2), _stream(stream)))
+    return p13, p2
 
 
 def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype) -> int:
@@ -196,8 +222,12 @@ def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype) -> int:
 
 
 def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, *, K, B,
-                    w13_scale=None, w2_scale=None, y_slots=None, workspace=None, stream=None):
-    """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots fp32 [T*K, H]."""
+                    w13_scale=None, w2_scale=None, y_slots=None, workspace=None, stream=None,
+                    stage_events=None, packed=False):
+    """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots fp32 [T*K, H].
+
+    stage_events: optional 5 raw hipEvent_t handles (ints) recorded at the stage
+    boundaries (the profiling entry point)."""
     lib = load_library()
     T, H = x.shape
     E, I2, H2 = w13.shape
@@ -216,15 +246,19 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     if y_slots is None:
         y_slots = torch.empty((T * K, H), dtype=torch.float32, device=x.device)
     _need(y_slots, torch.float32, "y_slots", T * K * H)
-    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype)
+    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed)
     need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check("moe_grouped_ffn", lib.moe_grouped_ffn(
-        ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
-        _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(y_slots),
-        _ptr(workspace), ws_bytes, _stream(stream)))
+    args = (ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+            _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(y_slots),
+            _ptr(workspace), ws_bytes, _stream(stream))
+    if stage_events is None:
+        _check("moe_grouped_ffn", lib.moe_grouped_ffn(*args))
+    else:
+        ev = (ctypes.c_void_p * 5)(*stage_events)
+        _check("moe_grouped_ffn_profiled", lib.moe_grouped_ffn_profiled(*args, ev))
     return y_slots
 
 
@@ -257,8 +291,13 @@ class MoELayer:
 
     def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
-                 w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16):
+                 w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None):
         dev = w13.device
+        if packed is None:
+            packed = w13.dtype != torch.float32
+        self.packed = bool(packed)
+        if self.packed:
+            w13, w2 = moe_prepack_weights(w13, w2)
         self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
         self.E_slabs = w13.shape[0]
         self.E_routed = self.E_slabs - (1 if shared else 0)
@@ -294,10 +333,11 @@ class MoELayer:
                               expert_ids=self.expert_ids, num_tokens_post_padded=self.ntpp,
                               expert_offsets=self.offsets, workspace=self.ws_align)
 
-    def ffn(self, x):
+    def ffn(self, x, stage_events=None):
         return moe_grouped_ffn(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
                                K=self.KO, B=self.B, w13_scale=self.w13_scale,
-                               w2_scale=self.w2_scale, y_slots=self.y_slots, workspace=self.ws_ffn)
+                               w2_scale=self.w2_scale, y_slots=self.y_slots, workspace=self.ws_ffn,
+                               stage_events=stage_events, packed=self.packed)
 
     def combine(self):
         return moe_combine(self.y_slots, self.topk_weights, self.topk_ids, self.E_slabs,
@@ -308,3 +348,45 @@ class MoELayer:
         self.align()
         self.ffn(x)
         return self.combine()
+
+
+# ------------------------------------------------------------ HIP events --
+class HipEvents:
+    """A pool of timing hipEvent_t handles (for measuring stages on a stream).
+
+    Created with hipEventDisableSystemFence: they only time work, so recording
+    them skips the system-scope cache writeback an ordinary event adds between
+    kernels (read them after synchronising the stream)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.handles.append(h.value)
+
+    def record(self, i, stream=None):
+        if self._hip.hipEventRecord(ctypes.c_void_p(self.handles[i]), _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        st = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.handles[i]),
+                                           ctypes.c_void_p(self.handles[j]))
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(ctypes.c_void_p(h))
+        self.handles = []

@@ -28,8 +28,8 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra, build_dir) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -39,9 +39,12 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile every kernel source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUILD_DIR) -> str:
+    """Compile every kernel source and link the shared library; returns its path.
+
+    ``extra`` adds hipcc flags (e.g. -D overrides of the kernels' tuning macros);
+    ``out`` / ``build_dir`` redirect the library and the objects."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     extra = list(extra)
     if verbose:
@@ -49,14 +52,14 @@ def build(verbose: bool = False, extra=()) -> str:
         os.environ["MOE_BUILD_VERBOSE"] = "1"
     workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), srcs))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -97,7 +97,21 @@ static moe_status_t ffn_check(const moe_ffn_params_t* p) {
     if (!ffn_block_ok(p->B) || p->E > kAlignMaxExperts) return MOE_ERR_UNSUPPORTED;
     if (f32 && (p->H % 64 || p->I % 64)) return MOE_ERR_UNSUPPORTED;
     if (!f32 && (p->H % 256 || p->I % 128)) return MOE_ERR_UNSUPPORTED;
+    if (p->weight_layout != MOE_LAYOUT_CANONICAL && p->weight_layout != MOE_LAYOUT_PACKED)
+        return MOE_ERR_INVALID_ARG;
+    if (f32 && p->weight_layout == MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
+}
+
+moe_status_t moe_prepack_weights(const moe_ffn_params_t* p, const void* w13, const void* w2,
+                                 void* w13_packed, void* w2_packed, void* stream) {
+    if (!p || p->E < 1 || p->H < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
+    if (p->w_dtype != MOE_BF16 && p->w_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (p->H % 256 || p->I % 128 || p->E > kAlignMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (!w13 || !w2 || !w13_packed || !w2_packed) return MOE_ERR_INVALID_ARG;
+    if (w13 == w13_packed || w2 == w2_packed) return MOE_ERR_INVALID_ARG;
+    const int esz = p->w_dtype == MOE_BF16 ? 2 : 1;
+    return from_hip(launch_prepack(p->E, p->H, p->I, esz, w13, w2, w13_packed, w2_packed, as_stream(stream)));
 }
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
@@ -106,11 +120,11 @@ int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
     return ffn_workspace_bytes(p->w_dtype, p->T, p->H, p->I, C);
 }
 
-moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
-                             const float* w13_scale, const void* w2, const float* w2_scale,
-                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                             const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
+                                const float* w13_scale, const void* w2, const float* w2_scale,
+                                const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
+                                size_t workspace_bytes, void* stream, hipEvent_t const* ev) {
     const moe_status_t st = ffn_check(p);
     if (st != MOE_OK) return st;
     const int64_t S = (int64_t)p->T * p->K;
@@ -127,11 +141,35 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const voi
     a.x = x; a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
     a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.post_padded = num_tokens_post_padded;
     a.y_slots = y_slots;
+    a.packed = p->weight_layout == MOE_LAYOUT_PACKED;
     hipError_t e;
-    if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream));
-    else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream));
-    else e = launch_ffn_fp8(a, workspace, as_stream(stream));
+    if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream), ev);
+    else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream), ev);
+    else e = launch_ffn_fp8(a, workspace, as_stream(stream), ev);
     return from_hip(e);
+}
+
+moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
+                             const float* w13_scale, const void* w2, const float* w2_scale,
+                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                             const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                       num_tokens_post_padded, y_slots, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, const void* w13,
+                                      const float* w13_scale, const void* w2, const float* w2_scale,
+                                      const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                      const int32_t* num_tokens_post_padded, float* y_slots,
+                                      void* workspace, size_t workspace_bytes, void* stream,
+                                      void* const* events) {
+    if (!events) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return MOE_ERR_INVALID_ARG;
+    return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                       num_tokens_post_padded, y_slots, workspace, workspace_bytes, stream,
+                       reinterpret_cast<hipEvent_t const*>(events));
 }
 
 moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float* y_slots,

@@ -59,18 +59,23 @@ ffn_f32_stage2(FfnArgs a, const float* __restrict__ h_in, int nN) {
     }
 }
 
-hipError_t launch_ffn_f32(const FfnArgs& a, void* ws, hipStream_t stream) {
+hipError_t launch_ffn_f32(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
     float* h = static_cast<float*>(ws);                     // [C, I] fp32
     const int nMB = (int)(a.C / a.B);
     const int nN1 = a.I / kF32Cols, nN2 = a.H / kF32Cols;
+    hipError_t err;
+    if ((err = record_stage(ev, 0, stream)) != hipSuccess) return err;
+    if ((err = record_stage(ev, 1, stream)) != hipSuccess) return err;
     if (nMB * nN1 > 0)
         hipLaunchKernelGGL(ffn_f32_stage1, dim3(nMB * nN1), dim3(kF32Threads), 0, stream, a, h, nN1);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = record_stage(ev, 2, stream)) != hipSuccess) return err;
+    if ((err = record_stage(ev, 3, stream)) != hipSuccess) return err;
     if (nMB * nN2 > 0)
         hipLaunchKernelGGL(ffn_f32_stage2, dim3(nMB * nN2), dim3(kF32Threads), 0, stream, a,
                            (const float*)h, nN2);
-    return hipGetLastError();
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return record_stage(ev, 4, stream);
 }
 
 }  // namespace moe

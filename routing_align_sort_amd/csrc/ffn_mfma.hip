@@ -48,6 +48,24 @@ constexpr int kFfnThreads = 256;
 constexpr int kStepBytes = 128;                 // bytes of a row per K-step
 constexpr int kLdsPitch = kStepBytes + 16;      // padded LDS row, bytes
 
+// K-steps of weights in flight per wave (register ring depth - 1).
+#ifndef MOE_FFN_PF
+#define MOE_FFN_PF 2
+#endif
+// M blocks per tile group: the tiles of GROUP_M consecutive M blocks are dealt
+// with the M block fastest, so the workgroups that run together on one XCD
+// cover GROUP_M blocks x a few N tiles and share both operands through L2.
+#ifndef MOE_FFN_GROUP_M
+#define MOE_FFN_GROUP_M 8
+#endif
+
+// Packed weight layout (written by moe_prepack_weights): for every expert,
+// N tile, K-step, wave and row set, the 64 lanes' 16-byte quarters q = 0..3
+// are stored as four contiguous 1 KB blocks, so each load instruction of a
+// wave reads 1 KB of consecutive bytes and a wave's K-step is 8 KB in one run.
+constexpr int kPackWaveBytes = 2 * 4 * 1024;              // two row sets x four quarters
+constexpr int kPackStepBytes = 4 * kPackWaveBytes;        // four waves
+
 template <int BM>
 struct Tile {
     static constexpr int MT = (BM < 32 ? 32 : BM) / 32;         // 32-row MFMA tiles
@@ -68,7 +86,7 @@ __device__ __forceinline__ i32x8_t as_i32x8(uint4 lo, uint4 hi) {
 // The shared K loop.  arow[m] points at row m of A (nullptr = zero row);
 // brow[ns] is this lane's weight row for B subtile ns, already offset by the
 // lane's half (64 bytes); nk K-steps of 128 bytes; acc[MT][NSUB] accumulates.
-template <bool kFp8, int BM, int NSUB, int PF>
+template <bool kFp8, bool kPacked, int BM, int NSUB, int PF>
 __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t* const (&brow)[NSUB], int nk,
                                       uint8_t* lds, f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
     using TL = Tile<BM>;
@@ -100,12 +118,14 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
                 *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = src[r];
         }
     };
+    constexpr int64_t kB = kPacked ? kPackStepBytes : kStepBytes;   // per K-step
+    constexpr int qB = kPacked ? 1024 : 16;                           // per quarter
     auto load_b = [&](uint4 (&dst)[NSUB][4], int k) {
 #pragma unroll
         for (int ns = 0; ns < NSUB; ++ns)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                dst[ns][q] = *(const uint4*)(brow[ns] + (int64_t)k * kStepBytes + q * 16);
+                dst[ns][q] = *(const uint4*)(brow[ns] + (int64_t)k * kB + q * qB);
     };
     auto compute = [&](const uint4 (&b)[NSUB][4], int buf) {
         const uint8_t* base = lds + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * 64;
@@ -172,6 +192,38 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-
 // Row of the 32x32 MFMA accumulator held by this lane in register i.
 __device__ __forceinline__ int acc_row(int i, int lane) { return (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3); }
 
+// Tile of this workgroup.  The grid covers the capacity; only the first
+// (P/B)*nN workgroups have a tile.  Those -- not the whole grid -- are dealt
+// XCD-contiguously, so the real work spreads over all XCDs; inside an XCD's
+// range, groups of GROUP_M M blocks are walked M-block fastest.  Returns
+// false for a workgroup without a tile.
+__device__ __forceinline__ bool ffn_tile(int nmb, int nN, int* mb, int* nt) {
+    const int nvalid = nmb * nN;
+    if ((int)blockIdx.x >= nvalid) return false;
+    const int t = xcd_contiguous_tile(blockIdx.x, nvalid);
+    const int per_group = MOE_FFN_GROUP_M * nN;
+    const int g = t / per_group;
+    const int first = g * MOE_FFN_GROUP_M;
+    const int gsize = min(nmb - first, MOE_FFN_GROUP_M);
+    const int r = t - g * per_group;
+    *mb = first + r % gsize;
+    *nt = r / gsize;
+    return true;
+}
+
+// This lane's first weight byte for row set ns of wave w in N tile nt.
+// Canonical: row `row` of a [rows, row_bytes] slab, this lane's 64-byte half.
+// Packed: the lane's 16 bytes in the first 1 KB block of the (nt, w, ns) run.
+template <bool kPacked>
+__device__ __forceinline__ const uint8_t* weight_lane_ptr(const uint8_t* slab, int row, int64_t row_bytes,
+                                                          int nt, int w, int ns, int lane) {
+    if (kPacked) {
+        const int64_t nk = row_bytes / kStepBytes;
+        return slab + (int64_t)nt * nk * kPackStepBytes + w * kPackWaveBytes + ns * 4096 + lane * 16;
+    }
+    return slab + (int64_t)row * row_bytes + (lane >> 5) * 64;
+}
+
 template <int MT, int NSUB>
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[MT][NSUB]) {
 #pragma unroll
@@ -198,17 +250,15 @@ struct Fp8Ws {
 template <int BM>
 constexpr int ffn_min_blocks() { return BM >= 128 ? 1 : 2; }
 
-template <bool kFp8, int BM, int PF>
+template <bool kFp8, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, ffn_min_blocks<BM>())
-ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN, int ntiles) {
+ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     using TL = Tile<BM>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
     __shared__ const uint8_t* arow[BM];
     __shared__ float rowscale[BM];
-    const int tile = xcd_contiguous_tile(blockIdx.x, ntiles);
-    const int mb = tile / nN, nt = tile % nN;
-    const int P = a.post_padded[0];
-    if (mb * BM >= P) return;
+    int mb, nt;
+    if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
     const int e = a.expert_ids[mb];
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int H = a.H, I = a.I;
@@ -226,13 +276,14 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN, int ntiles)
     __syncthreads();
 
     const int n0 = nt * 128 + w * 32;                       // this wave's intermediate columns
-    const int r32 = lane & 31, half = lane >> 5;
+    const int r32 = lane & 31;
     const uint8_t* wbase = (const uint8_t*)a.w13 + (int64_t)e * 2 * I * H * esz;
-    const uint8_t* const brow[2] = {wbase + ((int64_t)(n0 + r32) * H) * esz + half * 64,
-                                    wbase + ((int64_t)(I + n0 + r32) * H) * esz + half * 64};
+    const uint8_t* const brow[2] = {
+        weight_lane_ptr<kPacked>(wbase, n0 + r32, (int64_t)H * esz, nt, w, 0, lane),
+        weight_lane_ptr<kPacked>(wbase, I + n0 + r32, (int64_t)H * esz, nt, w, 1, lane)};
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
-    kloop<kFp8, BM, 2, PF>(arow, brow, H * esz / kStepBytes, lds, acc);
+    kloop<kFp8, kPacked, BM, 2, PF>(arow, brow, H * esz / kStepBytes, lds, acc);
 
     const int col = n0 + r32;
     float sg = 1.f, su = 1.f;
@@ -268,19 +319,16 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN, int ntiles)
 }
 
 // ------------------------------------------------------------------ stage 2 --
-template <bool kFp8, int BM, int PF>
+template <bool kFp8, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, ffn_min_blocks<BM>())
-ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN,
-           int ntiles) {
+ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     using TL = Tile<BM>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
     __shared__ const uint8_t* arow[BM];
     __shared__ int slots[BM];
     __shared__ float rowscale[BM];
-    const int tile = xcd_contiguous_tile(blockIdx.x, ntiles);
-    const int mb = tile / nN, nt = tile % nN;
-    const int P = a.post_padded[0];
-    if (mb * BM >= P) return;
+    int mb, nt;
+    if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
     const int e = a.expert_ids[mb];
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int H = a.H, I = a.I;
@@ -295,13 +343,14 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
     __syncthreads();
 
     const int n0 = nt * 256 + w * 64;                       // this wave's output columns
-    const int r32 = lane & 31, half = lane >> 5;
+    const int r32 = lane & 31;
     const uint8_t* wbase = (const uint8_t*)a.w2 + (int64_t)e * H * I * esz;
-    const uint8_t* const brow[2] = {wbase + ((int64_t)(n0 + r32) * I) * esz + half * 64,
-                                    wbase + ((int64_t)(n0 + 32 + r32) * I) * esz + half * 64};
+    const uint8_t* const brow[2] = {
+        weight_lane_ptr<kPacked>(wbase, n0 + r32, (int64_t)I * esz, nt, w, 0, lane),
+        weight_lane_ptr<kPacked>(wbase, n0 + 32 + r32, (int64_t)I * esz, nt, w, 1, lane)};
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
-    kloop<kFp8, BM, 2, PF>(arow, brow, I * esz / kStepBytes, lds, acc);
+    kloop<kFp8, kPacked, BM, 2, PF>(arow, brow, I * esz / kStepBytes, lds, acc);
 
     float s0 = 1.f, s1 = 1.f;
     if (kFp8) {
@@ -437,15 +486,16 @@ static Fp8Ws fp8_ws(void* ws, int64_t T, int64_t H, int64_t I, int64_t C) {
     return q;
 }
 
-template <bool kFp8, int BM>
-static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream) {
-    constexpr int PF = 2;
+template <bool kFp8, bool kPacked, int BM>
+static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
+    constexpr int PF = MOE_FFN_PF;
     const int nMB = (int)(a.C / BM);
     const int nN1 = a.I / 128, nN2 = a.H / 256;
     const int t1 = nMB * nN1, t2 = nMB * nN2;
     hipError_t err;
     Fp8Ws q{};
     const uint8_t* h_in = static_cast<const uint8_t*>(ws);
+    if ((err = record_stage(ev, 0, stream)) != hipSuccess) return err;
     if (kFp8) {
         q = fp8_ws(ws, a.T, a.H, a.I, a.C);
         if (a.T > 0)
@@ -454,33 +504,97 @@ static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream)
         if ((err = hipGetLastError()) != hipSuccess) return err;
         h_in = q.aq;
     }
+    if ((err = record_stage(ev, 1, stream)) != hipSuccess) return err;
     if (t1 > 0)
-        hipLaunchKernelGGL((ffn_stage1<kFp8, BM, PF>), dim3(t1), dim3(kFfnThreads), 0, stream, a,
-                           (uint16_t*)ws, q, nN1, t1);
+        hipLaunchKernelGGL((ffn_stage1<kFp8, kPacked, BM, PF>), dim3(t1), dim3(kFfnThreads), 0, stream, a,
+                           (uint16_t*)ws, q, nN1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = record_stage(ev, 2, stream)) != hipSuccess) return err;
     if (kFp8 && a.C > 0) {
         hipLaunchKernelGGL(requant_rows_kernel, dim3((unsigned)a.C), dim3(kQuantThreads), 0, stream,
                            (const float*)q.a, (const uint32_t*)q.amax, a.post_padded, a.I, q.aq, q.sa);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
+    if ((err = record_stage(ev, 3, stream)) != hipSuccess) return err;
     if (t2 > 0)
-        hipLaunchKernelGGL((ffn_stage2<kFp8, BM, PF>), dim3(t2), dim3(kFfnThreads), 0, stream, a, h_in,
-                           (const float*)q.sa, nN2, t2);
-    return hipGetLastError();
+        hipLaunchKernelGGL((ffn_stage2<kFp8, kPacked, BM, PF>), dim3(t2), dim3(kFfnThreads), 0, stream, a,
+                           h_in, (const float*)q.sa, nN2);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    return record_stage(ev, 4, stream);
 }
 
-template <bool kFp8>
-static hipError_t launch_mfma(const FfnArgs& a, void* ws, hipStream_t stream) {
+template <bool kFp8, bool kPacked>
+static hipError_t launch_mfma_layout(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
     switch (a.B) {
-        case 16: return launch_mfma_bm<kFp8, 16>(a, ws, stream);
-        case 32: return launch_mfma_bm<kFp8, 32>(a, ws, stream);
-        case 64: return launch_mfma_bm<kFp8, 64>(a, ws, stream);
-        case 128: return launch_mfma_bm<kFp8, 128>(a, ws, stream);
+        case 16: return launch_mfma_bm<kFp8, kPacked, 16>(a, ws, stream, ev);
+        case 32: return launch_mfma_bm<kFp8, kPacked, 32>(a, ws, stream, ev);
+        case 64: return launch_mfma_bm<kFp8, kPacked, 64>(a, ws, stream, ev);
+        case 128: return launch_mfma_bm<kFp8, kPacked, 128>(a, ws, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream) { return launch_mfma<false>(a, ws, stream); }
-hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream) { return launch_mfma<true>(a, ws, stream); }
+template <bool kFp8>
+static hipError_t launch_mfma(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
+    return a.packed ? launch_mfma_layout<kFp8, true>(a, ws, stream, ev)
+                    : launch_mfma_layout<kFp8, false>(a, ws, stream, ev);
+}
+
+hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
+    return launch_mfma<false>(a, ws, stream, ev);
+}
+hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
+    return launch_mfma<true>(a, ws, stream, ev);
+}
+
+// ----------------------------------------------------------------- prepack --
+// One 16-byte chunk per thread, walked in packed order (coalesced writes):
+// chunk c -> (expert, N tile, K-step, wave, row set, quarter, lane), and the
+// canonical row / byte it comes from.  Row of (tile, wave, row set, lane):
+// ns * ns_stride + tile * tile_rows + wave * wave_rows + lane % 32.
+__global__ void __launch_bounds__(256)
+prepack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nchunks, int nN,
+               int nk, int64_t rows_total, int64_t row_bytes, int ns_stride, int tile_rows,
+               int wave_rows) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= nchunks) return;
+    const int lane = (int)(c & 63);
+    const int q = (int)((c >> 6) & 3);
+    const int ns = (int)((c >> 8) & 1);
+    const int w = (int)((c >> 9) & 3);
+    const int64_t rest = c >> 11;
+    const int k = (int)(rest % nk);
+    const int t = (int)((rest / nk) % nN);
+    const int64_t e = rest / ((int64_t)nk * nN);
+    const int64_t row = (int64_t)ns * ns_stride + (int64_t)t * tile_rows + w * wave_rows + (lane & 31);
+    const int64_t byte = (int64_t)k * kStepBytes + (lane >> 5) * 64 + q * 16;
+    *(uint4*)(dst + c * 16) = *(const uint4*)(src + (e * rows_total + row) * row_bytes + byte);
+}
+
+hipError_t launch_prepack(int E, int H, int I, int esz, const void* w13, const void* w2, void* w13p,
+                          void* w2p, hipStream_t stream) {
+    // gate/up: rows [0,2I) of H*esz bytes; tiles of 128 intermediate columns;
+    // row set 0 = gate rows, 1 = up rows (I further on).
+    {
+        const int64_t row_bytes = (int64_t)H * esz;
+        const int nk = (int)(row_bytes / kStepBytes), nN = I / 128;
+        const int64_t n = (int64_t)E * nN * nk * (kPackStepBytes / 16);
+        hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           (const uint8_t*)w13, (uint8_t*)w13p, n, nN, nk, (int64_t)2 * I, row_bytes, I, 128,
+                           32);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    // down: rows [0,H) of I*esz bytes; tiles of 256 output columns; a wave's
+    // two row sets are adjacent 32-row blocks.
+    {
+        const int64_t row_bytes = (int64_t)I * esz;
+        const int nk = (int)(row_bytes / kStepBytes), nN = H / 256;
+        const int64_t n = (int64_t)E * nN * nk * (kPackStepBytes / 16);
+        hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           (const uint8_t*)w2, (uint8_t*)w2p, n, nN, nk, (int64_t)H, row_bytes, 32, 256, 64);
+    }
+    return hipGetLastError();
+}
 
 }  // namespace moe

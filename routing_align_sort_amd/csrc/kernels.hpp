@@ -51,12 +51,24 @@ struct FfnArgs {
     const int32_t* expert_ids;
     const int32_t* post_padded;
     float* y_slots;
+    int packed;                // weights in the layout written by launch_prepack
 };
 // Workspace layout per dtype path (bytes, each region 256-byte aligned).
 int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C);
-hipError_t launch_ffn_f32(const FfnArgs& a, void* ws, hipStream_t stream);
-hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream);
-hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream);
+// ev (nullable) = 5 caller-created events recorded at the stage boundaries:
+// before quantisation, before gate/up, after gate/up, before down, after down.
+hipError_t launch_ffn_f32(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);
+hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);
+hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);
+
+// Rewrites canonical W13 [E,2I,H] and W2 [E,H,I] (esz bytes per element) into
+// the packed layout the MFMA kernels stream (same sizes).
+hipError_t launch_prepack(int E, int H, int I, int esz, const void* w13, const void* w2, void* w13p,
+                          void* w2p, hipStream_t stream);
+
+inline hipError_t record_stage(hipEvent_t const* ev, int i, hipStream_t s) {
+    return ev ? hipEventRecord(ev[i], s) : hipSuccess;
+}
 
 // ----------------------------------------------------------------- combine --
 hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,

@@ -78,8 +78,8 @@ def route_oracle(cfg, L, K=None):
     return ids, w
 
 
-def make_gpu_layer(cfg, L, B=None):
-    return moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B or cfg["B"],
+def make_gpu_layer(cfg, L, B=None, packed=None):
+    return moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B or cfg["B"], packed=packed,
                         score=cfg["score"], n_group=cfg["n_group"], topk_group=cfg["topk_group"],
                         renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
                         w13_scale=L.get("w13_scale"), w2_scale=L.get("w2_scale"),

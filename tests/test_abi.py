@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -95,7 +95,7 @@ def test_ffn_validation_and_workspace(lib):
     with pytest.raises(moe.MoEError):       # fp8 activations are not a built combination
         moe.moe_grouped_ffn_workspace_bytes(64, 2, 8, 256, 256, 16, torch.float8_e4m3fn,
                                             torch.float8_e4m3fn)
-    p = moe._FfnParams(64, 2, 8, 256, 256, 16, 1, 1)
+    p = moe._FfnParams(64, 2, 8, 256, 256, 16, 1, 1, 0)
     P = ctypes.c_void_p
     st = lib.moe_grouped_ffn(ctypes.byref(p), P(8), P(8), None, P(8), None, P(8), P(8), P(8), P(8),
                              P(8), 10, None)
@@ -104,6 +104,14 @@ def test_ffn_validation_and_workspace(lib):
     st = lib.moe_grouped_ffn(ctypes.byref(p), P(8), P(8), None, P(8), None, P(8), P(8), P(8), P(8),
                              P(8), 1 << 30, None)
     assert st == moe.MOE_ERR_INVALID_ARG        # fp8 needs its scales
+    p.w_dtype = 1; p.weight_layout = 5
+    st = lib.moe_grouped_ffn(ctypes.byref(p), P(8), P(8), None, P(8), None, P(8), P(8), P(8), P(8),
+                             P(8), 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG        # unknown weight layout
+    f = moe._FfnParams(64, 2, 8, 256, 256, 16, 0, 0, 1)
+    assert lib.moe_prepack_weights(ctypes.byref(f), P(8), P(8), P(16), P(16), None) == moe.MOE_ERR_UNSUPPORTED
+    f.w_dtype = 1
+    assert lib.moe_prepack_weights(ctypes.byref(f), P(8), P(8), P(8), P(16), None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(4, 2, 8, 6, P(8), P(8), P(8), 1, P(8), None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(4, 2, 8, 8, P(8), P(8), P(8), 7, P(8), None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(0, 2, 8, 8, None, None, None, 1, None, None) == moe.MOE_OK

@@ -83,6 +83,25 @@ def test_ffn_output_is_block_size_invariant():
             assert torch.equal(y, ys[0]), name
 
 
+def test_packed_weights_give_identical_results():
+    dev = device()
+    for name in ("decode_bf16", "prefill_fp8"):
+        over = dict(T=150, H=512, I=256, E=6)
+        if name == "decode_bf16":
+            over.update(K=3, n_group=2, topk_group=2)
+        cfg = ms.scaled(name, **over)
+        L = ms.make_layer(cfg, device=dev)
+        for B in (16, 64, 128):
+            ys = []
+            for packed in (False, True):
+                layer = make_gpu_layer(cfg, L, B, packed=packed)
+                layer.forward(L["x"], L["logits"], L["bias"])
+                torch.cuda.synchronize()
+                ys.append(layer.y_slots.clone())
+            say(f"{name} B={B}: packed == canonical")
+            assert torch.equal(ys[0], ys[1]), (name, B)
+
+
 def test_fp8_token_quantisation_codes_match_oracle():
     dev = device()
     cfg = ms.scaled("prefill_fp8", T=257, H=1024, I=256, E=4)
