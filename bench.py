@@ -200,7 +200,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the align-only and secondary-workload figures")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-probe run into the traffic record under profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
+                           args.B or None)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
@@ -264,9 +273,93 @@ def main():
             del r2
             torch.cuda.empty_cache()
         line["other_workloads"] = extra
+    if args.copy_probe:
+        copy_probe(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(cfg, B, dev)
     print(json.dumps(line), flush=True)
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe(dev, reps=3):
+    """A plain device copy of COPY_PROBE_BYTES (ordinary 16-byte loads and
+    stores, read once, written once; routing_align_sort_amd/probe): the
+    reference the profiler's byte counters are scaled against."""
+    import ctypes
+
+    import torch
+
+    from routing_align_sort_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIB):
+        hip_build.build_probe()
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.moe_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(reps):
+        if lib.moe_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                              COPY_PROBE_BYTES, stream) != 0:
+            raise RuntimeError("copy probe launch failed")
+    torch.cuda.synchronize()
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_csv, write_csv, workload, B):
+    """HBM bytes per launch of the gate/up kernel: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch, summed over the XCD instances) each scaled by the
+    factor that makes the same counter read the known bytes of the plain
+    copy kernel; written to profiles/ffn_stage1_<workload>_B<B>_counters.json
+    with the hash of the kernel source it was measured on."""
+    import hashlib
+    import statistics
+
+    import moe_synth as ms
+    cfg = ms.CONFIGS[workload]
+    B = B or cfg["B"]
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in _counter_rows(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        by_kernel = {}
+        for (name, _), v in vals.items():
+            by_kernel.setdefault(name, []).append(v)
+        return by_kernel
+
+    fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = per_dispatch(write_csv, "WRITE_SIZE")
+    pick = lambda d, pat: statistics.median(next(v for k, v in d.items() if pat(k)))
+    biggest = lambda d: max(v for k, vs in d.items() if "copy_probe_kernel" in k for v in vs)
+    is_st1 = lambda k: "ffn_stage1" in k
+    copy_kib_r, copy_kib_w = biggest(fetch), biggest(write)
+    f_fetch = COPY_PROBE_BYTES / (copy_kib_r * 1024.0)
+    f_write = COPY_PROBE_BYTES / (copy_kib_w * 1024.0)
+    st1_r, st1_w = pick(fetch, is_st1), pick(write, is_st1)
+    src = os.path.join(ROOT, "routing_align_sort_amd", "csrc", "ffn_mfma.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    rec = {"kernel": "ffn_stage1", "workload": workload, "block_size_m": B,
+           "fetch_kib_per_launch": st1_r, "write_kib_per_launch": st1_w,
+           "copy_probe_bytes": COPY_PROBE_BYTES, "copy_fetch_kib": copy_kib_r,
+           "copy_write_kib": copy_kib_w, "fetch_scale": f_fetch, "write_scale": f_write,
+           "hbm_bytes_per_launch": round(st1_r * 1024 * f_fetch + st1_w * 1024 * f_write),
+           "kernel_source_sha256": digest}
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    out = os.path.join(PROFILE_DIR, f"ffn_stage1_{workload}_B{B}_counters.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def describe(name, cfg, B):

@@ -220,6 +220,14 @@ CONFIGS = {
     "prefill_fp8": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e4m3", score="softmax",
                         bias=False, n_group=1, topk_group=1, renormalize=False,
                         routing="zipf", zipf_s=1.2, shared=True, B=64),
+    # Compute-bound shapes of the same layer: 2048 tokens x top-8 over the 32
+    # local experts, exactly 512 slots per expert (bf16; and fp8 + shared expert).
+    "prefill_bf16_512": dict(T=2048, H=7168, I=2048, E=32, K=8, dtype="bf16", score="softmax",
+                             bias=False, n_group=1, topk_group=1, renormalize=True,
+                             routing="uniform8", B=128),
+    "prefill_fp8_512": dict(T=2048, H=7168, I=2048, E=32, K=8, dtype="e4m3", score="softmax",
+                            bias=False, n_group=1, topk_group=1, renormalize=True,
+                            routing="uniform8", shared=True, B=128),
 }
 
 ROUTER_SIGMA = 0.02
@@ -228,8 +236,18 @@ ASSIGN_MARGIN = 8.0
 
 
 def assigned_experts(cfg, seed=0) -> np.ndarray:
-    """For routing 'uniform' / 'zipf': the expert each token must route to."""
+    """For routing 'uniform' / 'zipf': the expert each token must route to;
+    for 'uniform8': [T, K] experts, token perm[j] taking {c, c+E/K, ...} with
+    c = j mod (E/K), so every expert gets exactly T*K/E slots."""
     T, E = cfg["T"], cfg["E"]
+    if cfg["routing"] == "uniform8":
+        K = cfg["K"]
+        stride = E // K
+        perm = permutation(seed, TAG_PERM, T)
+        a = np.empty((T, K), np.int64)
+        c = np.arange(T) % stride
+        a[perm] = c[:, None] + stride * np.arange(K)[None, :]
+        return a
     if cfg["routing"] == "uniform":
         perm = permutation(seed, TAG_PERM, T)
         a = np.empty(T, np.int64)
@@ -266,7 +284,10 @@ def make_layer(cfg, device="cpu", seed=0, weights=True):
     else:
         a = assigned_experts(cfg, seed)
         logits = normal(seed, TAG_LOGIT_NOISE, (T, E), 1.0, "cpu", torch.float32)
-        logits[torch.arange(T), torch.from_numpy(a)] += ASSIGN_MARGIN
+        if a.ndim == 1:
+            a = a[:, None]
+        rows = torch.arange(T)[:, None].expand(T, a.shape[1])
+        logits[rows, torch.from_numpy(a)] += ASSIGN_MARGIN
     out["logits"] = logits.to(device)
     out["bias"] = uniform(seed, TAG_BIAS, (E,), -0.1, 0.1, device) if cfg.get("bias") else None
     if weights:

@@ -16,6 +16,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
+# a separate copy kernel of known traffic, used to calibrate profiler byte counters
+PROBE_SRC = os.path.join(PKG, "probe", "copy_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -59,7 +62,19 @@ def build(verbose: bool = False, extra=(), out: str = LIB, build_dir: str = BUIL
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+    if out == LIB:
+        build_probe()
     return out
+
+
+def build_probe() -> str:
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

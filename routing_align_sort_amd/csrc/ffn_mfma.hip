@@ -39,6 +39,8 @@
 //   a few M blocks in that XCD's L2, and M blocks of one expert stay close in
 //   time so repeated weight tiles hit L2 (the pid remapping idea of the AITER
 //   section of the dignews.cc page, "AMD GPU ... 7x faster ...").
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -51,6 +53,9 @@ constexpr int kLdsPitch = kStepBytes + 16;      // padded LDS row, bytes
 // K-steps of weights in flight per wave (register ring depth - 1).
 #ifndef MOE_FFN_PF
 #define MOE_FFN_PF 2
+#endif
+#ifndef MOE_FFN_PF128            // the 128-row tile: fewer registers, two workgroups per CU
+#define MOE_FFN_PF128 1
 #endif
 // M blocks per tile group: the tiles of GROUP_M consecutive M blocks are dealt
 // with the M block fastest, so the workgroups that run together on one XCD
@@ -96,38 +101,53 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
     const int half = lane >> 5;
     const int r32 = lane & 31;
 
-    uint4 areg[PF + 1][TL::APT];
-    uint4 breg[PF + 1][NSUB][4];
+    uint4 areg[TL::APT];                 // A runs one K-step ahead
+    // Weights run PF K-steps ahead.  bf16: four 16-byte MFMA operands per row
+    // set; fp8: two 32-byte operands, each assembled from two 16-byte loads
+    // straight into its register tuple.
+    using BOp = typename std::conditional<kFp8, i32x8_t, uint4>::type;
+    constexpr int NB = kFp8 ? 2 : 4;
+    BOp breg[PF + 1][NSUB][NB];
 
-    auto load_a = [&](uint4 (&dst)[TL::APT], int k) {
+    auto load_a = [&](int k) {
 #pragma unroll
         for (int r = 0; r < TL::APT; ++r) {
             const int c = tid + r * kFfnThreads;
-            dst[r] = make_uint4(0, 0, 0, 0);
+            areg[r] = make_uint4(0, 0, 0, 0);
             if (c < TL::ACH) {
                 const uint8_t* src = arow[c >> 3];
-                if (src) dst[r] = *(const uint4*)(src + (int64_t)k * kStepBytes + (c & 7) * 16);
+                if (src) areg[r] = *(const uint4*)(src + (int64_t)k * kStepBytes + (c & 7) * 16);
             }
         }
     };
-    auto store_a = [&](const uint4 (&src)[TL::APT], int buf) {
+    auto store_a = [&](int buf) {
 #pragma unroll
         for (int r = 0; r < TL::APT; ++r) {
             const int c = tid + r * kFfnThreads;
             if (c < TL::ACH)
-                *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = src[r];
+                *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = areg[r];
         }
     };
     constexpr int64_t kB = kPacked ? kPackStepBytes : kStepBytes;   // per K-step
     constexpr int qB = kPacked ? 1024 : 16;                           // per quarter
-    auto load_b = [&](uint4 (&dst)[NSUB][4], int k) {
+    auto load_b = [&](BOp (&dst)[NSUB][NB], int k) {
 #pragma unroll
-        for (int ns = 0; ns < NSUB; ++ns)
+        for (int ns = 0; ns < NSUB; ++ns) {
+            const uint8_t* src = brow[ns] + (int64_t)k * kB;
+            if constexpr (kFp8) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dst[ns][q] = *(const uint4*)(brow[ns] + (int64_t)k * kB + q * qB);
+                for (int j = 0; j < 2; ++j) {
+                    const uint4 lo = *(const uint4*)(src + (2 * j) * qB);
+                    const uint4 hi = *(const uint4*)(src + (2 * j + 1) * qB);
+                    dst[ns][j] = as_i32x8(lo, hi);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dst[ns][q] = *(const uint4*)(src + q * qB);
+            }
+        }
     };
-    auto compute = [&](const uint4 (&b)[NSUB][4], int buf) {
+    auto compute = [&](const BOp (&b)[NSUB][NB], int buf) {
         const uint8_t* base = lds + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * 64;
         if constexpr (!kFp8) {
 #pragma unroll
@@ -136,9 +156,11 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
                 for (int mt = 0; mt < MT; ++mt) {
                     const uint4 af = *(const uint4*)(base + mt * 32 * kLdsPitch + kk * 16);
 #pragma unroll
-                    for (int ns = 0; ns < NSUB; ++ns)
-                        acc[mt][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            as_bf16x8(af), as_bf16x8(b[ns][kk]), acc[mt][ns], 0, 0, 0);
+                    for (int ns = 0; ns < NSUB; ++ns) {
+                        if constexpr (!kFp8)
+                            acc[mt][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                as_bf16x8(af), as_bf16x8(b[ns][kk]), acc[mt][ns], 0, 0, 0);
+                    }
                 }
             }
         } else {
@@ -151,22 +173,18 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
 #pragma unroll
                     for (int ns = 0; ns < NSUB; ++ns)
                         acc[mt][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            as_i32x8(a0, a1), as_i32x8(b[ns][2 * kk], b[ns][2 * kk + 1]), acc[mt][ns],
-                            0, 0, 0, 127, 0, 127);
+                            as_i32x8(a0, a1), b[ns][kk], acc[mt][ns], 0, 0, 0, 127, 0, 127);
                 }
             }
         }
     };
 
-    // prologue: K-steps 0..PF-1 in flight, step 0 of A in LDS
+    // prologue: A step 0 into LDS, weight steps 0..PF-1 in flight
+    load_a(0);
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-        if (s < nk) {
-            load_a(areg[s], s);
-            load_b(breg[s], s);
-        }
-    }
-    store_a(areg[0], 0);
+    for (int s = 0; s < PF; ++s)
+        if (s < nk) load_b(breg[s], s);
+    store_a(0);
     __syncthreads();
 
     for (int k0 = 0; k0 < nk; k0 += PF + 1) {
@@ -174,13 +192,10 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
         for (int u = 0; u <= PF; ++u) {
             const int k = k0 + u;
             if (k < nk) {
-                const int nxt = (u + PF) % (PF + 1);
-                if (k + PF < nk) {
-                    load_a(areg[nxt], k + PF);
-                    load_b(breg[nxt], k + PF);
-                }
+                if (k + 1 < nk) load_a(k + 1);
+                if (k + PF < nk) load_b(breg[(u + PF) % (PF + 1)], k + PF);
                 compute(breg[u], k & 1);
-                if (k + 1 < nk) store_a(areg[(u + 1) % (PF + 1)], (k + 1) & 1);
+                if (k + 1 < nk) store_a((k + 1) & 1);
                 __syncthreads();
             }
         }
@@ -245,13 +260,18 @@ struct Fp8Ws {
 
 // ------------------------------------------------------------------ stage 1 --
 // bf16: h_out is bf16 [C,I].  fp8: writes fp32 a and the row amax.
-// Workgroups per CU the register budget is sized for: the 128-row tile keeps
-// 4x2 accumulator tiles per wave and takes the whole register file.
-template <int BM>
-constexpr int ffn_min_blocks() { return BM >= 128 ? 1 : 2; }
+// Workgroups per CU the register budget is sized for: two (8 waves per CU),
+// except the fp8 128-row tile, whose 32-byte operand tuples need the whole
+// register file of one workgroup.
+template <bool kFp8, int BM>
+constexpr int ffn_min_blocks() { return (kFp8 && BM >= 128) ? 1 : 2; }
+// Weight K-steps in flight: fewer for the register-hungry 128-row tile at two
+// workgroups per CU, more where one workgroup has the CU to itself.
+template <bool kFp8, int BM>
+constexpr int ffn_pf() { return BM < 128 ? MOE_FFN_PF : (kFp8 ? MOE_FFN_PF : MOE_FFN_PF128); }
 
 template <bool kFp8, bool kPacked, int BM, int PF>
-__global__ void __launch_bounds__(kFfnThreads, ffn_min_blocks<BM>())
+__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     using TL = Tile<BM>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
@@ -320,7 +340,7 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
 
 // ------------------------------------------------------------------ stage 2 --
 template <bool kFp8, bool kPacked, int BM, int PF>
-__global__ void __launch_bounds__(kFfnThreads, ffn_min_blocks<BM>())
+__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     using TL = Tile<BM>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
@@ -488,7 +508,7 @@ static Fp8Ws fp8_ws(void* ws, int64_t T, int64_t H, int64_t I, int64_t C) {
 
 template <bool kFp8, bool kPacked, int BM>
 static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
-    constexpr int PF = MOE_FFN_PF;
+    constexpr int PF = ffn_pf<kFp8, BM>();
     const int nMB = (int)(a.C / BM);
     const int nN1 = a.I / 128, nN2 = a.H / 256;
     const int t1 = nMB * nN1, t2 = nMB * nN2;
