@@ -262,6 +262,7 @@ def main():
     del r
     torch.cuda.empty_cache()
     if not args.no_extras:
+        line["hbm_probe"] = hbm_probe(dev)
         line["align_sort_16k"] = align_only(dev)
         extra = {}
         for name in ("prefill_fp8", "decode_bf16"):
@@ -304,6 +305,50 @@ def copy_probe(dev, reps=3):
                               COPY_PROBE_BYTES, stream) != 0:
             raise RuntimeError("copy probe launch failed")
     torch.cuda.synchronize()
+
+
+def hbm_probe(dev, nbytes=4 << 30, reps=10):
+    """Bandwidth a plain kernel reaches: a 16-byte-per-thread copy (reads and
+    writes nbytes/2 each) and a read-only stream of nbytes, event-timed,
+    best of `reps`."""
+    import ctypes
+
+    import torch
+
+    import routing_align_sort_amd as moe
+    from routing_align_sort_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIB):
+        hip_build.build_probe()
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    for f in (lib.moe_probe_copy, lib.moe_probe_read):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    half = nbytes // 2
+    out = torch.empty(4096, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ev = moe.HipEvents(4 * reps)
+    res = {}
+    for name, call, moved in (
+            ("copy", lambda: lib.moe_probe_copy(ctypes.c_void_p(buf.data_ptr()),
+                                                ctypes.c_void_p(buf.data_ptr() + half), half, stream),
+             2 * half),
+            ("read", lambda: lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()),
+                                                ctypes.c_void_p(out.data_ptr()), nbytes, stream),
+             nbytes)):
+        call()
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev.record(2 * i)
+            if call() != 0:
+                raise RuntimeError("probe launch failed")
+            ev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        best = min(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)) * 1e-3
+        res[name + "_gbs"] = round(moved / best / 1e9, 1)
+    ev.close()
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def _counter_rows(path):

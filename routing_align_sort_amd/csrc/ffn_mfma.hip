@@ -88,11 +88,16 @@ __device__ __forceinline__ i32x8_t as_i32x8(uint4 lo, uint4 hi) {
     return r;
 }
 
-// The shared K loop.  arow[m] points at row m of A (nullptr = zero row);
-// brow[ns] is this lane's weight row for B subtile ns, already offset by the
-// lane's half (64 bytes); nk K-steps of 128 bytes; acc[MT][NSUB] accumulates.
+// The shared K loop.  A row m starts at abase + arow[m] * arow_bytes
+// (arow[m] < 0: a zero row); brow[ns] is this lane's first weight byte for
+// row set ns; nk K-steps of 128 bytes; acc[MT][NSUB] accumulates.
+// Every address derives from the kernel's global-memory arguments, so all
+// loads are global loads (vmcnt only) and waiting for one K-step's
+// activations never drains the weight loads already in flight for later
+// K-steps.
 template <bool kFp8, bool kPacked, int BM, int NSUB, int PF>
-__device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t* const (&brow)[NSUB], int nk,
+__device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const int* arow, int64_t arow_bytes,
+                                      const uint8_t* const (&brow)[NSUB], int nk,
                                       uint8_t* lds, f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
     using TL = Tile<BM>;
     constexpr int MT = TL::MT;
@@ -100,6 +105,18 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
     const int lane = lane_id();
     const int half = lane >> 5;
     const int r32 = lane & 31;
+
+    // this thread's A chunks: fixed rows for the whole K loop (a thread
+    // without a chunk, or a padding row, reads row 0 and keeps zeros)
+    const uint8_t* asrc[TL::APT];
+    bool aok[TL::APT];
+#pragma unroll
+    for (int r = 0; r < TL::APT; ++r) {
+        const int c = tid + r * kFfnThreads;
+        const int row = (c < TL::ACH) ? arow[c >> 3] : -1;
+        aok[r] = row >= 0;
+        asrc[r] = abase + (int64_t)(row >= 0 ? row : 0) * arow_bytes + (c & 7) * 16;
+    }
 
     uint4 areg[TL::APT];                 // A runs one K-step ahead
     // Weights run PF K-steps ahead.  bf16: four 16-byte MFMA operands per row
@@ -109,15 +126,14 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
     constexpr int NB = kFp8 ? 2 : 4;
     BOp breg[PF + 1][NSUB][NB];
 
+    // Loads are issued unconditionally (K-step indices clamped at the end):
+    // with a fixed number of loads per K-step the compiler's wait counts can
+    // wait for just the oldest loads instead of draining everything in flight.
     auto load_a = [&](int k) {
 #pragma unroll
         for (int r = 0; r < TL::APT; ++r) {
-            const int c = tid + r * kFfnThreads;
-            areg[r] = make_uint4(0, 0, 0, 0);
-            if (c < TL::ACH) {
-                const uint8_t* src = arow[c >> 3];
-                if (src) areg[r] = *(const uint4*)(src + (int64_t)k * kStepBytes + (c & 7) * 16);
-            }
+            const uint4 v = *(const uint4*)(asrc[r] + (int64_t)k * kStepBytes);
+            areg[r] = aok[r] ? v : make_uint4(0, 0, 0, 0);
         }
     };
     auto store_a = [&](int buf) {
@@ -182,8 +198,7 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
     // prologue: A step 0 into LDS, weight steps 0..PF-1 in flight
     load_a(0);
 #pragma unroll
-    for (int s = 0; s < PF; ++s)
-        if (s < nk) load_b(breg[s], s);
+    for (int s = 0; s < PF; ++s) load_b(breg[s], min(s, nk - 1));
     store_a(0);
     __syncthreads();
 
@@ -192,8 +207,8 @@ __device__ __forceinline__ void kloop(const uint8_t* const* arow, const uint8_t*
         for (int u = 0; u <= PF; ++u) {
             const int k = k0 + u;
             if (k < nk) {
-                if (k + 1 < nk) load_a(k + 1);
-                if (k + PF < nk) load_b(breg[(u + PF) % (PF + 1)], k + PF);
+                load_a(min(k + 1, nk - 1));
+                load_b(breg[(u + PF) % (PF + 1)], min(k + PF, nk - 1));
                 compute(breg[u], k & 1);
                 if (k + 1 < nk) store_a((k + 1) & 1);
                 __syncthreads();
@@ -275,7 +290,7 @@ __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     using TL = Tile<BM>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
-    __shared__ const uint8_t* arow[BM];
+    __shared__ int arow[BM];
     __shared__ float rowscale[BM];
     int mb, nt;
     if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
@@ -287,8 +302,7 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
         const int slot = a.sorted_ids[(int64_t)mb * BM + tid];
         const bool ok = slot < a.S;
         const int t = ok ? slot / a.K : 0;
-        const uint8_t* xs = kFp8 ? q.xq : (const uint8_t*)a.x;
-        arow[tid] = ok ? xs + (int64_t)t * H * esz : nullptr;
+        arow[tid] = ok ? t : -1;                          // token row of x, -1 = padding
         if (kFp8) rowscale[tid] = ok ? q.sx[t] : 0.f;
     }
     if (BM < TL::ROWS)
@@ -303,7 +317,8 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
         weight_lane_ptr<kPacked>(wbase, I + n0 + r32, (int64_t)H * esz, nt, w, 1, lane)};
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
-    kloop<kFp8, kPacked, BM, 2, PF>(arow, brow, H * esz / kStepBytes, lds, acc);
+    const uint8_t* xs = kFp8 ? (const uint8_t*)q.xq : (const uint8_t*)a.x;
+    kloop<kFp8, kPacked, BM, 2, PF>(xs, arow, (int64_t)H * esz, brow, H * esz / kStepBytes, lds, acc);
 
     const int col = n0 + r32;
     float sg = 1.f, su = 1.f;
@@ -344,7 +359,7 @@ __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     using TL = Tile<BM>;
     __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
-    __shared__ const uint8_t* arow[BM];
+    __shared__ int arow[BM];
     __shared__ int slots[BM];
     __shared__ float rowscale[BM];
     int mb, nt;
@@ -354,7 +369,7 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
     const int H = a.H, I = a.I;
     constexpr int esz = kFp8 ? 1 : 2;
     if (tid < BM) {
-        arow[tid] = h_in + ((int64_t)mb * BM + tid) * I * esz;
+        arow[tid] = mb * BM + tid;                        // sorted row of the intermediate
         slots[tid] = a.sorted_ids[(int64_t)mb * BM + tid];
         if (kFp8) rowscale[tid] = sa[(int64_t)mb * BM + tid];
     }
@@ -370,7 +385,7 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
         weight_lane_ptr<kPacked>(wbase, n0 + 32 + r32, (int64_t)I * esz, nt, w, 1, lane)};
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
-    kloop<kFp8, kPacked, BM, 2, PF>(arow, brow, I * esz / kStepBytes, lds, acc);
+    kloop<kFp8, kPacked, BM, 2, PF>(h_in, arow, (int64_t)I * esz, brow, I * esz / kStepBytes, lds, acc);
 
     float s0 = 1.f, s1 = 1.f;
     if (kFp8) {
