@@ -71,6 +71,24 @@ constexpr int kLdsPitch = kStepBytes + 16;      // padded LDS row, bytes
 constexpr int kPackWaveBytes = 2 * 4 * 1024;              // two row sets x four quarters
 constexpr int kPackStepBytes = 4 * kPackWaveBytes;        // four waves
 
+// Cache policy of the weight loads.  A tile whose expert has a single M block
+// in the launch is the only reader of its weights: streaming (non-temporal)
+// loads keep those bytes from displacing reusable lines.  Where several M
+// blocks of one expert run close together their tiles re-read the same
+// weights, and ordinary loads let the repeats hit L2.
+// 0 = always ordinary, 1 = always streaming, 2 = chosen per tile as above.
+#ifndef MOE_FFN_NT_MODE
+#define MOE_FFN_NT_MODE 2
+#endif
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool kNT>
+__device__ __forceinline__ uint4 load_weight(const uint8_t* p) {
+    if constexpr (kNT) return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)p));
+    else return *(const uint4*)p;
+}
+
 template <int BM>
 struct Tile {
     static constexpr int MT = (BM < 32 ? 32 : BM) / 32;         // 32-row MFMA tiles
@@ -95,7 +113,7 @@ __device__ __forceinline__ i32x8_t as_i32x8(uint4 lo, uint4 hi) {
 // loads are global loads (vmcnt only) and waiting for one K-step's
 // activations never drains the weight loads already in flight for later
 // K-steps.
-template <bool kFp8, bool kPacked, int BM, int NSUB, int PF>
+template <bool kFp8, bool kPacked, bool kNT, int BM, int NSUB, int PF, int LA>
 __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const int* arow, int64_t arow_bytes,
                                       const uint8_t* const (&brow)[NSUB], int nk,
                                       uint8_t* lds, f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
@@ -118,7 +136,10 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
         asrc[r] = abase + (int64_t)(row >= 0 ? row : 0) * arow_bytes + (c & 7) * 16;
     }
 
-    uint4 areg[TL::APT];                 // A runs one K-step ahead
+    // A runs LA K-steps ahead in a ring of LA register sets (LA is 1 or PF+1,
+    // so ring slots stay compile-time indices in the loop unrolled by PF+1).
+    static_assert(LA == 1 || LA == PF + 1, "activation lookahead must divide the unroll");
+    uint4 areg[LA][TL::APT];
     // Weights run PF K-steps ahead.  bf16: four 16-byte MFMA operands per row
     // set; fp8: two 32-byte operands, each assembled from two 16-byte loads
     // straight into its register tuple.
@@ -129,19 +150,19 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
     // Loads are issued unconditionally (K-step indices clamped at the end):
     // with a fixed number of loads per K-step the compiler's wait counts can
     // wait for just the oldest loads instead of draining everything in flight.
-    auto load_a = [&](int k) {
+    auto load_a = [&](uint4 (&dst)[TL::APT], int k) {
 #pragma unroll
         for (int r = 0; r < TL::APT; ++r) {
             const uint4 v = *(const uint4*)(asrc[r] + (int64_t)k * kStepBytes);
-            areg[r] = aok[r] ? v : make_uint4(0, 0, 0, 0);
+            dst[r] = aok[r] ? v : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](const uint4 (&src)[TL::APT], int buf) {
 #pragma unroll
         for (int r = 0; r < TL::APT; ++r) {
             const int c = tid + r * kFfnThreads;
             if (c < TL::ACH)
-                *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = areg[r];
+                *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = src[r];
         }
     };
     constexpr int64_t kB = kPacked ? kPackStepBytes : kStepBytes;   // per K-step
@@ -153,13 +174,13 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
             if constexpr (kFp8) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const uint4 lo = *(const uint4*)(src + (2 * j) * qB);
-                    const uint4 hi = *(const uint4*)(src + (2 * j + 1) * qB);
+                    const uint4 lo = load_weight<kNT>(src + (2 * j) * qB);
+                    const uint4 hi = load_weight<kNT>(src + (2 * j + 1) * qB);
                     dst[ns][j] = as_i32x8(lo, hi);
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dst[ns][q] = *(const uint4*)(src + q * qB);
+                for (int q = 0; q < 4; ++q) dst[ns][q] = load_weight<kNT>(src + q * qB);
             }
         }
     };
@@ -195,23 +216,123 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
         }
     };
 
-    // prologue: A step 0 into LDS, weight steps 0..PF-1 in flight
-    load_a(0);
+    // prologue: A steps 0..LA-1 loaded and step 0 stored to LDS, weight steps
+    // 0..PF-1 in flight
+#pragma unroll
+    for (int j = 0; j < LA; ++j) load_a(areg[j], min(j, nk - 1));
 #pragma unroll
     for (int s = 0; s < PF; ++s) load_b(breg[s], min(s, nk - 1));
-    store_a(0);
+    store_a(areg[0], 0);
     __syncthreads();
 
+    // step k: load A(k+LA) into the slot A(k) left (stored during step k-1),
+    // load weights for step k+PF, multiply step k, store A(k+1) to the other
+    // LDS buffer.
     for (int k0 = 0; k0 < nk; k0 += PF + 1) {
 #pragma unroll
         for (int u = 0; u <= PF; ++u) {
             const int k = k0 + u;
             if (k < nk) {
-                load_a(min(k + 1, nk - 1));
+                load_a(areg[u % LA], min(k + LA, nk - 1));
                 load_b(breg[(u + PF) % (PF + 1)], min(k + PF, nk - 1));
                 compute(breg[u], k & 1);
-                if (k + 1 < nk) store_a((k + 1) & 1);
+                if (k + 1 < nk) store_a(areg[(u + 1) % LA], (k + 1) & 1);
                 __syncthreads();
+            }
+        }
+    }
+}
+
+// The K loop without LDS: every wave loads its own A operands (the rows of
+// the block, 64 bytes of each per K-step per lane) straight from global
+// memory -- the four waves of a workgroup read the same rows, so three of
+// four reads hit L1 -- and runs with no workgroup barrier at all, so a wave
+// never waits on another wave's memory latency.  A and weights both run PF
+// K-steps ahead in register rings.
+template <bool kFp8, bool kPacked, int BM, int NSUB, int PF>
+__device__ __forceinline__ void kloop_direct(const uint8_t* __restrict__ abase, const int* arow,
+                                             int64_t arow_bytes, const uint8_t* const (&brow)[NSUB], int nk,
+                                             f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
+    constexpr int MT = Tile<BM>::MT;
+    const int lane = lane_id();
+    const int half = lane >> 5;
+    const int r32 = lane & 31;
+    using Op = typename std::conditional<kFp8, i32x8_t, uint4>::type;
+    constexpr int NOP = kFp8 ? 2 : 4;                          // operands per row set per K-step
+    constexpr int64_t kB = kPacked ? kPackStepBytes : kStepBytes;
+    constexpr int qB = kPacked ? 1024 : 16;
+
+    const uint8_t* asrc[MT];
+    bool aok[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 32 + r32;
+        const int row = (m < BM) ? arow[m] : -1;
+        aok[mt] = row >= 0;
+        asrc[mt] = abase + (int64_t)(row >= 0 ? row : 0) * arow_bytes + half * 64;
+    }
+    Op areg[PF + 1][MT][NOP];
+    Op breg[PF + 1][NSUB][NOP];
+
+    auto load = [&](Op (&da)[MT][NOP], Op (&db)[NSUB][NOP], int k) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint8_t* src = asrc[mt] + (int64_t)k * kStepBytes;
+            if constexpr (kFp8) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    uint4 lo = *(const uint4*)(src + 32 * j);
+                    uint4 hi = *(const uint4*)(src + 32 * j + 16);
+                    if (!aok[mt]) lo = hi = make_uint4(0, 0, 0, 0);
+                    da[mt][j] = as_i32x8(lo, hi);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 v = *(const uint4*)(src + 16 * q);
+                    da[mt][q] = aok[mt] ? v : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int ns = 0; ns < NSUB; ++ns) {
+            const uint8_t* src = brow[ns] + (int64_t)k * kB;
+            if constexpr (kFp8) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    db[ns][j] = as_i32x8(*(const uint4*)(src + (2 * j) * qB), *(const uint4*)(src + (2 * j + 1) * qB));
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) db[ns][q] = *(const uint4*)(src + q * qB);
+            }
+        }
+    };
+    auto compute = [&](const Op (&a)[MT][NOP], const Op (&b)[NSUB][NOP]) {
+#pragma unroll
+        for (int kk = 0; kk < NOP; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int ns = 0; ns < NSUB; ++ns) {
+                    if constexpr (kFp8)
+                        acc[mt][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a[mt][kk], b[ns][kk], acc[mt][ns], 0, 0, 0, 127, 0, 127);
+                    else
+                        acc[mt][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            as_bf16x8(a[mt][kk]), as_bf16x8(b[ns][kk]), acc[mt][ns], 0, 0, 0);
+                }
+    };
+
+#pragma unroll
+    for (int s = 0; s < PF; ++s) load(areg[s], breg[s], min(s, nk - 1));
+    for (int k0 = 0; k0 < nk; k0 += PF + 1) {
+#pragma unroll
+        for (int u = 0; u <= PF; ++u) {
+            const int k = k0 + u;
+            if (k < nk) {
+                const int nxt = (u + PF) % (PF + 1);
+                load(areg[nxt], breg[nxt], min(k + PF, nk - 1));
+                compute(areg[u], breg[u]);
             }
         }
     }
@@ -273,23 +394,58 @@ struct Fp8Ws {
     float* sa;          // [C]   per-row scales
 };
 
+// Whether M block mb (of expert e) reads its weights with the streaming policy.
+__device__ __forceinline__ bool stream_weights(const FfnArgs& a, int mb, int BM, int e) {
+    if (MOE_FFN_NT_MODE == 0) return false;
+    if (MOE_FFN_NT_MODE == 1) return true;
+    const int nblk = a.post_padded[0] / BM;
+    return (mb == 0 || a.expert_ids[mb - 1] != e) && (mb + 1 >= nblk || a.expert_ids[mb + 1] != e);
+}
+
 // ------------------------------------------------------------------ stage 1 --
 // bf16: h_out is bf16 [C,I].  fp8: writes fp32 a and the row amax.
 // Workgroups per CU the register budget is sized for: two (8 waves per CU),
 // except the fp8 128-row tile, whose 32-byte operand tuples need the whole
 // register file of one workgroup.
+#ifndef MOE_FFN_FP8_128_OCC
+#define MOE_FFN_FP8_128_OCC 1
+#endif
+#ifndef MOE_FFN_FP8_128_PF
+#define MOE_FFN_FP8_128_PF 2
+#endif
+// Activation path: 1 = every wave loads its own A from global memory (no LDS,
+// no barriers), 0 = A staged once per workgroup through LDS.
+#ifndef MOE_FFN_DIRECT
+#define MOE_FFN_DIRECT 0
+#endif
+#ifndef MOE_FFN_DIRECT_PF
+#define MOE_FFN_DIRECT_PF 1
+#endif
 template <bool kFp8, int BM>
-constexpr int ffn_min_blocks() { return (kFp8 && BM >= 128) ? 1 : 2; }
+constexpr int ffn_min_blocks() {
+    return MOE_FFN_DIRECT ? (BM >= 128 ? 1 : 2) : ((kFp8 && BM >= 128) ? MOE_FFN_FP8_128_OCC : 2);
+}
 // Weight K-steps in flight: fewer for the register-hungry 128-row tile at two
 // workgroups per CU, more where one workgroup has the CU to itself.
+// Activation K-steps in flight: PF+1 where registers allow, 1 for the bf16
+// 128-row tile (two workgroups per CU leave no room for the ring).
+#ifndef MOE_FFN_LA_FULL
+#define MOE_FFN_LA_FULL 1
+#endif
+template <bool kFp8, int BM, int PF>
+constexpr int ffn_la() { return ((BM < 128 || kFp8) && MOE_FFN_LA_FULL) ? PF + 1 : 1; }
 template <bool kFp8, int BM>
-constexpr int ffn_pf() { return BM < 128 ? MOE_FFN_PF : (kFp8 ? MOE_FFN_PF : MOE_FFN_PF128); }
+constexpr int ffn_pf() {
+    if (MOE_FFN_DIRECT) return BM <= 32 ? 2 : (BM == 64 ? MOE_FFN_DIRECT_PF : 2);
+    return BM < 128 ? MOE_FFN_PF : (kFp8 ? MOE_FFN_FP8_128_PF : MOE_FFN_PF128);
+}
 
 template <bool kFp8, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     using TL = Tile<BM>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
+    constexpr bool kDirect = MOE_FFN_DIRECT;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kDirect ? 16 : TL::LDS_BYTES];
     __shared__ int arow[BM];
     __shared__ float rowscale[BM];
     int mb, nt;
@@ -305,7 +461,7 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
         arow[tid] = ok ? t : -1;                          // token row of x, -1 = padding
         if (kFp8) rowscale[tid] = ok ? q.sx[t] : 0.f;
     }
-    if (BM < TL::ROWS)
+    if (!kDirect && BM < TL::ROWS)
         for (int i = tid; i < TL::LDS_BYTES / 16; i += kFfnThreads) ((uint4*)lds)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
@@ -318,7 +474,14 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
     const uint8_t* xs = kFp8 ? (const uint8_t*)q.xq : (const uint8_t*)a.x;
-    kloop<kFp8, kPacked, BM, 2, PF>(xs, arow, (int64_t)H * esz, brow, H * esz / kStepBytes, lds, acc);
+    if constexpr (kDirect)
+        kloop_direct<kFp8, kPacked, BM, 2, PF>(xs, arow, (int64_t)H * esz, brow, H * esz / kStepBytes, acc);
+    else if (stream_weights(a, mb, BM, e))
+        kloop<kFp8, kPacked, true, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(xs, arow, (int64_t)H * esz, brow,
+                                                                    H * esz / kStepBytes, lds, acc);
+    else
+        kloop<kFp8, kPacked, false, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(xs, arow, (int64_t)H * esz, brow,
+                                                                     H * esz / kStepBytes, lds, acc);
 
     const int col = n0 + r32;
     float sg = 1.f, su = 1.f;
@@ -358,7 +521,8 @@ template <bool kFp8, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     using TL = Tile<BM>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
+    constexpr bool kDirect = MOE_FFN_DIRECT;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kDirect ? 16 : TL::LDS_BYTES];
     __shared__ int arow[BM];
     __shared__ int slots[BM];
     __shared__ float rowscale[BM];
@@ -373,7 +537,7 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
         slots[tid] = a.sorted_ids[(int64_t)mb * BM + tid];
         if (kFp8) rowscale[tid] = sa[(int64_t)mb * BM + tid];
     }
-    if (BM < TL::ROWS)
+    if (!kDirect && BM < TL::ROWS)
         for (int i = tid; i < TL::LDS_BYTES / 16; i += kFfnThreads) ((uint4*)lds)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
@@ -385,7 +549,14 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
         weight_lane_ptr<kPacked>(wbase, n0 + 32 + r32, (int64_t)I * esz, nt, w, 1, lane)};
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
-    kloop<kFp8, kPacked, BM, 2, PF>(h_in, arow, (int64_t)I * esz, brow, I * esz / kStepBytes, lds, acc);
+    if constexpr (kDirect)
+        kloop_direct<kFp8, kPacked, BM, 2, PF>(h_in, arow, (int64_t)I * esz, brow, I * esz / kStepBytes, acc);
+    else if (stream_weights(a, mb, BM, e))
+        kloop<kFp8, kPacked, true, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(h_in, arow, (int64_t)I * esz, brow,
+                                                                    I * esz / kStepBytes, lds, acc);
+    else
+        kloop<kFp8, kPacked, false, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(h_in, arow, (int64_t)I * esz, brow,
+                                                                     I * esz / kStepBytes, lds, acc);
 
     float s0 = 1.f, s1 = 1.f;
     if (kFp8) {
