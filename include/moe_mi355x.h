@@ -168,7 +168,7 @@ moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32
  * aligned, clobbered.
  * weight_layout MOE_LAYOUT_PACKED means w13 and w2 were rewritten by
  * moe_prepack_weights (below); the scales stay in their canonical layout.
- * Limits: B in {16,32,64,128}; H a multiple of 256 and I a multiple of 128
+ * Limits: B in {16,32,64,128,256}; H a multiple of 256 and I a multiple of 128
  * (fp32: multiples of 64, canonical layout only); E <= 1024.
  */
 typedef enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layout_t;

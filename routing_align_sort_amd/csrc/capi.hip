@@ -22,7 +22,7 @@ bool align_args_ok(int32_t T, int32_t K, int32_t E, int32_t B) {
     return S + capacity(S, E, B) < ((int64_t)1 << 31);
 }
 
-bool ffn_block_ok(int32_t B) { return B == 16 || B == 32 || B == 64 || B == 128; }
+bool ffn_block_ok(int32_t B) { return B == 16 || B == 32 || B == 64 || B == 128 || B == 256; }
 
 }  // namespace
 

@@ -71,6 +71,10 @@ constexpr int kLdsPitch = kStepBytes + 16;      // padded LDS row, bytes
 constexpr int kPackWaveBytes = 2 * 4 * 1024;              // two row sets x four quarters
 constexpr int kPackStepBytes = 4 * kPackWaveBytes;        // four waves
 
+#ifndef MOE_FFN_PIN_LOADS
+#define MOE_FFN_PIN_LOADS 1
+#endif
+
 // Cache policy of the weight loads.  A tile whose expert has a single M block
 // in the launch is the only reader of its weights: streaming (non-temporal)
 // loads keep those bytes from displacing reusable lines.  Where several M
@@ -93,8 +97,9 @@ template <int BM>
 struct Tile {
     static constexpr int MT = (BM < 32 ? 32 : BM) / 32;         // 32-row MFMA tiles
     static constexpr int ROWS = MT * 32;
-    static constexpr int ACH = BM * (kStepBytes / 16);           // 16-byte A chunks per K-step
-    static constexpr int APT = (ACH + kFfnThreads - 1) / kFfnThreads;
+    static constexpr int ACH = ROWS * (kStepBytes / 16);         // 16-byte A chunks per K-step
+    static constexpr int APT = ACH / kFfnThreads;                // chunks per thread (exact)
+    static_assert(ACH % kFfnThreads == 0, "every thread moves whole chunks");
     static constexpr int LDS_BYTES = 2 * ROWS * kLdsPitch;
 };
 
@@ -124,15 +129,16 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
     const int half = lane >> 5;
     const int r32 = lane & 31;
 
-    // this thread's A chunks: fixed rows for the whole K loop (a thread
-    // without a chunk, or a padding row, reads row 0 and keeps zeros)
+    // this thread's A chunks: fixed rows for the whole K loop.  Every row of
+    // the MFMA tile is loaded and stored, so the loop holds no lane-dependent
+    // condition.  A padding row (-1), and a tile row past the block, reads row
+    // 0 instead: rows of the product depend only on their own A row, and the
+    // outputs of those rows are never used.
     const uint8_t* asrc[TL::APT];
-    bool aok[TL::APT];
 #pragma unroll
     for (int r = 0; r < TL::APT; ++r) {
         const int c = tid + r * kFfnThreads;
-        const int row = (c < TL::ACH) ? arow[c >> 3] : -1;
-        aok[r] = row >= 0;
+        const int row = (c >> 3) < BM ? arow[c >> 3] : -1;
         asrc[r] = abase + (int64_t)(row >= 0 ? row : 0) * arow_bytes + (c & 7) * 16;
     }
 
@@ -152,17 +158,14 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
     // wait for just the oldest loads instead of draining everything in flight.
     auto load_a = [&](uint4 (&dst)[TL::APT], int k) {
 #pragma unroll
-        for (int r = 0; r < TL::APT; ++r) {
-            const uint4 v = *(const uint4*)(asrc[r] + (int64_t)k * kStepBytes);
-            dst[r] = aok[r] ? v : make_uint4(0, 0, 0, 0);
-        }
+        for (int r = 0; r < TL::APT; ++r)
+            dst[r] = __builtin_bit_cast(uint4, *(const u32x4_t*)(asrc[r] + (int64_t)k * kStepBytes));
     };
     auto store_a = [&](const uint4 (&src)[TL::APT], int buf) {
 #pragma unroll
         for (int r = 0; r < TL::APT; ++r) {
             const int c = tid + r * kFfnThreads;
-            if (c < TL::ACH)
-                *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = src[r];
+            *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = src[r];
         }
     };
     constexpr int64_t kB = kPacked ? kPackStepBytes : kStepBytes;   // per K-step
@@ -235,104 +238,15 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
             if (k < nk) {
                 load_a(areg[u % LA], min(k + LA, nk - 1));
                 load_b(breg[(u + PF) % (PF + 1)], min(k + PF, nk - 1));
+                // keep the loads ahead of this step's MFMAs: left to itself
+                // the scheduler sinks them to the end of the step
+                if (MOE_FFN_PIN_LOADS) __builtin_amdgcn_sched_barrier(0);
                 compute(breg[u], k & 1);
-                if (k + 1 < nk) store_a(areg[(u + 1) % LA], (k + 1) & 1);
+                // unconditional: after the last step it rewrites the idle
+                // buffer with data nobody reads, but a condition here would
+                // let the compiler sink the A loads down to this store
+                store_a(areg[(u + 1) % LA], (k + 1) & 1);
                 __syncthreads();
-            }
-        }
-    }
-}
-
-// The K loop without LDS: every wave loads its own A operands (the rows of
-// the block, 64 bytes of each per K-step per lane) straight from global
-// memory -- the four waves of a workgroup read the same rows, so three of
-// four reads hit L1 -- and runs with no workgroup barrier at all, so a wave
-// never waits on another wave's memory latency.  A and weights both run PF
-// K-steps ahead in register rings.
-template <bool kFp8, bool kPacked, int BM, int NSUB, int PF>
-__device__ __forceinline__ void kloop_direct(const uint8_t* __restrict__ abase, const int* arow,
-                                             int64_t arow_bytes, const uint8_t* const (&brow)[NSUB], int nk,
-                                             f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
-    constexpr int MT = Tile<BM>::MT;
-    const int lane = lane_id();
-    const int half = lane >> 5;
-    const int r32 = lane & 31;
-    using Op = typename std::conditional<kFp8, i32x8_t, uint4>::type;
-    constexpr int NOP = kFp8 ? 2 : 4;                          // operands per row set per K-step
-    constexpr int64_t kB = kPacked ? kPackStepBytes : kStepBytes;
-    constexpr int qB = kPacked ? 1024 : 16;
-
-    const uint8_t* asrc[MT];
-    bool aok[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = mt * 32 + r32;
-        const int row = (m < BM) ? arow[m] : -1;
-        aok[mt] = row >= 0;
-        asrc[mt] = abase + (int64_t)(row >= 0 ? row : 0) * arow_bytes + half * 64;
-    }
-    Op areg[PF + 1][MT][NOP];
-    Op breg[PF + 1][NSUB][NOP];
-
-    auto load = [&](Op (&da)[MT][NOP], Op (&db)[NSUB][NOP], int k) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint8_t* src = asrc[mt] + (int64_t)k * kStepBytes;
-            if constexpr (kFp8) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    uint4 lo = *(const uint4*)(src + 32 * j);
-                    uint4 hi = *(const uint4*)(src + 32 * j + 16);
-                    if (!aok[mt]) lo = hi = make_uint4(0, 0, 0, 0);
-                    da[mt][j] = as_i32x8(lo, hi);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 v = *(const uint4*)(src + 16 * q);
-                    da[mt][q] = aok[mt] ? v : make_uint4(0, 0, 0, 0);
-                }
-            }
-        }
-#pragma unroll
-        for (int ns = 0; ns < NSUB; ++ns) {
-            const uint8_t* src = brow[ns] + (int64_t)k * kB;
-            if constexpr (kFp8) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    db[ns][j] = as_i32x8(*(const uint4*)(src + (2 * j) * qB), *(const uint4*)(src + (2 * j + 1) * qB));
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) db[ns][q] = *(const uint4*)(src + q * qB);
-            }
-        }
-    };
-    auto compute = [&](const Op (&a)[MT][NOP], const Op (&b)[NSUB][NOP]) {
-#pragma unroll
-        for (int kk = 0; kk < NOP; ++kk)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int ns = 0; ns < NSUB; ++ns) {
-                    if constexpr (kFp8)
-                        acc[mt][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            a[mt][kk], b[ns][kk], acc[mt][ns], 0, 0, 0, 127, 0, 127);
-                    else
-                        acc[mt][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            as_bf16x8(a[mt][kk]), as_bf16x8(b[ns][kk]), acc[mt][ns], 0, 0, 0);
-                }
-    };
-
-#pragma unroll
-    for (int s = 0; s < PF; ++s) load(areg[s], breg[s], min(s, nk - 1));
-    for (int k0 = 0; k0 < nk; k0 += PF + 1) {
-#pragma unroll
-        for (int u = 0; u <= PF; ++u) {
-            const int k = k0 + u;
-            if (k < nk) {
-                const int nxt = (u + PF) % (PF + 1);
-                load(areg[nxt], breg[nxt], min(k + PF, nk - 1));
-                compute(areg[u], breg[u]);
             }
         }
     }
@@ -404,48 +318,68 @@ __device__ __forceinline__ bool stream_weights(const FfnArgs& a, int mb, int BM,
 
 // ------------------------------------------------------------------ stage 1 --
 // bf16: h_out is bf16 [C,I].  fp8: writes fp32 a and the row amax.
-// Workgroups per CU the register budget is sized for: two (8 waves per CU),
-// except the fp8 128-row tile, whose 32-byte operand tuples need the whole
-// register file of one workgroup.
+// Per-tile tuning: workgroups per CU the register budget is sized for, the
+// weight K-steps in flight (PF, a register ring of PF + 1 steps) and whether
+// the activations also run PF + 1 steps ahead (else one step).  Tiles up to
+// 64 rows: two workgroups per CU.  The 128-row tile: 128 accumulator
+// registers; two workgroups per CU leave room for one weight step in flight.
+// The 256-row tile: 256 accumulator registers (the AGPR half of the file),
+// one workgroup per CU.
+#ifndef MOE_FFN_OCC128
+#define MOE_FFN_OCC128 2
+#endif
+#ifndef MOE_FFN_LA128
+#define MOE_FFN_LA128 0
+#endif
 #ifndef MOE_FFN_FP8_128_OCC
-#define MOE_FFN_FP8_128_OCC 1
+#define MOE_FFN_FP8_128_OCC 2
 #endif
 #ifndef MOE_FFN_FP8_128_PF
-#define MOE_FFN_FP8_128_PF 2
+#define MOE_FFN_FP8_128_PF 1
 #endif
-// Activation path: 1 = every wave loads its own A from global memory (no LDS,
-// no barriers), 0 = A staged once per workgroup through LDS.
-#ifndef MOE_FFN_DIRECT
-#define MOE_FFN_DIRECT 0
+#ifndef MOE_FFN_FP8_128_LA
+#define MOE_FFN_FP8_128_LA 1
 #endif
-#ifndef MOE_FFN_DIRECT_PF
-#define MOE_FFN_DIRECT_PF 1
+#ifndef MOE_FFN_PF256
+#define MOE_FFN_PF256 2
 #endif
-template <bool kFp8, int BM>
-constexpr int ffn_min_blocks() {
-    return MOE_FFN_DIRECT ? (BM >= 128 ? 1 : 2) : ((kFp8 && BM >= 128) ? MOE_FFN_FP8_128_OCC : 2);
-}
-// Weight K-steps in flight: fewer for the register-hungry 128-row tile at two
-// workgroups per CU, more where one workgroup has the CU to itself.
-// Activation K-steps in flight: PF+1 where registers allow, 1 for the bf16
-// 128-row tile (two workgroups per CU leave no room for the ring).
+#ifndef MOE_FFN_LA256
+#define MOE_FFN_LA256 0
+#endif
+#ifndef MOE_FFN_FP8_256_PF
+#define MOE_FFN_FP8_256_PF 1
+#endif
+#ifndef MOE_FFN_FP8_256_LA
+#define MOE_FFN_FP8_256_LA 0
+#endif
 #ifndef MOE_FFN_LA_FULL
 #define MOE_FFN_LA_FULL 1
 #endif
-template <bool kFp8, int BM, int PF>
-constexpr int ffn_la() { return ((BM < 128 || kFp8) && MOE_FFN_LA_FULL) ? PF + 1 : 1; }
+template <bool kFp8, int BM>
+constexpr int ffn_min_blocks() {
+    if (BM >= 256) return 1;
+    if (BM == 128) return kFp8 ? MOE_FFN_FP8_128_OCC : MOE_FFN_OCC128;
+    return 2;
+}
 template <bool kFp8, int BM>
 constexpr int ffn_pf() {
-    if (MOE_FFN_DIRECT) return BM <= 32 ? 2 : (BM == 64 ? MOE_FFN_DIRECT_PF : 2);
-    return BM < 128 ? MOE_FFN_PF : (kFp8 ? MOE_FFN_FP8_128_PF : MOE_FFN_PF128);
+    if (BM >= 256) return kFp8 ? MOE_FFN_FP8_256_PF : MOE_FFN_PF256;
+    if (BM == 128) return kFp8 ? MOE_FFN_FP8_128_PF : MOE_FFN_PF128;
+    return MOE_FFN_PF;
+}
+template <bool kFp8, int BM, int PF>
+constexpr int ffn_la() {
+    const bool full = BM < 128    ? MOE_FFN_LA_FULL
+                      : BM == 128 ? (kFp8 ? MOE_FFN_FP8_128_LA : MOE_FFN_LA128)
+                                  : (kFp8 ? MOE_FFN_FP8_256_LA : MOE_FFN_LA256);
+    return full ? PF + 1 : 1;
 }
 
 template <bool kFp8, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     using TL = Tile<BM>;
-    constexpr bool kDirect = MOE_FFN_DIRECT;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kDirect ? 16 : TL::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[Tile<BM>::LDS_BYTES];
     __shared__ int arow[BM];
     __shared__ float rowscale[BM];
     int mb, nt;
@@ -461,8 +395,6 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
         arow[tid] = ok ? t : -1;                          // token row of x, -1 = padding
         if (kFp8) rowscale[tid] = ok ? q.sx[t] : 0.f;
     }
-    if (!kDirect && BM < TL::ROWS)
-        for (int i = tid; i < TL::LDS_BYTES / 16; i += kFfnThreads) ((uint4*)lds)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     const int n0 = nt * 128 + w * 32;                       // this wave's intermediate columns
@@ -474,9 +406,7 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
     const uint8_t* xs = kFp8 ? (const uint8_t*)q.xq : (const uint8_t*)a.x;
-    if constexpr (kDirect)
-        kloop_direct<kFp8, kPacked, BM, 2, PF>(xs, arow, (int64_t)H * esz, brow, H * esz / kStepBytes, acc);
-    else if (stream_weights(a, mb, BM, e))
+    if (stream_weights(a, mb, BM, e))
         kloop<kFp8, kPacked, true, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(xs, arow, (int64_t)H * esz, brow,
                                                                     H * esz / kStepBytes, lds, acc);
     else
@@ -521,8 +451,7 @@ template <bool kFp8, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     using TL = Tile<BM>;
-    constexpr bool kDirect = MOE_FFN_DIRECT;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kDirect ? 16 : TL::LDS_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[Tile<BM>::LDS_BYTES];
     __shared__ int arow[BM];
     __shared__ int slots[BM];
     __shared__ float rowscale[BM];
@@ -537,8 +466,6 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
         slots[tid] = a.sorted_ids[(int64_t)mb * BM + tid];
         if (kFp8) rowscale[tid] = sa[(int64_t)mb * BM + tid];
     }
-    if (!kDirect && BM < TL::ROWS)
-        for (int i = tid; i < TL::LDS_BYTES / 16; i += kFfnThreads) ((uint4*)lds)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     const int n0 = nt * 256 + w * 64;                       // this wave's output columns
@@ -549,9 +476,7 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
         weight_lane_ptr<kPacked>(wbase, n0 + 32 + r32, (int64_t)I * esz, nt, w, 1, lane)};
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
-    if constexpr (kDirect)
-        kloop_direct<kFp8, kPacked, BM, 2, PF>(h_in, arow, (int64_t)I * esz, brow, I * esz / kStepBytes, acc);
-    else if (stream_weights(a, mb, BM, e))
+    if (stream_weights(a, mb, BM, e))
         kloop<kFp8, kPacked, true, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(h_in, arow, (int64_t)I * esz, brow,
                                                                     I * esz / kStepBytes, lds, acc);
     else
@@ -736,6 +661,7 @@ static hipError_t launch_mfma_layout(const FfnArgs& a, void* ws, hipStream_t str
         case 32: return launch_mfma_bm<kFp8, kPacked, 32>(a, ws, stream, ev);
         case 64: return launch_mfma_bm<kFp8, kPacked, 64>(a, ws, stream, ev);
         case 128: return launch_mfma_bm<kFp8, kPacked, 128>(a, ws, stream, ev);
+        case 256: return launch_mfma_bm<kFp8, kPacked, 256>(a, ws, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }

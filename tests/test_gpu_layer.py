@@ -52,7 +52,7 @@ def test_layer_tiny_fp32():
     check_layer(cfg, L, np.arange(cfg["T"]), label="tiny fp32 B=16")
 
 
-@pytest.mark.parametrize("B", [16, 32, 64, 128])
+@pytest.mark.parametrize("B", [16, 32, 64, 128, 256])
 def test_layer_small_bf16_all_tokens(B):
     dev = device()
     cfg = ms.scaled("decode_bf16", T=300, H=512, I=384, E=16, K=4, n_group=4, topk_group=2)
@@ -60,7 +60,7 @@ def test_layer_small_bf16_all_tokens(B):
     check_layer(cfg, L, np.arange(cfg["T"]), B=B, label=f"small bf16 B={B}")
 
 
-@pytest.mark.parametrize("B", [16, 32, 64, 128])
+@pytest.mark.parametrize("B", [16, 32, 64, 128, 256])
 def test_layer_small_fp8_all_tokens(B):
     dev = device()
     cfg = ms.scaled("prefill_fp8", T=333, H=768, I=256, E=12)
@@ -76,7 +76,7 @@ def test_ffn_output_is_block_size_invariant():
             cfg = ms.scaled(name, T=200, H=256, I=256, E=8)
         L = ms.make_layer(cfg, device=dev)
         ys = []
-        for B in (16, 32, 64, 128):
+        for B in (16, 32, 64, 128, 256):
             layer, _ = run_layer(cfg, L, B)
             ys.append(layer.y_slots.clone())
         for y in ys[1:]:
@@ -91,7 +91,7 @@ def test_packed_weights_give_identical_results():
             over.update(K=3, n_group=2, topk_group=2)
         cfg = ms.scaled(name, **over)
         L = ms.make_layer(cfg, device=dev)
-        for B in (16, 64, 128):
+        for B in (16, 64, 128, 256):
             ys = []
             for packed in (False, True):
                 layer = make_gpu_layer(cfg, L, B, packed=packed)
