@@ -152,26 +152,59 @@ def summarize(cfg, B, r):
     }
 
 
-def align_only(dev, iters=200):
-    """Align & Sort alone on 16384 tokens x top-8 of 256 experts (Zipf 1.1), block 64."""
+_SPIN = {}
+
+
+def _spin_cycles(dev, target_ms=3.0):
+    """Argument of torch.cuda._sleep that keeps the GPU busy for ~target_ms."""
+    import torch
+
+    import routing_align_sort_amd as moe
+
+    if dev not in _SPIN:
+        ev = moe.HipEvents(2)
+        n = 1 << 20
+        torch.cuda.synchronize()
+        ev.record(0)
+        torch.cuda._sleep(n)
+        ev.record(1)
+        torch.cuda.synchronize()
+        ms = max(ev.elapsed_ms(0, 1), 1e-3)
+        ev.close()
+        _SPIN[dev] = int(n * target_ms / ms)
+    return _SPIN[dev]
+
+
+def align_timed(dev, T, iters=200, cold=False, K=8, E=256, B=64, zipf_s=1.1):
+    """Align & Sort alone on T tokens x top-K of E experts (Zipf), event-timed
+    per call.  cold=True rewrites a 512 MB buffer between calls so that the
+    ids and outputs are not in L2 or the infinity cache."""
     import numpy as np
     import torch
 
     import moe_synth as ms
     import routing_align_sort_amd as moe
 
-    cfg = ms.CONFIGS["align_16k"]
-    ids_np = ms.zipf_topk_ids(0, ms.TAG_IDS, cfg["T"], cfg["K"], cfg["E"], cfg["zipf_s"])
+    ids_np = ms.zipf_topk_ids(0, ms.TAG_IDS, T, K, E, zipf_s)
     ids = torch.from_numpy(ids_np).to(dev)
-    E, B = cfg["E"], cfg["B"]
-    ws_b = moe.moe_align_sort_workspace_bytes(cfg["T"], cfg["K"], E, B)
+    ws_b = moe.moe_align_sort_workspace_bytes(T, K, E, B)
     ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=dev)
     out = moe.moe_align_sort(ids, E, B, workspace=ws)            # allocates the outputs once
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
     ev = moe.HipEvents(2 * iters)
-    for _ in range(20):
+    for _ in range(10):
         moe.moe_align_sort(ids, E, B, workspace=ws, **out)
     torch.cuda.synchronize()
+    # A GPU-side spin ahead of every batch lets the host queue the batch
+    # before the GPU reaches it, so the events time the kernels and not the
+    # host's launch latency.
+    spin = _spin_cycles(dev)
+    batch = 20
     for i in range(iters):
+        if i % batch == 0:
+            torch.cuda._sleep(spin)
+        if cold:
+            scrub.fill_(i & 0xFF)
         ev.record(2 * i)
         moe.moe_align_sort(ids, E, B, workspace=ws, **out)
         ev.record(2 * i + 1)
@@ -181,13 +214,31 @@ def align_only(dev, iters=200):
     P = int(out["num_tokens_post_padded"].item())
     S = ids_np.size
     C = out["sorted_token_ids"].numel()
-    # algorithmic bytes: ids read, sorted_token_ids written up to capacity, expert_ids written
+    # algorithmic bytes: ids read, sorted_token_ids written to capacity, expert_ids written
     nbytes = 4 * S + 4 * C + 4 * (C // B)
     med = t[len(t) // 2]
-    return {"workload": "16384 tokens x top-8 of 256 experts, Zipf(1.1), block_size_m 64",
-            "us_median": round(med, 2), "us_p10": round(t[len(t) // 10], 2),
+    del scrub
+    return {"tokens": T, "cold": cold, "us_median": round(med, 2), "us_p10": round(t[len(t) // 10], 2),
             "us_p90": round(t[9 * len(t) // 10], 2), "num_tokens_post_padded": P,
-            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (med * 1e-6) / 1e9, 1)}
+            "algorithmic_bytes": nbytes, "gbs": round(nbytes / (med * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+ALIGN_SWEEP_T = (64, 1024, 16384, 131072, 1048576)
+
+
+def align_only(dev, iters=200):
+    """Align & Sort on 16384 tokens x top-8 of 256 experts (Zipf 1.1), block 64:
+    warm (ids just written) and cold; plus the token-count sweep (warm)."""
+    warm = align_timed(dev, 16384, iters)
+    cold = align_timed(dev, 16384, iters, cold=True)
+    sweep = [align_timed(dev, T, 50 if T >= 131072 else iters) for T in ALIGN_SWEEP_T]
+    return {"workload": "16384 tokens x top-8 of 256 experts, Zipf(1.1), block_size_m 64",
+            "us_median": warm["us_median"], "us_p10": warm["us_p10"], "us_p90": warm["us_p90"],
+            "num_tokens_post_padded": warm["num_tokens_post_padded"],
+            "algorithmic_bytes": warm["algorithmic_bytes"], "gbs": warm["gbs"],
+            "cold_us_median": cold["us_median"],
+            "sweep": [{k: r[k] for k in ("tokens", "us_median", "gbs", "hbm_frac")} for r in sweep]}
 
 
 def main():

@@ -56,14 +56,17 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
     return v;
 }
-// Inclusive prefix sum across the wave.
+// Inclusive prefix sum across the wave, in DPP moves (no LDS traffic):
+// row_shr 1/2/4/8 scans each 16-lane row (lanes shifted in from outside the
+// row read 0), then row_bcast:15 adds row r's total into row r+1 (rows 1,3)
+// and row_bcast:31 adds lane 31's running total into rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan_i32(int v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int t = __shfl_up(v, o, kWave);
-        if (l >= o) v += t;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
     return v;
 }
 

@@ -23,13 +23,12 @@ hipError_t launch_route_topk(const RouteArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------- align&sort --
 constexpr int kAlignMaxExperts = 1024;
-constexpr int64_t kAlignSingleMaxSlots = 4096;   // one workgroup, one launch, up to here
-constexpr int64_t kAlignSlotsPerWg = 2048;       // target chunk of the multi-block path
-constexpr int kAlignMaxWg = 256;
 
 struct AlignPlan {
-    bool single;
-    int G;
+    bool single;               // one workgroup, one launch
+    bool scan;                 // a scan launch merges the counts (many workgroups)
+    int G;                     // workgroups
+    int R;                     // slots per thread (chunk = 1024 * R)
     int64_t chunk;
     int64_t workspace_bytes;
 };

@@ -78,3 +78,9 @@ def test_align_is_deterministic():
     for _ in range(10):
         again = moe.moe_align_sort(ids, 256, 64)["sorted_token_ids"]
         assert torch.equal(first, again)
+
+
+def test_align_many_experts_large():
+    # 4M slots over 1024 experts: the widest chunk that 1024 experts leave room for
+    rng = np.random.default_rng(11)
+    run_and_compare(rng.integers(0, 1024, size=(524288, 8)).astype(np.int32), 1024, 32, "524288x8/1024")
