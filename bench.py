@@ -251,6 +251,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the align-only and secondary-workload figures")
+    ap.add_argument("--align-only", action="store_true",
+                    help="time Align & Sort alone (16k tokens warm / cold and the token-count sweep), "
+                         "print its JSON and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -277,6 +280,9 @@ def main():
         hip_build.build()
     moe.load_library()
     dev = torch.device("cuda:0")
+    if args.align_only:
+        print(json.dumps(align_only(dev)), flush=True)
+        return
     cfg = ms.CONFIGS[args.workload]
     B = args.B or cfg["B"]
 
@@ -316,12 +322,16 @@ def main():
         line["hbm_probe"] = hbm_probe(dev)
         line["align_sort_16k"] = align_only(dev)
         extra = {}
-        for name in ("prefill_fp8", "decode_bf16"):
+        # the HBM-bound secondary shapes at their own block size; the
+        # compute-bound 512-tokens-per-expert shapes at block 128
+        for name, b2 in (("prefill_fp8", None), ("decode_bf16", None), ("prefill_bf16_512", 128),
+                         ("prefill_fp8_512", 128)):
             if name == args.workload:
                 continue
             c2 = ms.CONFIGS[name]
-            r2 = run_layer_timed(c2, c2["B"], 10, 3, dev)
-            extra[name] = {"workload": describe(name, c2, c2["B"]), **summarize(c2, c2["B"], r2)}
+            b2 = b2 or c2["B"]
+            r2 = run_layer_timed(c2, b2, 10, 3, dev)
+            extra[name] = {"workload": describe(name, c2, b2), **summarize(c2, b2, r2)}
             del r2
             torch.cuda.empty_cache()
         line["other_workloads"] = extra
@@ -532,7 +542,7 @@ def run_cpu_baseline(cfg, B, dev, budget_s=12.0):
                          inter=wdt, w13_scale=s13, w2_scale=s2, E=E_slabs)
         return time.perf_counter() - t1
 
-    n0 = 2
+    n0 = int(min(T, 4 * oracle.num_threads()))   # enough tokens to occupy every oracle thread
     t_probe = ffn(np.sort(order[:n0]))
     n = int(min(T, max(n0, budget_s / max(t_probe / n0, 1e-9))))
     t_ffn = ffn(np.sort(order[:n]))
