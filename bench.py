@@ -320,6 +320,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extras:
         line["hbm_probe"] = hbm_probe(dev)
+        line["mfma_probe"] = mfma_probe(dev)
         line["align_sort_16k"] = align_only(dev)
         extra = {}
         # the HBM-bound secondary shapes at their own block size; the
@@ -409,6 +410,43 @@ def hbm_probe(dev, nbytes=4 << 30, reps=10):
     ev.close()
     del buf
     torch.cuda.empty_cache()
+    return res
+
+
+def mfma_probe(dev, reps=5):
+    """Matrix-core throughput a kernel with no memory traffic reaches: 8
+    independent MFMA chains per wave, two waves per SIMD, bf16 and fp8,
+    event-timed, best of `reps` (the practical ceiling under sustained load)."""
+    import ctypes
+
+    import torch
+
+    import routing_align_sort_amd as moe
+    from routing_align_sort_amd import build as hip_build
+    if not os.path.exists(hip_build.PROBE_LIB):
+        hip_build.build_probe()
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    blocks, iters = 256 * 2 * 4, 2000
+    out = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ev = moe.HipEvents(2 * reps)
+    res = {}
+    for name, fp8, k in (("bf16", 0, 16), ("fp8", 1, 64)):
+        flops = blocks * 4 * iters * 8 * 2 * 32 * 32 * k
+        lib.moe_probe_mfma(fp8, ctypes.c_void_p(out.data_ptr()), blocks, iters, stream)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            ev.record(2 * i)
+            if lib.moe_probe_mfma(fp8, ctypes.c_void_p(out.data_ptr()), blocks, iters, stream) != 0:
+                raise RuntimeError("probe launch failed")
+            ev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        best = min(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)) * 1e-3
+        tf = flops / best / 1e12
+        res[name + "_tflops"] = round(tf, 1)
+        res[name + "_frac_of_peak"] = round(tf / MFMA_PEAK_TFLOPS["bf16" if name == "bf16" else "e4m3"], 4)
+    ev.close()
     return res
 
 

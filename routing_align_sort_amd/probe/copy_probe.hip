@@ -46,3 +46,47 @@ extern "C" int moe_probe_read(const void* src, void* out, size_t bytes, void* st
                        (const uint4*)src, (uint32_t*)out, n);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
+
+// Matrix-core throughput with no memory traffic: every wave runs `iters`
+// rounds of 8 independent 32x32 MFMA accumulation chains (bf16 32x32x16, or
+// fp8 32x32x64 with unit scales) on register operands, then folds the
+// accumulators into one word per wave so the work cannot be dropped.
+template <bool kFp8>
+__global__ void __launch_bounds__(256) mfma_probe_kernel(float* __restrict__ out, int iters) {
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    f32x16 acc[8];
+    for (int c = 0; c < 8; ++c)
+        for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
+    const int lane = threadIdx.x & 63;
+    if constexpr (kFp8) {
+        i32x8 a, b;
+        for (int i = 0; i < 8; ++i) { a[i] = 0x38383838 ^ (lane + i); b[i] = 0x30303030 ^ (lane * 3 + i); }
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 0, 0, 0, 127, 0, 127);
+    } else {
+        bf16x8 a, b;
+        for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(0.001f * (lane + i)); b[i] = (__bf16)(0.002f * (lane - i)); }
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.f;
+    for (int c = 0; c < 8; ++c)
+        for (int i = 0; i < 16; ++i) s += acc[c][i];
+    if (lane == 0) out[blockIdx.x * 4 + threadIdx.x / 64] = s;
+}
+
+// FLOPs per launch = blocks * 4 waves * iters * 8 * (2*32*32*K), K = 16 (bf16) or 64 (fp8).
+extern "C" int moe_probe_mfma(int fp8, float* out, int blocks, int iters, void* stream) {
+    if (!out || blocks <= 0 || iters <= 0) return 1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (fp8)
+        hipLaunchKernelGGL(mfma_probe_kernel<true>, dim3(blocks), dim3(256), 0, s, out, iters);
+    else
+        hipLaunchKernelGGL(mfma_probe_kernel<false>, dim3(blocks), dim3(256), 0, s, out, iters);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
