@@ -87,12 +87,33 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
                          x_dtype=L["x"].dtype,
                          out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16)
     x, logits, bias = L["x"], L["logits"], L["bias"]
-    NE = 9
-    ev = moe.HipEvents(NE * max(steps, 1))
     for _ in range(warmup):
         layer.forward(x, logits, bias)
     torch.cuda.synchronize()
+    # 1. the layer as a caller runs it: the four calls back to back, nothing
+    #    else on the stream; wall clock between device synchronisations
     t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, logits, bias)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # 2. the same four calls captured once in a HIP graph and replayed
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, logits, bias)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    wall_graph = time.perf_counter() - t0
+    del g
+    # 3. per-stage durations: events around every kernel (each event adds a
+    #    few us of stream time, so these steps are not the wall-clock figure)
+    NE = 9
+    ev = moe.HipEvents(NE * max(steps, 1))
+    torch.cuda.synchronize()
     for s in range(steps):
         b = NE * s
         ev.record(b + 0)
@@ -104,7 +125,6 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
         layer.combine()
         ev.record(b + 8)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     names = ["route", "align", None, "quant", "gate_up", "requant", "down", "combine"]
     per = {n: [] for n in names if n}
     total = []
@@ -118,6 +138,7 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
     ids_np = layer.topk_ids.cpu().numpy()
     res = {
         "wall_s": wall,
+        "wall_graph_s": wall_graph,
         "us": {n: _mean(v) for n, v in per.items()},
         "us_step_events": _mean(total),
         "P": int(layer.ntpp.item()),
@@ -126,6 +147,7 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
         "E_slabs": layer.E_slabs,
         "L": L,
         "layer": layer,
+        "steps": steps,
     }
     return res
 
@@ -136,10 +158,13 @@ def summarize(cfg, B, r):
     flops = layer_flops(ab["slots"], cfg["H"], cfg["I"])
     gemm_us = us["gate_up"] + us["down"]
     dt = cfg["dtype"]
+    steps = r["steps"]
     return {
         "block_size_m": B,
-        "tokens_per_s": cfg["T"] / (r["us_step_events"] * 1e-6),
-        "us_per_step": r["us_step_events"],
+        "tokens_per_s": cfg["T"] * steps / r["wall_s"],
+        "us_per_step": r["wall_s"] / steps * 1e6,
+        "graph_us_per_step": r["wall_graph_s"] / steps * 1e6,
+        "event_timed_us_per_step": r["us_step_events"],
         "us": {k: round(v, 2) for k, v in us.items()},
         "experts_hit": ab["experts_hit"],
         "num_tokens_post_padded": r["P"],
@@ -148,7 +173,7 @@ def summarize(cfg, B, r):
         "gate_up_hbm_gbs": ab["stage1"] / (us["gate_up"] * 1e-6) / 1e9,
         "down_hbm_gbs": ab["stage2"] / (us["down"] * 1e-6) / 1e9,
         "weights_gb": ab["weights"] / 1e9,
-        "layer_weight_stream_frac": ab["weights"] / (r["us_step_events"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "layer_weight_stream_frac": ab["weights"] / (r["wall_s"] / steps) / 1e9 / HBM_PEAK_GBS,
     }
 
 
@@ -336,6 +361,19 @@ def main():
             del r2
             torch.cuda.empty_cache()
         line["other_workloads"] = extra
+        # the headline workload at the other block sizes the pages tune over
+        sweep = {}
+        for b2 in (32, 64, 128):
+            if b2 == B:
+                sm = line["layer"]
+            else:
+                r2 = run_layer_timed(cfg, b2, 10, 3, dev)
+                sm = summarize(cfg, b2, r2)
+                del r2
+                torch.cuda.empty_cache()
+            sweep[str(b2)] = {"us_per_step": round(sm["us_per_step"], 1), "gate_up_us": sm["us"]["gate_up"],
+                              "down_us": sm["us"]["down"], "grouped_gemm_tflops": round(sm["grouped_gemm_tflops"], 1)}
+        line["block_size_sweep"] = sweep
     if args.copy_probe:
         copy_probe(dev)
     if not args.no_cpu_baseline:
