@@ -623,8 +623,16 @@ def run_cpu_baseline(cfg, B, dev, budget_s=12.0):
     n = int(min(T, max(n0, budget_s / max(t_probe / n0, 1e-9))))
     t_ffn = ffn(np.sort(order[:n]))
     per_token = t_ra / T + t_ffn / n
+    # the Align & Sort oracle alone (serial C, one core) on the 16384 x top-8 workload
+    a16 = ms.CONFIGS["align_16k"]
+    ids16 = ms.zipf_topk_ids(0, ms.TAG_IDS, a16["T"], a16["K"], a16["E"], a16["zipf_s"])
+    t1 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        oracle.align_sort(ids16, a16["E"], a16["B"])
+    align_ms = (time.perf_counter() - t1) / reps * 1e3
     return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "align_sort_16k_single_core_ms": round(align_ms, 3),
             "sample": f"routing + Align & Sort over all {T} tokens ({t_ra:.3f} s), expert FFN + "
                       f"combine for {n} seeded tokens ({t_ffn:.2f} s), double precision; "
                       f"tokens/s extrapolated per token"}
