@@ -228,6 +228,13 @@ CONFIGS = {
     "prefill_fp8_512": dict(T=2048, H=7168, I=2048, E=32, K=8, dtype="e4m3", score="softmax",
                             bias=False, n_group=1, topk_group=1, renormalize=True,
                             routing="uniform8", shared=True, B=128),
+    # MXFP4 expert weights (E2M1 codes + E8M0 scales per 32 elements; fp8
+    # per-token activations): the decode shape and the one-GPU prefill share.
+    "decode_fp4": dict(T=64, H=7168, I=2048, E=256, K=8, dtype="e2m1", score="sigmoid", bias=True,
+                       n_group=8, topk_group=4, renormalize=True, routing="router", B=16),
+    "prefill_fp4": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e2m1", score="softmax",
+                        bias=False, n_group=1, topk_group=1, renormalize=False,
+                        routing="uniform", B=64),
 }
 
 ROUTER_SIGMA = 0.02
@@ -301,6 +308,19 @@ def make_weights(cfg, device="cpu", seed=0, experts=None):
     Ew = E + (1 if cfg.get("shared") else 0)
     sel = list(range(Ew)) if experts is None else list(experts)
     dt = cfg["dtype"]
+    if dt == "e2m1":
+        # MXFP4: bytes of two E2M1 codes along the row + one E8M0 scale per 32
+        w13 = torch.empty((len(sel), 2 * I, H // 2), dtype=torch.uint8, device=device)
+        w2 = torch.empty((len(sel), H, I // 2), dtype=torch.uint8, device=device)
+        res = {"w13": w13, "w2": w2,
+               "w13_scale": torch.empty((len(sel), 2 * I, H // 32), dtype=torch.uint8, device=device),
+               "w2_scale": torch.empty((len(sel), H, I // 32), dtype=torch.uint8, device=device)}
+        for n, e in enumerate(sel):
+            for tag, shape, dst, sc in ((TAG_W13, (2 * I, H), w13, "w13_scale"), (TAG_W2, (H, I), w2, "w2_scale")):
+                q, s = quantise_rows_mxfp4_input(normal_slab(seed, tag, e, shape, WEIGHT_SIGMA, device))
+                dst[n].copy_(q)
+                res[sc][n].copy_(s)
+        return res
     wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}[dt]
     w13 = torch.empty((len(sel), 2 * I, H), dtype=wdt, device=device)
     w2 = torch.empty((len(sel), H, I), dtype=wdt, device=device)
@@ -336,6 +356,38 @@ def _quantise_rows_e4m3_input(w: torch.Tensor):
     inv = c448 / amax
     q = (w * inv[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
     return q, amax / c448
+
+
+# E2M1 magnitude grid (in units of the block scale) and the midpoints between
+# neighbours; a midpoint rounds to the neighbour with the even code (mantissa
+# bit 0), i.e. up exactly at the odd-indexed midpoints 0.75, 1.75 and 3.5.
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def quantise_rows_mxfp4_input(w: torch.Tensor):
+    """Input preparation for the MXFP4 workloads' weights (the library receives
+    them in this form): per block of 32 consecutive elements of a row, the
+    shared exponent is floor(log2(amax)) - 2 (2 = the largest E2M1 exponent),
+    stored as the E8M0 byte exponent + 127 (127 when the block is all zero);
+    each element is w / 2^exponent rounded to the nearest E2M1 value (ties to
+    the even code) and saturated at 6.  Codes are packed two per byte, the
+    even column in the low nibble.  Every step is exact, so host and device
+    give the same bytes."""
+    R, K = w.shape
+    blk = w.reshape(R, K // 32, 32)
+    amax = blk.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
+    se = torch.where(amax > 0, ex - 3, torch.zeros_like(ex)).clamp(-127, 127)
+    v = torch.ldexp(blk.abs(), (-se)[:, :, None].to(torch.int32))
+    code = torch.zeros_like(v, dtype=torch.int32)
+    for i, m in enumerate(_E2M1_MIDS):
+        code += (v > m).to(torch.int32)
+        if i % 2 == 1:
+            code += (v == m).to(torch.int32)
+    sign = ((blk < 0) & (code > 0)).to(torch.int32)
+    nib = (code | (sign << 3)).reshape(R, K)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).to(torch.uint8)
+    return packed, (se + 127).to(torch.uint8)
 
 
 def scaled(cfg_name, **over):

@@ -25,7 +25,7 @@ _lib = None
 
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
-W_F32, W_BF16, W_E4M3 = 0, 1, 2
+W_F32, W_BF16, W_E4M3, W_MXFP4 = 0, 1, 2, 3
 X_F32, X_BF16 = 0, 1
 INTER_F64, INTER_F32, INTER_BF16, INTER_E4M3 = 0, 1, 2, 3
 
@@ -57,8 +57,11 @@ def _load():
     lib.oracle_bf16_decode_array.argtypes = [P, i64, P]
     lib.oracle_e4m3_encode_array.argtypes = [P, i64, P]
     lib.oracle_e4m3_decode_array.argtypes = [P, i64, P]
+    lib.oracle_e2m1_decode_array.argtypes = [P, i64, P]
+    lib.oracle_e8m0_decode_array.argtypes = [P, i64, P]
     for f in (lib.oracle_bf16_encode_array, lib.oracle_bf16_decode_array,
-              lib.oracle_e4m3_encode_array, lib.oracle_e4m3_decode_array):
+              lib.oracle_e4m3_encode_array, lib.oracle_e4m3_decode_array,
+              lib.oracle_e2m1_decode_array, lib.oracle_e8m0_decode_array):
         f.restype = None
     lib.oracle_route_topk.argtypes = [i32, i32, i32, i32, i32, i32, i32, f64, i32, P, P, P, P]
     lib.oracle_route_topk.restype = i32
@@ -121,6 +124,22 @@ def e4m3_decode(c) -> np.ndarray:
     c = _c(c, np.uint8)
     out = np.empty(c.shape, np.float64)
     _load().oracle_e4m3_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e2m1_decode(nibbles) -> np.ndarray:
+    """OCP MX FP4 (E2M1) element codes (one per uint8, low 4 bits) -> values."""
+    c = _c(nibbles, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e2m1_decode_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e8m0_decode(e) -> np.ndarray:
+    """E8M0 block scales (uint8) -> 2^(e-127) (NaN for 255)."""
+    c = _c(e, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e8m0_decode_array(_ptr(c), c.size, _ptr(out))
     return out
 
 
@@ -195,7 +214,8 @@ def quant_row_e4m3(v):
 
 
 # ------------------------------------------------------------ FFN, combine ----
-_WDT = {"f32": (W_F32, np.float32), "bf16": (W_BF16, np.uint16), "e4m3": (W_E4M3, np.uint8)}
+_WDT = {"f32": (W_F32, np.float32), "bf16": (W_BF16, np.uint16), "e4m3": (W_E4M3, np.uint8),
+        "e2m1": (W_MXFP4, np.uint8)}
 _XDT = {"f32": (X_F32, np.float32), "bf16": (X_BF16, np.uint16)}
 _INTER = {"f64": INTER_F64, "f32": INTER_F32, "bf16": INTER_BF16, "e4m3": INTER_E4M3}
 
@@ -204,8 +224,10 @@ def expert_ffn(x, w13, w2, topk_ids, *, w_dtype, x_dtype, inter, w13_scale=None,
     """y_slots[t*K+k] = FFN_{ids[t,k]}(x[t]) as float32 [T*K, H].
 
     x: [T,H] fp32 or bf16 bit patterns; w13 [E,2I,H], w2 [E,H,I] in fp32, bf16 bits
-    or E4M3 codes (with w13_scale [E,2I], w2_scale [E,H]).  Slots with ids out of
-    range are left at zero.
+    or E4M3 codes (with fp32 w13_scale [E,2I], w2_scale [E,H]); for "e2m1"
+    (MXFP4) w13 [E,2I,H/2], w2 [E,H,I/2] bytes of two codes each, with E8M0
+    block scales w13_scale [E,2I,H/32], w2_scale [E,H,I/32] (uint8).  Slots
+    with ids out of range are left at zero.
     """
     wcode, wnp = _WDT[w_dtype]
     xcode, xnp = _XDT[x_dtype]
@@ -217,9 +239,16 @@ def expert_ffn(x, w13, w2, topk_ids, *, w_dtype, x_dtype, inter, w13_scale=None,
     K = ids.shape[1]
     E, I2, H2 = w13.shape
     I = I2 // 2
-    assert H2 == H and w2.shape == (E, H, I) and ids.shape[0] == T
-    s13 = None if w13_scale is None else _c(w13_scale, np.float32)
-    s2 = None if w2_scale is None else _c(w2_scale, np.float32)
+    fp4 = w_dtype == "e2m1"
+    if fp4:
+        assert H2 * 2 == H and w2.shape == (E, H, I // 2) and ids.shape[0] == T
+    else:
+        assert H2 == H and w2.shape == (E, H, I) and ids.shape[0] == T
+    snp = np.uint8 if fp4 else np.float32
+    s13 = None if w13_scale is None else _c(w13_scale, snp)
+    s2 = None if w2_scale is None else _c(w2_scale, snp)
+    if fp4 and s13 is not None:
+        assert s13.shape == (E, 2 * I, H // 32) and s2.shape == (E, H, I // 32)
     y = np.zeros((T * K, H), np.float32)
     rc = _load().oracle_expert_ffn(T, K, E, H, I, wcode, xcode, _INTER[inter], _ptr(x), _ptr(w13),
                                    _ptr(s13), _ptr(w2), _ptr(s2), _ptr(ids), _ptr(y))

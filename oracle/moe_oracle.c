@@ -106,6 +106,25 @@ uint8_t oracle_e4m3_encode(float v)
 }
 
 /* Array forms of the codecs, for the test suite. */
+/* OCP microscaling FP4, E2M1 element: 1 sign bit, 2 exponent bits (bias 1),
+ * 1 mantissa bit, no infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ * E8M0 block scale: the power of two 2^(e-127), e = 255 is NaN.  A block of 32
+ * consecutive elements of a row shares one scale.  The GC-MoE abstract
+ * (zhuanzhiai.com) names FP4 expert weights. */
+double oracle_e2m1_decode(uint8_t nib)
+{
+    int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+double oracle_e8m0_decode(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+void oracle_e2m1_decode_array(const uint8_t *nib, int64_t n, double *out)
+{ for (int64_t i = 0; i < n; i++) out[i] = oracle_e2m1_decode(nib[i]); }
+void oracle_e8m0_decode_array(const uint8_t *e, int64_t n, double *out)
+{ for (int64_t i = 0; i < n; i++) out[i] = oracle_e8m0_decode(e[i]); }
+
 void oracle_bf16_encode_array(const float *v, int64_t n, uint16_t *out)
 { for (int64_t i = 0; i < n; i++) out[i] = oracle_bf16_encode(v[i]); }
 void oracle_bf16_decode_array(const uint16_t *b, int64_t n, double *out)
@@ -334,34 +353,59 @@ void oracle_quant_tokens_e4m3(const uint16_t *x_bf16, int T, int H, uint8_t *q, 
  *
  * Layouts: x [T,H]; w13 [E,2I,H] with rows [0,I) the gate and [I,2I) the up
  * projection; w2 [E,H,I].  w_dtype: 0 fp32, 1 bf16 bits, 2 E4M3 codes with
- * one fp32 scale per output row (w13_scale [E,2I], w2_scale [E,H]).
- * For w_dtype 2 the activations are the bf16 x quantised per token (above),
- * and the dot products are formed on the decoded codes (exact in double) and
- * then multiplied by the two scales.
+ * one fp32 scale per output row (w13_scale [E,2I], w2_scale [E,H]), 3 MXFP4:
+ * E2M1 codes two per byte (w13 [E,2I,H/2], w2 [E,H,I/2] bytes) with one E8M0
+ * scale per 32 elements of a row (w13_scale [E,2I,H/32], w2_scale [E,H,I/32]
+ * bytes).
+ * For w_dtype 2 and 3 the activations are the bf16 x quantised per token
+ * (above), and the dot products are formed on the decoded values (exact in
+ * double; for MXFP4 each weight already carries its block scale) and then
+ * multiplied by the token's scale and, for E4M3 weights, the row's scale.
  * inter: 0 keep double (no rounding, used by the oracle's own checks),
  *        1 round to fp32, 2 round to fp32 then to bf16,
  *        3 round to fp32 then requantise the row to E4M3 with a per-row scale
  *          (same rule as the activation quantisation).
  */
-static double load_w(int w_dtype, const void *w, size_t idx)
+static double e2m1_table[16], e8m0_table[256];
+
+static void mx_tables(void)
 {
+    for (int i = 0; i < 16; i++) e2m1_table[i] = oracle_e2m1_decode((uint8_t)i);
+    for (int i = 0; i < 256; i++) e8m0_table[i] = oracle_e8m0_decode((uint8_t)i);
+}
+
+/* Element (row, col) of a weight matrix whose rows have `len` elements.
+ * w_dtype 3 (MXFP4): two codes per byte along the row, the even column in the
+ * low nibble; the scale of columns [32b, 32b+32) of a row is byte b of that
+ * row's scale array (len/32 bytes per row); the value includes it. */
+static double load_w(int w_dtype, const void *w, const void *wscale, size_t row, int col, int len)
+{
+    size_t idx = row * (size_t)len + (size_t)col;
     if (w_dtype == 0) return (double)((const float *)w)[idx];
     if (w_dtype == 1) return oracle_bf16_decode(((const uint16_t *)w)[idx]);
-    return oracle_e4m3_decode(((const uint8_t *)w)[idx]);
+    if (w_dtype == 2) return oracle_e4m3_decode(((const uint8_t *)w)[idx]);
+    uint8_t b = ((const uint8_t *)w)[idx / 2];
+    uint8_t nib = (col & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+    uint8_t sc = ((const uint8_t *)wscale)[row * (size_t)(len / 32) + (size_t)(col / 32)];
+    return e2m1_table[nib] * e8m0_table[sc];
 }
 
 int oracle_expert_ffn(int T, int K, int E, int H, int I, int w_dtype, int x_dtype, int inter,
-                      const void *x, const void *w13, const float *w13_scale,
-                      const void *w2, const float *w2_scale,
+                      const void *x, const void *w13, const void *w13_scale,
+                      const void *w2, const void *w2_scale,
                       const int32_t *topk_ids, float *y_slots)
 {
     if (T < 0 || K < 1 || E < 1 || H < 1 || I < 1) return 1;
-    if (w_dtype == 2 && x_dtype != 1) return 1;
-    if (w_dtype == 2 && (!w13_scale || !w2_scale)) return 1;
+    if (w_dtype < 0 || w_dtype > 3) return 1;
+    if (w_dtype >= 2 && x_dtype != 1) return 1;
+    if (w_dtype >= 2 && (!w13_scale || !w2_scale)) return 1;
+    if (w_dtype == 3 && (H % 32 || I % 32)) return 1;
+    mx_tables();
+    const float *s13 = (const float *)w13_scale, *s2 = (const float *)w2_scale;
     int64_t S = (int64_t)T * K;
     uint8_t *xq = NULL;
     float *sx = NULL;
-    if (w_dtype == 2) {
+    if (w_dtype >= 2) {
         xq = (uint8_t *)malloc((size_t)T * H);
         sx = (float *)malloc(sizeof(float) * (size_t)T);
         oracle_quant_tokens_e4m3((const uint16_t *)x, T, H, xq, sx);
@@ -382,22 +426,25 @@ int oracle_expert_ffn(int T, int K, int E, int H, int I, int w_dtype, int x_dtyp
             /* the token's activations */
             for (int h = 0; h < H; h++) {
                 size_t xi = (size_t)t * H + h;
-                if (w_dtype == 2) xt[h] = oracle_e4m3_decode(xq[xi]);
+                if (w_dtype >= 2) xt[h] = oracle_e4m3_decode(xq[xi]);
                 else if (x_dtype == 0) xt[h] = (double)((const float *)x)[xi];
                 else xt[h] = oracle_bf16_decode(((const uint16_t *)x)[xi]);
             }
             /* gate and up projections, SiLU(gate) * up */
             for (int j = 0; j < I; j++) {
-                size_t rg = ((size_t)e * 2 * I + j) * H;
-                size_t ru = ((size_t)e * 2 * I + I + j) * H;
+                size_t rg = (size_t)e * 2 * I + j;          /* rows of W13 */
+                size_t ru = (size_t)e * 2 * I + I + j;
                 double g = 0.0, u = 0.0;
                 for (int h = 0; h < H; h++) {
-                    g += xt[h] * load_w(w_dtype, w13, rg + h);
-                    u += xt[h] * load_w(w_dtype, w13, ru + h);
+                    g += xt[h] * load_w(w_dtype, w13, w13_scale, rg, h, H);
+                    u += xt[h] * load_w(w_dtype, w13, w13_scale, ru, h, H);
                 }
                 if (w_dtype == 2) {
-                    g = g * (double)sx[t] * (double)w13_scale[(size_t)e * 2 * I + j];
-                    u = u * (double)sx[t] * (double)w13_scale[(size_t)e * 2 * I + I + j];
+                    g = g * (double)sx[t] * (double)s13[rg];
+                    u = u * (double)sx[t] * (double)s13[ru];
+                } else if (w_dtype == 3) {                 /* block scales are in the values */
+                    g = g * (double)sx[t];
+                    u = u * (double)sx[t];
                 }
                 a[j] = g / (1.0 + exp(-g)) * u;
             }
@@ -416,10 +463,10 @@ int oracle_expert_ffn(int T, int K, int E, int H, int I, int w_dtype, int x_dtyp
             }
             /* down projection */
             for (int h = 0; h < H; h++) {
-                size_t rd = ((size_t)e * H + h) * I;
+                size_t rd = (size_t)e * H + h;              /* row of W2 */
                 double y = 0.0;
-                for (int j = 0; j < I; j++) y += a[j] * load_w(w_dtype, w2, rd + j);
-                if (w_dtype == 2) y = y * sa * (double)w2_scale[(size_t)e * H + h];
+                for (int j = 0; j < I; j++) y += a[j] * load_w(w_dtype, w2, w2_scale, rd, j, I);
+                if (w_dtype == 2) y = y * sa * (double)s2[rd];
                 else if (inter == 3) y = y * sa;
                 y_slots[i * H + h] = (float)y;
             }

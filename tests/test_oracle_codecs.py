@@ -102,3 +102,22 @@ def test_e4m3_saturates():
     got = oracle.e4m3_encode(v)
     assert list(got) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
     assert oracle.e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+# OCP Microscaling Formats (MX) v1.0, FP4 E2M1 element values by code (sign
+# bit 3): the eight non-negative magnitudes of the format.
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_matches_the_format_table():
+    got = oracle.e2m1_decode(np.arange(16, dtype=np.uint8))
+    want = np.array(E2M1_MAGNITUDES + [-m for m in E2M1_MAGNITUDES])
+    assert np.array_equal(got, want)
+    assert np.signbit(got[8]) and not np.signbit(got[0])      # code 8 is -0
+
+
+def test_e8m0_decode_is_a_power_of_two():
+    e = np.arange(256, dtype=np.uint8)
+    got = oracle.e8m0_decode(e)
+    assert np.array_equal(got[:255], np.ldexp(1.0, e[:255].astype(np.int64) - 127))
+    assert np.isnan(got[255])

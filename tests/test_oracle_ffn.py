@@ -194,3 +194,54 @@ def test_fp8_layer_against_dense_with_library_casts():
     exact = dense_layer(xd.astype(np.float64), w13.astype(np.float64), w2.astype(np.float64),
                         ids, w, E)
     assert np.max(np.abs(out - exact)) / np.max(np.abs(exact)) < 0.15
+
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def mxfp4_random(rng, rows, cols):
+    """Random MXFP4 operands and their exact float values, built independently
+    of the oracle: nibbles, one E8M0 byte per 32 elements of a row, the even
+    column in the low nibble."""
+    nib = rng.integers(0, 16, (rows, cols)).astype(np.uint8)
+    sc = rng.integers(120, 125, (rows, cols // 32)).astype(np.uint8)
+    vals = E2M1[nib] * np.ldexp(1.0, np.repeat(sc.astype(np.int64) - 127, 32, axis=1))
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sc, vals
+
+
+def test_mxfp4_layer_against_dense_with_float_weights():
+    rng = np.random.default_rng(7)
+    T, H, I, E, K = 10, 64, 96, 3, 2
+    x = rng.normal(0, 1, (T, H)).astype(np.float32)
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.1, 1.0, (T, K)).astype(np.float32)
+    parts13 = [mxfp4_random(rng, 2 * I, H) for _ in range(E)]
+    parts2 = [mxfp4_random(rng, H, I) for _ in range(E)]
+    w13q = np.stack([p[0] for p in parts13]); s13 = np.stack([p[1] for p in parts13])
+    w2q = np.stack([p[0] for p in parts2]); s2 = np.stack([p[1] for p in parts2])
+    w13d = np.stack([p[2] for p in parts13]); w2d = np.stack([p[2] for p in parts2])
+    xb = oracle.bf16_encode(x)
+    out, _ = oracle.moe_layer(xb, w13q, w2q, ids, w, w_dtype="e2m1", x_dtype="bf16", inter="e4m3",
+                              w13_scale=s13, w2_scale=s2)
+    xd = oracle.bf16_decode(xb).astype(np.float32)
+    amax = np.abs(xd).max(1)
+    sx = (amax / np.float32(448)).astype(np.float32)
+    xq = np.stack([_torch_e4m3(xd[t] * (np.float32(448) / amax[t])) for t in range(T)]) * sx[:, None]
+
+    def requant(a):
+        a32 = a.astype(np.float32)
+        am = np.abs(a32).max(1)
+        sa = (am / np.float32(448)).astype(np.float64)
+        return np.stack([_torch_e4m3(a32[t] * (np.float32(448) / am[t])) for t in range(len(a))]) \
+            * sa[:, None]
+    ref = dense_layer(xq, w13d, w2d, ids, w, E, round_a=requant)
+    err = np.max(np.abs(out - ref)) / np.max(np.abs(ref))
+    assert err < 1e-5, err
+    # a wrong nibble order or block index would change the values: swap the
+    # nibbles of one expert's gate rows and the result must move
+    w13s = w13q.copy()
+    w13s[0] = (w13s[0] >> 4) | ((w13s[0] & 15) << 4)
+    out_s, _ = oracle.moe_layer(xb, w13s, w2q, ids, w, w_dtype="e2m1", x_dtype="bf16", inter="e4m3",
+                                w13_scale=s13, w2_scale=s2)
+    assert np.max(np.abs(out_s - out)) > 1e-3 * np.max(np.abs(out))
