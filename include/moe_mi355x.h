@@ -53,7 +53,7 @@ typedef enum {
     MOE_ERR_HIP = 4            /* a HIP launch failed (no device, bad pointer)  */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_FP4_E2M1 = 3 } moe_dtype_t;
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_t;
 
 int32_t moe_abi_version(void);
@@ -161,15 +161,28 @@ moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32
  *     per output row (w13_scale [E,2I], w2_scale [E,H]); products accumulate
  *     in fp32 and are scaled by the two scales; a is requantised per row the
  *     same way before the down projection.
+ *   w_dtype = MOE_FP4_E2M1, x_dtype = MOE_BF16 (a8w4, OCP microscaling FP4
+ *     weights; the GC-MoE abstract names FP4 expert weights with block-scaled
+ *     products): activations and a are quantised exactly as in a8w8; weights
+ *     are E2M1 codes, two per byte with the even column in the low nibble
+ *     (w13 [E,2I,H/2] and w2 [E,H,I/2] bytes), and every 32 consecutive
+ *     elements of a row share one E8M0 scale byte 2^(s-127) (w13_scale
+ *     [E,2I,H/32], w2_scale [E,H,I/32] bytes); products accumulate in fp32
+ *     and are scaled by the token's (or a's row's) scale only.
  * x device [T,H] (fp32 or bf16); w13 device [E,2I,H]; w2 device [E,H,I];
  * sorted_token_ids / expert_ids / num_tokens_post_padded as produced by
  * moe_align_sort with the same T,K,E,B; y_slots device fp32 [T*K,H] (out);
  * workspace device, at least moe_grouped_ffn_workspace_bytes(p), 256-byte
  * aligned, clobbered.
  * weight_layout MOE_LAYOUT_PACKED means w13 and w2 were rewritten by
- * moe_prepack_weights (below); the scales stay in their canonical layout.
+ * moe_prepack_weights (below); fp32 scales of E4M3 weights stay canonical,
+ * E8M0 block scales of E2M1 weights must then be rewritten by
+ * moe_prepack_block_scales.
  * Limits: B in {16,32,64,128,256}; H a multiple of 256 and I a multiple of 128
- * (fp32: multiples of 64, canonical layout only); E <= 1024.
+ * (fp32: multiples of 64, canonical layout only); E <= 1024; except for fp32,
+ * T*H and C*I (C = moe_align_sort_capacity) times the activation element size
+ * (2 for bf16, 1 for the quantised paths) at most 4 GiB.  Beyond any limit:
+ * MOE_ERR_UNSUPPORTED.
  */
 typedef enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layout_t;
 
@@ -182,14 +195,15 @@ typedef struct {
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);
 moe_status_t moe_grouped_ffn(const moe_ffn_params_t *p, const void *x, const void *w13,
-                             const float *w13_scale, const void *w2, const float *w2_scale,
+                             const void *w13_scale, const void *w2, const void *w2_scale,
                              const int32_t *sorted_token_ids, const int32_t *expert_ids,
                              const int32_t *num_tokens_post_padded, float *y_slots,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One-time weight preparation, off the per-token path: rewrites canonical
- * w13 [E,2I,H] and w2 [E,H,I] (bf16 or E4M3, per p->w_dtype; uses p->E, H, I)
+ * w13 [E,2I,H] and w2 [E,H,I] (bf16, E4M3 or packed E2M1 pairs, per p->w_dtype;
+ * uses p->E, H, I)
  * into the packed layout (same byte sizes) that moe_grouped_ffn streams with
  * one contiguous 1 KB read per load instruction.  The packed layout is a
  * permutation of the bytes, private to this library: produce it only with
@@ -197,6 +211,17 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t *p, const void *x, const voi
  */
 moe_status_t moe_prepack_weights(const moe_ffn_params_t *p, const void *w13, const void *w2,
                                  void *w13_packed, void *w2_packed, void *stream);
+
+/*
+ * The companion of moe_prepack_weights for E2M1 weights (p->w_dtype ==
+ * MOE_FP4_E2M1, else MOE_ERR_UNSUPPORTED): rewrites the E8M0 block scales
+ * w13_scale [E,2I,H/32] and w2_scale [E,H,I/32] (device bytes) into the
+ * packed order that moe_grouped_ffn reads beside packed weights (same byte
+ * sizes, private to this library).  Outputs must not alias the inputs.
+ */
+moe_status_t moe_prepack_block_scales(const moe_ffn_params_t *p, const void *w13_scale,
+                                      const void *w2_scale, void *w13_scale_packed,
+                                      void *w2_scale_packed, void *stream);
 
 /*
  * Profiling form of moe_grouped_ffn: the same work and results, plus five
@@ -209,7 +234,7 @@ moe_status_t moe_prepack_weights(const moe_ffn_params_t *p, const void *w13, con
  * A NULL array or handle is MOE_ERR_INVALID_ARG.
  */
 moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t *p, const void *x, const void *w13,
-                                      const float *w13_scale, const void *w2, const float *w2_scale,
+                                      const void *w13_scale, const void *w2, const void *w2_scale,
                                       const int32_t *sorted_token_ids, const int32_t *expert_ids,
                                       const int32_t *num_tokens_post_padded, float *y_slots,
                                       void *workspace, size_t workspace_bytes, void *stream,

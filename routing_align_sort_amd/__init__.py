@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1 = 0, 1, 2, 3
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 
 _lib = None
@@ -45,7 +45,8 @@ class _FfnParams(ctypes.Structure):
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
-            "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_prepack_weights", "moe_combine")
+            "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_prepack_weights",
+            "moe_prepack_block_scales", "moe_combine")
 
 
 def load_library(path: str = LIB_PATH):
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_grouped_ffn_profiled.restype = i32
     lib.moe_prepack_weights.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P]
     lib.moe_prepack_weights.restype = i32
+    lib.moe_prepack_block_scales.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P]
+    lib.moe_prepack_block_scales.restype = i32
     lib.moe_combine.argtypes = [i32, i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_combine.restype = i32
     _lib = lib
@@ -187,7 +190,19 @@ def moe_align_sort(topk_ids, E, B, *, sorted_token_ids=None, expert_ids=None,
 
 
 # -------------------------------------------------------------- grouped FFN --
-_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3}
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.float8_e4m3fn: MOE_FP8_E4M3,
+       torch.float4_e2m1fn_x2: MOE_FP4_E2M1}
+# MXFP4 weights are float4_e2m1fn_x2 tensors (one element = two E2M1 codes,
+# the even column in the low nibble) with float8_e8m0fnu block scales, one per
+# 32 elements of a row.
+FP4 = torch.float4_e2m1fn_x2
+E8M0 = torch.float8_e8m0fnu
+
+
+def weight_dims(w13):
+    """(E, I, H) of a gate/up weight tensor [E, 2I, H] (MXFP4: [E, 2I, H/2])."""
+    E, I2, Hc = w13.shape
+    return E, I2 // 2, Hc * (2 if w13.dtype == FP4 else 1)
 
 
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PACKED = 0, 1
@@ -202,14 +217,29 @@ def moe_prepack_weights(w13, w2, *, stream=None):
     """One-time rewrite of canonical expert weights into the packed streaming
     layout; returns (w13_packed, w2_packed), same shapes and dtype (opaque)."""
     lib = load_library()
-    E, I2, H = w13.shape
+    E, I, H = weight_dims(w13)
     _need(w13, w13.dtype, "w13")
-    _need(w2, w13.dtype, "w2", E * H * (I2 // 2))
+    _need(w2, w13.dtype, "w2", w13.numel() // 2)
     p13 = torch.empty_like(w13)
     p2 = torch.empty_like(w2)
-    p = _ffn_params(1, 1, E, H, I2 // 2, 16, w13.dtype, torch.bfloat16)
+    p = _ffn_params(1, 1, E, H, I, 16, w13.dtype, torch.bfloat16)
     _check("moe_prepack_weights", lib.moe_prepack_weights(ctypes.byref(p), _ptr(w13), _ptr(w2),
                                                           _ptr(p13), _ptr(p2), _stream(stream)))
+    return p13, p2
+
+
+def moe_prepack_block_scales(w13_scale, w2_scale, H, I, *, stream=None):
+    """One-time rewrite of MXFP4 block scales (float8_e8m0fnu [E,2I,H/32] and
+    [E,H,I/32]) into the order read beside packed weights; returns the pair."""
+    lib = load_library()
+    E = w13_scale.shape[0]
+    _need(w13_scale, E8M0, "w13_scale", E * 2 * I * (H // 32))
+    _need(w2_scale, E8M0, "w2_scale", E * H * (I // 32))
+    p13 = torch.empty_like(w13_scale)
+    p2 = torch.empty_like(w2_scale)
+    p = _ffn_params(1, 1, E, H, I, 16, FP4, torch.bfloat16)
+    _check("moe_prepack_block_scales", lib.moe_prepack_block_scales(
+        ctypes.byref(p), _ptr(w13_scale), _ptr(w2_scale), _ptr(p13), _ptr(p2), _stream(stream)))
     return p13, p2
 
 
@@ -230,9 +260,9 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     boundaries (the profiling entry point)."""
     lib = load_library()
     T, H = x.shape
-    E, I2, H2 = w13.shape
-    I = I2 // 2
-    if H2 != H or tuple(w2.shape) != (E, H, I):
+    E, I, H2 = weight_dims(w13)
+    fp4 = w13.dtype == FP4
+    if H2 != H or tuple(w2.shape) != (E, H, I // 2 if fp4 else I):
         raise ValueError("weight shapes do not match x")
     _need(x, x.dtype, "x")
     _need(w13, w13.dtype, "w13")
@@ -243,6 +273,9 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     if w13.dtype == torch.float8_e4m3fn:
         _need(w13_scale, torch.float32, "w13_scale", E * 2 * I)
         _need(w2_scale, torch.float32, "w2_scale", E * H)
+    if fp4:
+        _need(w13_scale, E8M0, "w13_scale", E * 2 * I * (H // 32))
+        _need(w2_scale, E8M0, "w2_scale", E * H * (I // 32))
     if y_slots is None:
         y_slots = torch.empty((T * K, H), dtype=torch.float32, device=x.device)
     _need(y_slots, torch.float32, "y_slots", T * K * H)
@@ -296,14 +329,17 @@ class MoELayer:
         if packed is None:
             packed = w13.dtype != torch.float32
         self.packed = bool(packed)
+        E, I, H = weight_dims(w13)
         if self.packed:
             w13, w2 = moe_prepack_weights(w13, w2)
+            if w13.dtype == FP4:
+                w13_scale, w2_scale = moe_prepack_block_scales(w13_scale, w2_scale, H, I)
         self.w13, self.w2, self.w13_scale, self.w2_scale = w13, w2, w13_scale, w2_scale
-        self.E_slabs = w13.shape[0]
+        self.E_slabs = E
         self.E_routed = self.E_slabs - (1 if shared else 0)
         self.T, self.K, self.B, self.shared = T, K, B, shared
         self.KO = K + (1 if shared else 0)
-        self.H, self.I = w13.shape[2], w13.shape[1] // 2
+        self.H, self.I = H, I
         self.route_kw = dict(score=score, n_group=n_group, topk_group=topk_group,
                              renormalize=renormalize, routed_scaling=routed_scaling,
                              append_shared=shared)

@@ -93,25 +93,46 @@ static moe_status_t ffn_check(const moe_ffn_params_t* p) {
     const bool f32 = p->w_dtype == MOE_F32 && p->x_dtype == MOE_F32;
     const bool bf16 = p->w_dtype == MOE_BF16 && p->x_dtype == MOE_BF16;
     const bool fp8 = p->w_dtype == MOE_FP8_E4M3 && p->x_dtype == MOE_BF16;
-    if (!(f32 || bf16 || fp8)) return MOE_ERR_UNSUPPORTED;
+    const bool fp4 = p->w_dtype == MOE_FP4_E2M1 && p->x_dtype == MOE_BF16;
+    if (!(f32 || bf16 || fp8 || fp4)) return MOE_ERR_UNSUPPORTED;
     if (!ffn_block_ok(p->B) || p->E > kAlignMaxExperts) return MOE_ERR_UNSUPPORTED;
     if (f32 && (p->H % 64 || p->I % 64)) return MOE_ERR_UNSUPPORTED;
     if (!f32 && (p->H % 256 || p->I % 128)) return MOE_ERR_UNSUPPORTED;
     if (p->weight_layout != MOE_LAYOUT_CANONICAL && p->weight_layout != MOE_LAYOUT_PACKED)
         return MOE_ERR_INVALID_ARG;
     if (f32 && p->weight_layout == MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
+    if (!f32) {
+        // the matrix-core kernels address each GEMM's activation operand
+        // (x, then the intermediate) with 32-bit byte offsets
+        const int64_t esz = bf16 ? 2 : 1;
+        const int64_t C = capacity((int64_t)p->T * p->K, p->E, p->B);
+        if ((int64_t)p->T * p->H * esz > kFfnMaxOperandBytes || C * p->I * esz > kFfnMaxOperandBytes)
+            return MOE_ERR_UNSUPPORTED;
+    }
     return MOE_OK;
 }
 
 moe_status_t moe_prepack_weights(const moe_ffn_params_t* p, const void* w13, const void* w2,
                                  void* w13_packed, void* w2_packed, void* stream) {
     if (!p || p->E < 1 || p->H < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
-    if (p->w_dtype != MOE_BF16 && p->w_dtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+    if (p->w_dtype != MOE_BF16 && p->w_dtype != MOE_FP8_E4M3 && p->w_dtype != MOE_FP4_E2M1)
+        return MOE_ERR_UNSUPPORTED;
     if (p->H % 256 || p->I % 128 || p->E > kAlignMaxExperts) return MOE_ERR_UNSUPPORTED;
     if (!w13 || !w2 || !w13_packed || !w2_packed) return MOE_ERR_INVALID_ARG;
     if (w13 == w13_packed || w2 == w2_packed) return MOE_ERR_INVALID_ARG;
-    const int esz = p->w_dtype == MOE_BF16 ? 2 : 1;
-    return from_hip(launch_prepack(p->E, p->H, p->I, esz, w13, w2, w13_packed, w2_packed, as_stream(stream)));
+    const int bits = p->w_dtype == MOE_BF16 ? 16 : p->w_dtype == MOE_FP8_E4M3 ? 8 : 4;
+    return from_hip(launch_prepack(p->E, p->H, p->I, bits, w13, w2, w13_packed, w2_packed, as_stream(stream)));
+}
+
+moe_status_t moe_prepack_block_scales(const moe_ffn_params_t* p, const void* w13_scale, const void* w2_scale,
+                                      void* w13_scale_packed, void* w2_scale_packed, void* stream) {
+    if (!p || p->E < 1 || p->H < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
+    if (p->w_dtype != MOE_FP4_E2M1) return MOE_ERR_UNSUPPORTED;
+    if (p->H % 256 || p->I % 128 || p->E > kAlignMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (!w13_scale || !w2_scale || !w13_scale_packed || !w2_scale_packed) return MOE_ERR_INVALID_ARG;
+    if (w13_scale == w13_scale_packed || w2_scale == w2_scale_packed) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_prepack_scales(p->E, p->H, p->I, w13_scale, w2_scale, w13_scale_packed,
+                                          w2_scale_packed, as_stream(stream)));
 }
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
@@ -121,7 +142,7 @@ int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
 }
 
 static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
-                                const float* w13_scale, const void* w2, const float* w2_scale,
+                                const void* w13_scale, const void* w2, const void* w2_scale,
                                 const int32_t* sorted_token_ids, const int32_t* expert_ids,
                                 const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
                                 size_t workspace_bytes, void* stream, hipEvent_t const* ev) {
@@ -132,7 +153,8 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     if (S == 0) return MOE_OK;
     if (!x || !w13 || !w2 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !y_slots)
         return MOE_ERR_INVALID_ARG;
-    if (p->w_dtype == MOE_FP8_E4M3 && (!w13_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+    if ((p->w_dtype == MOE_FP8_E4M3 || p->w_dtype == MOE_FP4_E2M1) && (!w13_scale || !w2_scale))
+        return MOE_ERR_INVALID_ARG;
     const int64_t need = ffn_workspace_bytes(p->w_dtype, p->T, p->H, p->I, C);
     if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
     FfnArgs a;
@@ -145,12 +167,13 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     hipError_t e;
     if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream), ev);
     else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream), ev);
-    else e = launch_ffn_fp8(a, workspace, as_stream(stream), ev);
+    else if (p->w_dtype == MOE_FP8_E4M3) e = launch_ffn_fp8(a, workspace, as_stream(stream), ev);
+    else e = launch_ffn_fp4(a, workspace, as_stream(stream), ev);
     return from_hip(e);
 }
 
 moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
-                             const float* w13_scale, const void* w2, const float* w2_scale,
+                             const void* w13_scale, const void* w2, const void* w2_scale,
                              const int32_t* sorted_token_ids, const int32_t* expert_ids,
                              const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
                              size_t workspace_bytes, void* stream) {
@@ -159,7 +182,7 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const voi
 }
 
 moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, const void* w13,
-                                      const float* w13_scale, const void* w2, const float* w2_scale,
+                                      const void* w13_scale, const void* w2, const void* w2_scale,
                                       const int32_t* sorted_token_ids, const int32_t* expert_ids,
                                       const int32_t* num_tokens_post_padded, float* y_slots,
                                       void* workspace, size_t workspace_bytes, void* stream,

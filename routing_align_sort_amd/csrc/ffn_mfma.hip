@@ -47,8 +47,33 @@
 namespace moe {
 
 constexpr int kFfnThreads = 256;
-constexpr int kStepBytes = 128;                 // bytes of a row per K-step
-constexpr int kLdsPitch = kStepBytes + 16;      // padded LDS row, bytes
+constexpr int kAStepBytes = 128;                // activation bytes of a row per K-step
+constexpr int kLdsPitch = kAStepBytes + 16;     // padded LDS row, bytes
+
+// Weight formats of the matrix-core path.  A K-step is 128 activation bytes
+// of a row: 64 bf16 or 128 E4M3 elements of the contraction.  The weights
+// of a K-step are 128 bytes of a row (bf16, E4M3) or 64 (E2M1: two codes per
+// byte), loaded by each lane as Q 16-byte quarters of its half of the row.
+enum : int { kWBf16 = 0, kWFp8 = 1, kWFp4 = 2 };
+template <int kW>
+struct Fmt {
+    static constexpr int kBits = kW == kWBf16 ? 16 : kW == kWFp8 ? 8 : 4;
+    static constexpr int kBStep = kW == kWFp4 ? 64 : 128;   // weight bytes of a row per K-step
+    static constexpr int Q = kBStep / 32;                   // 16-byte quarters per lane and K-step
+    static constexpr bool kQuantA = kW != kWBf16;           // E4M3 activations, one scale per row
+    static constexpr bool kChanScale = kW == kWFp8;         // one fp32 scale per weight row
+    // Packed weight layout (written by moe_prepack_weights): for every expert,
+    // N tile, K-step, wave and row set, the 64 lanes' quarters q = 0..Q-1 are
+    // stored as Q contiguous 1 KB blocks, so each load instruction of a wave
+    // reads 1 KB of consecutive bytes and a wave's K-step is one run.
+    static constexpr int kPackWave = 2 * Q * 1024;          // two row sets
+    static constexpr int kPackStep = 4 * kPackWave;         // four waves
+};
+// Packed E8M0 block scales of E2M1 weights: for every expert, N tile, K-step
+// and wave, one 4-byte word per lane: the lane's two scale bytes of row set 0
+// (low half) and of row set 1 (high half).
+constexpr int kPackScaleWaveBytes = 64 * 4;
+constexpr int kPackScaleStepBytes = 4 * kPackScaleWaveBytes;
 
 // K-steps of weights in flight per wave (register ring depth - 1).
 #ifndef MOE_FFN_PF
@@ -64,12 +89,6 @@ constexpr int kLdsPitch = kStepBytes + 16;      // padded LDS row, bytes
 #define MOE_FFN_GROUP_M 8
 #endif
 
-// Packed weight layout (written by moe_prepack_weights): for every expert,
-// N tile, K-step, wave and row set, the 64 lanes' 16-byte quarters q = 0..3
-// are stored as four contiguous 1 KB blocks, so each load instruction of a
-// wave reads 1 KB of consecutive bytes and a wave's K-step is 8 KB in one run.
-constexpr int kPackWaveBytes = 2 * 4 * 1024;              // two row sets x four quarters
-constexpr int kPackStepBytes = 4 * kPackWaveBytes;        // four waves
 
 #ifndef MOE_FFN_PIN_LOADS
 #define MOE_FFN_PIN_LOADS 1
@@ -97,7 +116,8 @@ template <int BM>
 struct Tile {
     static constexpr int MT = (BM < 32 ? 32 : BM) / 32;         // 32-row MFMA tiles
     static constexpr int ROWS = MT * 32;
-    static constexpr int ACH = ROWS * (kStepBytes / 16);         // 16-byte A chunks per K-step
+    static constexpr int CPR = kAStepBytes / 16;                  // 16-byte A chunks per row
+    static constexpr int ACH = ROWS * CPR;                        // A chunks per K-step
     static constexpr int APT = ACH / kFfnThreads;                // chunks per thread (exact)
     static_assert(ACH % kFfnThreads == 0, "every thread moves whole chunks");
     static constexpr int LDS_BYTES = 2 * ROWS * kLdsPitch;
@@ -110,20 +130,40 @@ __device__ __forceinline__ i32x8_t as_i32x8(uint4 lo, uint4 hi) {
     r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
     return r;
 }
+// An E2M1 operand (32 codes, element j in bits 4j..4j+3) in the low four
+// registers of the operand tuple; the instruction reads only those.
+__device__ __forceinline__ i32x8_t as_fp4_operand(uint4 v) {
+    i32x8_t r;
+    r[0] = (int)v.x; r[1] = (int)v.y; r[2] = (int)v.z; r[3] = (int)v.w;
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
 
 // The shared K loop.  A row m starts at abase + arow[m] * arow_bytes
 // (arow[m] < 0: a zero row); brow[ns] is this lane's first weight byte for
-// row set ns; nk K-steps of 128 bytes; acc[MT][NSUB] accumulates.
+// row set ns; nk K-steps; acc[MT][NSUB] accumulates.  E2M1 weights also
+// stream their block scales: sptr is this lane's first scale word (below).
 // Every address derives from the kernel's global-memory arguments, so all
 // loads are global loads (vmcnt only) and waiting for one K-step's
 // activations never drains the weight loads already in flight for later
 // K-steps.
-template <bool kFp8, bool kPacked, bool kNT, int BM, int NSUB, int PF, int LA>
+//
+// Contraction order inside a K-step (any permutation works if A and B agree):
+// lane half h of the 64-wide weight operand covers the K-step's elements
+// [h*KS/2, (h+1)*KS/2), split into consecutive MFMA slices (32 elements for
+// E4M3 / E2M1, 8 per lane for bf16) -- so each lane's weight bytes of a
+// K-step are one contiguous half of its row's K-step, loaded as 16-byte
+// quarters, and its E2M1 block scales (one per 32-element slice) are two
+// consecutive bytes of the row's scales.  The activation fragments are read
+// from LDS in whatever order pairs them with those weight elements.
+template <int kW, bool kPacked, bool kNT, int BM, int NSUB, int PF, int LA>
 __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const int* arow, int64_t arow_bytes,
-                                      const uint8_t* const (&brow)[NSUB], int nk,
-                                      uint8_t* lds, f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
+                                      const uint8_t* const (&brow)[NSUB], const uint8_t* const (&srow)[NSUB],
+                                      int nk, uint8_t* lds, f32x16_t (&acc)[Tile<BM>::MT][NSUB]) {
     using TL = Tile<BM>;
+    using F = Fmt<kW>;
     constexpr int MT = TL::MT;
+    constexpr int CPR = TL::CPR;
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int half = lane >> 5;
@@ -134,24 +174,34 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
     // condition.  A padding row (-1), and a tile row past the block, reads row
     // 0 instead: rows of the product depend only on their own A row, and the
     // outputs of those rows are never used.
-    const uint8_t* asrc[TL::APT];
+    // Chunk r of this thread is tile row tid/CPR + r*RPS, bytes (tid%CPR)*16:
+    // one column, so LDS addresses differ by constants and the global
+    // addresses are 32-bit offsets from the uniform base (the activation
+    // operand is below 4 GiB, checked on the host).
+    static_assert(kFfnThreads % CPR == 0, "chunks of a thread share a column");
+    constexpr int RPS = kFfnThreads / CPR;            // tile rows between a thread's chunks
+    const int lds_a = (tid / CPR) * kLdsPitch + (tid % CPR) * 16;
+    uint32_t aoff[TL::APT];
 #pragma unroll
     for (int r = 0; r < TL::APT; ++r) {
-        const int c = tid + r * kFfnThreads;
-        const int row = (c >> 3) < BM ? arow[c >> 3] : -1;
-        asrc[r] = abase + (int64_t)(row >= 0 ? row : 0) * arow_bytes + (c & 7) * 16;
+        const int m = tid / CPR + r * RPS;
+        const int row = m < BM ? arow[m] : -1;
+        aoff[r] = (uint32_t)((int64_t)(row >= 0 ? row : 0) * arow_bytes) + (uint32_t)((tid % CPR) * 16);
     }
 
     // A runs LA K-steps ahead in a ring of LA register sets (LA is 1 or PF+1,
     // so ring slots stay compile-time indices in the loop unrolled by PF+1).
     static_assert(LA == 1 || LA == PF + 1, "activation lookahead must divide the unroll");
     uint4 areg[LA][TL::APT];
-    // Weights run PF K-steps ahead.  bf16: four 16-byte MFMA operands per row
-    // set; fp8: two 32-byte operands, each assembled from two 16-byte loads
-    // straight into its register tuple.
-    using BOp = typename std::conditional<kFp8, i32x8_t, uint4>::type;
-    constexpr int NB = kFp8 ? 2 : 4;
+    // Weights run PF K-steps ahead.  bf16 / E2M1: Q 16-byte quarters per row
+    // set (one MFMA slice each); E4M3: two 32-byte operands, each assembled
+    // from two 16-byte loads straight into its register tuple.
+    using BOp = typename std::conditional<kW == kWFp8, i32x8_t, uint4>::type;
+    constexpr int NB = kW == kWFp8 ? 2 : F::Q;
     BOp breg[PF + 1][NSUB][NB];
+    // E2M1: one scale word per K-step, byte 2*ns + kk = row set ns, slice kk
+    uint32_t sreg[PF + 1];
+    static_assert(kW != kWFp4 || NSUB == 2, "scale words pair two row sets");
 
     // Loads are issued unconditionally (K-step indices clamped at the end):
     // with a fixed number of loads per K-step the compiler's wait counts can
@@ -159,22 +209,20 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
     auto load_a = [&](uint4 (&dst)[TL::APT], int k) {
 #pragma unroll
         for (int r = 0; r < TL::APT; ++r)
-            dst[r] = __builtin_bit_cast(uint4, *(const u32x4_t*)(asrc[r] + (int64_t)k * kStepBytes));
+            dst[r] = __builtin_bit_cast(uint4, *(const u32x4_t*)(abase + (aoff[r] + (uint32_t)(k * kAStepBytes))));
     };
     auto store_a = [&](const uint4 (&src)[TL::APT], int buf) {
 #pragma unroll
-        for (int r = 0; r < TL::APT; ++r) {
-            const int c = tid + r * kFfnThreads;
-            *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + (c >> 3) * kLdsPitch + (c & 7) * 16) = src[r];
-        }
+        for (int r = 0; r < TL::APT; ++r)
+            *(uint4*)(lds + buf * TL::ROWS * kLdsPitch + lds_a + r * RPS * kLdsPitch) = src[r];
     };
-    constexpr int64_t kB = kPacked ? kPackStepBytes : kStepBytes;   // per K-step
+    constexpr int64_t kB = kPacked ? F::kPackStep : F::kBStep;      // per K-step
     constexpr int qB = kPacked ? 1024 : 16;                           // per quarter
-    auto load_b = [&](BOp (&dst)[NSUB][NB], int k) {
+    auto load_b = [&](BOp (&dst)[NSUB][NB], uint32_t& sdst, int k) {
 #pragma unroll
         for (int ns = 0; ns < NSUB; ++ns) {
             const uint8_t* src = brow[ns] + (int64_t)k * kB;
-            if constexpr (kFp8) {
+            if constexpr (kW == kWFp8) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const uint4 lo = load_weight<kNT>(src + (2 * j) * qB);
@@ -183,27 +231,34 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) dst[ns][q] = load_weight<kNT>(src + q * qB);
+                for (int q = 0; q < NB; ++q) dst[ns][q] = load_weight<kNT>(src + q * qB);
+            }
+        }
+        if constexpr (kW == kWFp4) {
+            if constexpr (kPacked) {
+                sdst = *(const uint32_t*)(srow[0] + (int64_t)k * kPackScaleStepBytes);
+            } else {
+                const uint32_t s0 = *(const uint16_t*)(srow[0] + (int64_t)k * 4);
+                const uint32_t s1 = *(const uint16_t*)(srow[1] + (int64_t)k * 4);
+                sdst = s0 | (s1 << 16);
             }
         }
     };
-    auto compute = [&](const BOp (&b)[NSUB][NB], int buf) {
-        const uint8_t* base = lds + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * 64;
-        if constexpr (!kFp8) {
+    auto compute = [&](const BOp (&b)[NSUB][NB], uint32_t sc, int buf) {
+        const uint8_t* base = lds + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * (kAStepBytes / 2);
+        if constexpr (kW == kWBf16) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const uint4 af = *(const uint4*)(base + mt * 32 * kLdsPitch + kk * 16);
 #pragma unroll
-                    for (int ns = 0; ns < NSUB; ++ns) {
-                        if constexpr (!kFp8)
-                            acc[mt][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                as_bf16x8(af), as_bf16x8(b[ns][kk]), acc[mt][ns], 0, 0, 0);
-                    }
+                    for (int ns = 0; ns < NSUB; ++ns)
+                        acc[mt][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af), as_bf16x8(b[ns][kk]),
+                                                                              acc[mt][ns], 0, 0, 0);
                 }
             }
-        } else {
+        } else if constexpr (kW == kWFp8) {
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -216,6 +271,31 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
                             as_i32x8(a0, a1), b[ns][kk], acc[mt][ns], 0, 0, 0, 127, 0, 127);
                 }
             }
+        } else {
+            // E4M3 x E2M1.  Each lane half of the E2M1 operand holds 32
+            // consecutive elements (slice kk of its half of the K-step, as
+            // for E4M3), but the instruction pairs bytes [0,16) of an E4M3
+            // lane half h with elements [16h, 16h+16) of the first E2M1 lane
+            // half, and bytes [16,32) with the same range of the second: so
+            // the activations come from two 16-byte chunks 64 bytes apart.
+            // The weights' block scale of (ns, kk) is byte 2*ns + kk of the
+            // scale word (an immediate of the instruction); the activations'
+            // scale field is 1.0.
+            const uint8_t* abase4 = lds + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * 16;
+            auto slice = [&](auto kkc) {
+                constexpr int kk = decltype(kkc)::value;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const i32x8_t af = as_i32x8(*(const uint4*)(abase4 + mt * 32 * kLdsPitch + kk * 32),
+                                                *(const uint4*)(abase4 + mt * 32 * kLdsPitch + 64 + kk * 32));
+                    acc[mt][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af, as_fp4_operand(b[0][kk]), acc[mt][0], 0, 4, 0, 127, kk, (int)sc);
+                    acc[mt][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af, as_fp4_operand(b[1][kk]), acc[mt][1], 0, 4, 0, 127, 2 + kk, (int)sc);
+                }
+            };
+            slice(std::integral_constant<int, 0>{});
+            slice(std::integral_constant<int, 1>{});
         }
     };
 
@@ -224,7 +304,7 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
 #pragma unroll
     for (int j = 0; j < LA; ++j) load_a(areg[j], min(j, nk - 1));
 #pragma unroll
-    for (int s = 0; s < PF; ++s) load_b(breg[s], min(s, nk - 1));
+    for (int s = 0; s < PF; ++s) load_b(breg[s], sreg[s], min(s, nk - 1));
     store_a(areg[0], 0);
     __syncthreads();
 
@@ -237,11 +317,11 @@ __device__ __forceinline__ void kloop(const uint8_t* __restrict__ abase, const i
             const int k = k0 + u;
             if (k < nk) {
                 load_a(areg[u % LA], min(k + LA, nk - 1));
-                load_b(breg[(u + PF) % (PF + 1)], min(k + PF, nk - 1));
+                load_b(breg[(u + PF) % (PF + 1)], sreg[(u + PF) % (PF + 1)], min(k + PF, nk - 1));
                 // keep the loads ahead of this step's MFMAs: left to itself
                 // the scheduler sinks them to the end of the step
                 if (MOE_FFN_PIN_LOADS) __builtin_amdgcn_sched_barrier(0);
-                compute(breg[u], k & 1);
+                compute(breg[u], sreg[u], k & 1);
                 // unconditional: after the last step it rewrites the idle
                 // buffer with data nobody reads, but a condition here would
                 // let the compiler sink the A loads down to this store
@@ -277,16 +357,29 @@ __device__ __forceinline__ bool ffn_tile(int nmb, int nN, int* mb, int* nt) {
 }
 
 // This lane's first weight byte for row set ns of wave w in N tile nt.
-// Canonical: row `row` of a [rows, row_bytes] slab, this lane's 64-byte half.
-// Packed: the lane's 16 bytes in the first 1 KB block of the (nt, w, ns) run.
-template <bool kPacked>
+// Canonical: row `row` of a [rows, row_bytes] slab, this lane's half of the
+// row's first K-step.  Packed: the lane's 16 bytes in the first 1 KB block of
+// the (nt, w, ns) run.
+template <int kW, bool kPacked>
 __device__ __forceinline__ const uint8_t* weight_lane_ptr(const uint8_t* slab, int row, int64_t row_bytes,
                                                           int nt, int w, int ns, int lane) {
+    using F = Fmt<kW>;
     if (kPacked) {
-        const int64_t nk = row_bytes / kStepBytes;
-        return slab + (int64_t)nt * nk * kPackStepBytes + w * kPackWaveBytes + ns * 4096 + lane * 16;
+        const int64_t nk = row_bytes / F::kBStep;
+        return slab + (int64_t)nt * nk * F::kPackStep + w * F::kPackWave + ns * (F::Q * 1024) + lane * 16;
     }
-    return slab + (int64_t)row * row_bytes + (lane >> 5) * 64;
+    return slab + (int64_t)row * row_bytes + (lane >> 5) * (F::kBStep / 2);
+}
+
+// This lane's first E8M0 scale bytes (nk K-steps of 128 elements; a row has
+// nk * 4 scale bytes, the lane's two are those of its half of the K-step).
+// Canonical: in row `row` of the [rows, nk*4] scale slab.  Packed: the lane's
+// word of (nt, w), which also holds the second row set's pair.
+template <bool kPacked>
+__device__ __forceinline__ const uint8_t* scale_lane_ptr(const uint8_t* slab, int row, int nk, int nt, int w,
+                                                         int lane) {
+    if (kPacked) return slab + ((int64_t)nt * nk * 4 + w) * kPackScaleWaveBytes + lane * 4;
+    return slab + (int64_t)row * nk * 4 + (lane >> 5) * 2;
 }
 
 template <int MT, int NSUB>
@@ -355,31 +448,57 @@ __device__ __forceinline__ bool stream_weights(const FfnArgs& a, int mb, int BM,
 #ifndef MOE_FFN_LA_FULL
 #define MOE_FFN_LA_FULL 1
 #endif
-template <bool kFp8, int BM>
+// E2M1 weights: half the weight registers of E4M3 per K-step in flight.
+#ifndef MOE_FFN_FP4_PF
+#define MOE_FFN_FP4_PF 2
+#endif
+#ifndef MOE_FFN_FP4_LA_FULL
+#define MOE_FFN_FP4_LA_FULL 1
+#endif
+#ifndef MOE_FFN_FP4_128_OCC
+#define MOE_FFN_FP4_128_OCC 2
+#endif
+#ifndef MOE_FFN_FP4_128_PF
+#define MOE_FFN_FP4_128_PF 1
+#endif
+#ifndef MOE_FFN_FP4_128_LA
+#define MOE_FFN_FP4_128_LA 1
+#endif
+#ifndef MOE_FFN_FP4_256_PF
+#define MOE_FFN_FP4_256_PF 2
+#endif
+#ifndef MOE_FFN_FP4_256_LA
+#define MOE_FFN_FP4_256_LA 0
+#endif
+template <int kW, int BM>
 constexpr int ffn_min_blocks() {
     if (BM >= 256) return 1;
-    if (BM == 128) return kFp8 ? MOE_FFN_FP8_128_OCC : MOE_FFN_OCC128;
+    if (BM == 128)
+        return kW == kWFp8 ? MOE_FFN_FP8_128_OCC : kW == kWFp4 ? MOE_FFN_FP4_128_OCC : MOE_FFN_OCC128;
     return 2;
 }
-template <bool kFp8, int BM>
+template <int kW, int BM>
 constexpr int ffn_pf() {
-    if (BM >= 256) return kFp8 ? MOE_FFN_FP8_256_PF : MOE_FFN_PF256;
-    if (BM == 128) return kFp8 ? MOE_FFN_FP8_128_PF : MOE_FFN_PF128;
-    return MOE_FFN_PF;
+    if (BM >= 256) return kW == kWFp8 ? MOE_FFN_FP8_256_PF : kW == kWFp4 ? MOE_FFN_FP4_256_PF : MOE_FFN_PF256;
+    if (BM == 128) return kW == kWFp8 ? MOE_FFN_FP8_128_PF : kW == kWFp4 ? MOE_FFN_FP4_128_PF : MOE_FFN_PF128;
+    return kW == kWFp4 ? MOE_FFN_FP4_PF : MOE_FFN_PF;
 }
-template <bool kFp8, int BM, int PF>
+template <int kW, int BM, int PF>
 constexpr int ffn_la() {
-    const bool full = BM < 128    ? MOE_FFN_LA_FULL
-                      : BM == 128 ? (kFp8 ? MOE_FFN_FP8_128_LA : MOE_FFN_LA128)
-                                  : (kFp8 ? MOE_FFN_FP8_256_LA : MOE_FFN_LA256);
+    const bool full = BM < 128    ? (kW == kWFp4 ? MOE_FFN_FP4_LA_FULL : MOE_FFN_LA_FULL)
+                      : BM == 128 ? (kW == kWFp8 ? MOE_FFN_FP8_128_LA : kW == kWFp4 ? MOE_FFN_FP4_128_LA
+                                                                                  : MOE_FFN_LA128)
+                                  : (kW == kWFp8 ? MOE_FFN_FP8_256_LA : kW == kWFp4 ? MOE_FFN_FP4_256_LA
+                                                                                  : MOE_FFN_LA256);
     return full ? PF + 1 : 1;
 }
 
-template <bool kFp8, bool kPacked, int BM, int PF>
-__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
+template <int kW, bool kPacked, int BM, int PF>
+__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
 ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     using TL = Tile<BM>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[Tile<BM>::LDS_BYTES];
+    using F = Fmt<kW>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
     __shared__ int arow[BM];
     __shared__ float rowscale[BM];
     int mb, nt;
@@ -387,37 +506,43 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     const int e = a.expert_ids[mb];
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int H = a.H, I = a.I;
-    constexpr int esz = kFp8 ? 1 : 2;
     if (tid < BM) {
         const int slot = a.sorted_ids[(int64_t)mb * BM + tid];
         const bool ok = slot < a.S;
         const int t = ok ? slot / a.K : 0;
         arow[tid] = ok ? t : -1;                          // token row of x, -1 = padding
-        if (kFp8) rowscale[tid] = ok ? q.sx[t] : 0.f;
+        if (F::kQuantA) rowscale[tid] = ok ? q.sx[t] : 0.f;
     }
     __syncthreads();
 
     const int n0 = nt * 128 + w * 32;                       // this wave's intermediate columns
     const int r32 = lane & 31;
-    const uint8_t* wbase = (const uint8_t*)a.w13 + (int64_t)e * 2 * I * H * esz;
-    const uint8_t* const brow[2] = {
-        weight_lane_ptr<kPacked>(wbase, n0 + r32, (int64_t)H * esz, nt, w, 0, lane),
-        weight_lane_ptr<kPacked>(wbase, I + n0 + r32, (int64_t)H * esz, nt, w, 1, lane)};
+    const int64_t wrow = (int64_t)H * F::kBits / 8;         // weight bytes of a row
+    const int nk = (int)(wrow / F::kBStep);
+    const uint8_t* wbase = (const uint8_t*)a.w13 + (int64_t)e * 2 * I * wrow;
+    const uint8_t* const brow[2] = {weight_lane_ptr<kW, kPacked>(wbase, n0 + r32, wrow, nt, w, 0, lane),
+                                    weight_lane_ptr<kW, kPacked>(wbase, I + n0 + r32, wrow, nt, w, 1, lane)};
+    const uint8_t* srow[2] = {nullptr, nullptr};
+    if constexpr (kW == kWFp4) {
+        const uint8_t* sbase = (const uint8_t*)a.w13_scale + (int64_t)e * 2 * I * nk * 4;
+        srow[0] = scale_lane_ptr<kPacked>(sbase, n0 + r32, nk, nt, w, lane);
+        srow[1] = scale_lane_ptr<kPacked>(sbase, I + n0 + r32, nk, nt, w, lane);
+    }
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
-    const uint8_t* xs = kFp8 ? (const uint8_t*)q.xq : (const uint8_t*)a.x;
+    const uint8_t* xs = F::kQuantA ? (const uint8_t*)q.xq : (const uint8_t*)a.x;
+    const int64_t xrow = F::kQuantA ? (int64_t)H : (int64_t)H * 2;
     if (stream_weights(a, mb, BM, e))
-        kloop<kFp8, kPacked, true, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(xs, arow, (int64_t)H * esz, brow,
-                                                                    H * esz / kStepBytes, lds, acc);
+        kloop<kW, kPacked, true, BM, 2, PF, ffn_la<kW, BM, PF>()>(xs, arow, xrow, brow, srow, nk, lds, acc);
     else
-        kloop<kFp8, kPacked, false, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(xs, arow, (int64_t)H * esz, brow,
-                                                                     H * esz / kStepBytes, lds, acc);
+        kloop<kW, kPacked, false, BM, 2, PF, ffn_la<kW, BM, PF>()>(xs, arow, xrow, brow, srow, nk, lds, acc);
 
     const int col = n0 + r32;
     float sg = 1.f, su = 1.f;
-    if (kFp8) {
-        sg = a.w13_scale[(int64_t)e * 2 * I + col];
-        su = a.w13_scale[(int64_t)e * 2 * I + I + col];
+    if (F::kChanScale) {
+        const float* ws13 = (const float*)a.w13_scale;
+        sg = ws13[(int64_t)e * 2 * I + col];
+        su = ws13[(int64_t)e * 2 * I + I + col];
     }
 #pragma unroll
     for (int mt = 0; mt < TL::MT; ++mt)
@@ -425,13 +550,13 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
         for (int i = 0; i < 16; ++i) {
             const int m = mt * 32 + acc_row(i, lane);
             float g = acc[mt][0][i], u = acc[mt][1][i];
-            if (kFp8) {
+            if (F::kQuantA) {
                 const float s = (m < BM) ? rowscale[m] : 0.f;
                 g = g * s * sg;
                 u = u * s * su;
             }
             const float hval = silu_f32(g) * u;
-            if constexpr (kFp8) {
+            if constexpr (F::kQuantA) {
                 // row max over this wave's 32 columns, then one atomic per row
                 float mx = fabsf(hval);
 #pragma unroll
@@ -447,11 +572,12 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
 }
 
 // ------------------------------------------------------------------ stage 2 --
-template <bool kFp8, bool kPacked, int BM, int PF>
-__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kFp8, BM>()))
+template <int kW, bool kPacked, int BM, int PF>
+__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     using TL = Tile<BM>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[Tile<BM>::LDS_BYTES];
+    using F = Fmt<kW>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
     __shared__ int arow[BM];
     __shared__ int slots[BM];
     __shared__ float rowscale[BM];
@@ -460,33 +586,39 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
     const int e = a.expert_ids[mb];
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int H = a.H, I = a.I;
-    constexpr int esz = kFp8 ? 1 : 2;
     if (tid < BM) {
         arow[tid] = mb * BM + tid;                        // sorted row of the intermediate
         slots[tid] = a.sorted_ids[(int64_t)mb * BM + tid];
-        if (kFp8) rowscale[tid] = sa[(int64_t)mb * BM + tid];
+        if (F::kQuantA) rowscale[tid] = sa[(int64_t)mb * BM + tid];
     }
     __syncthreads();
 
     const int n0 = nt * 256 + w * 64;                       // this wave's output columns
     const int r32 = lane & 31;
-    const uint8_t* wbase = (const uint8_t*)a.w2 + (int64_t)e * H * I * esz;
-    const uint8_t* const brow[2] = {
-        weight_lane_ptr<kPacked>(wbase, n0 + r32, (int64_t)I * esz, nt, w, 0, lane),
-        weight_lane_ptr<kPacked>(wbase, n0 + 32 + r32, (int64_t)I * esz, nt, w, 1, lane)};
+    const int64_t wrow = (int64_t)I * F::kBits / 8;
+    const int nk = (int)(wrow / F::kBStep);
+    const uint8_t* wbase = (const uint8_t*)a.w2 + (int64_t)e * H * wrow;
+    const uint8_t* const brow[2] = {weight_lane_ptr<kW, kPacked>(wbase, n0 + r32, wrow, nt, w, 0, lane),
+                                    weight_lane_ptr<kW, kPacked>(wbase, n0 + 32 + r32, wrow, nt, w, 1, lane)};
+    const uint8_t* srow[2] = {nullptr, nullptr};
+    if constexpr (kW == kWFp4) {
+        const uint8_t* sbase = (const uint8_t*)a.w2_scale + (int64_t)e * H * nk * 4;
+        srow[0] = scale_lane_ptr<kPacked>(sbase, n0 + r32, nk, nt, w, lane);
+        srow[1] = scale_lane_ptr<kPacked>(sbase, n0 + 32 + r32, nk, nt, w, lane);
+    }
     f32x16_t acc[TL::MT][2];
     zero_acc(acc);
+    const int64_t hrow = F::kQuantA ? (int64_t)I : (int64_t)I * 2;
     if (stream_weights(a, mb, BM, e))
-        kloop<kFp8, kPacked, true, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(h_in, arow, (int64_t)I * esz, brow,
-                                                                    I * esz / kStepBytes, lds, acc);
+        kloop<kW, kPacked, true, BM, 2, PF, ffn_la<kW, BM, PF>()>(h_in, arow, hrow, brow, srow, nk, lds, acc);
     else
-        kloop<kFp8, kPacked, false, BM, 2, PF, ffn_la<kFp8, BM, PF>()>(h_in, arow, (int64_t)I * esz, brow,
-                                                                     I * esz / kStepBytes, lds, acc);
+        kloop<kW, kPacked, false, BM, 2, PF, ffn_la<kW, BM, PF>()>(h_in, arow, hrow, brow, srow, nk, lds, acc);
 
     float s0 = 1.f, s1 = 1.f;
-    if (kFp8) {
-        s0 = a.w2_scale[(int64_t)e * H + n0 + r32];
-        s1 = a.w2_scale[(int64_t)e * H + n0 + 32 + r32];
+    if (F::kChanScale) {
+        const float* ws2 = (const float*)a.w2_scale;
+        s0 = ws2[(int64_t)e * H + n0 + r32];
+        s1 = ws2[(int64_t)e * H + n0 + 32 + r32];
     }
 #pragma unroll
     for (int mt = 0; mt < TL::MT; ++mt)
@@ -497,7 +629,7 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
                 const int slot = slots[m];
                 if (slot < a.S) {
                     float y0 = acc[mt][0][i], y1 = acc[mt][1][i];
-                    if (kFp8) {
+                    if (F::kQuantA) {
                         const float rs = rowscale[m];
                         y0 = y0 * rs * s0;
                         y1 = y1 * rs * s1;
@@ -617,9 +749,10 @@ static Fp8Ws fp8_ws(void* ws, int64_t T, int64_t H, int64_t I, int64_t C) {
     return q;
 }
 
-template <bool kFp8, bool kPacked, int BM>
+template <int kW, bool kPacked, int BM>
 static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
-    constexpr int PF = ffn_pf<kFp8, BM>();
+    constexpr int PF = ffn_pf<kW, BM>();
+    constexpr bool kQuant = Fmt<kW>::kQuantA;
     const int nMB = (int)(a.C / BM);
     const int nN1 = a.I / 128, nN2 = a.H / 256;
     const int t1 = nMB * nN1, t2 = nMB * nN2;
@@ -627,7 +760,7 @@ static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream,
     Fp8Ws q{};
     const uint8_t* h_in = static_cast<const uint8_t*>(ws);
     if ((err = record_stage(ev, 0, stream)) != hipSuccess) return err;
-    if (kFp8) {
+    if (kQuant) {
         q = fp8_ws(ws, a.T, a.H, a.I, a.C);
         if (a.T > 0)
             hipLaunchKernelGGL(quant_tokens_kernel, dim3(a.T), dim3(kQuantThreads), 0, stream,
@@ -637,94 +770,143 @@ static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream,
     }
     if ((err = record_stage(ev, 1, stream)) != hipSuccess) return err;
     if (t1 > 0)
-        hipLaunchKernelGGL((ffn_stage1<kFp8, kPacked, BM, PF>), dim3(t1), dim3(kFfnThreads), 0, stream, a,
+        hipLaunchKernelGGL((ffn_stage1<kW, kPacked, BM, PF>), dim3(t1), dim3(kFfnThreads), 0, stream, a,
                            (uint16_t*)ws, q, nN1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = record_stage(ev, 2, stream)) != hipSuccess) return err;
-    if (kFp8 && a.C > 0) {
+    if (kQuant && a.C > 0) {
         hipLaunchKernelGGL(requant_rows_kernel, dim3((unsigned)a.C), dim3(kQuantThreads), 0, stream,
                            (const float*)q.a, (const uint32_t*)q.amax, a.post_padded, a.I, q.aq, q.sa);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if ((err = record_stage(ev, 3, stream)) != hipSuccess) return err;
     if (t2 > 0)
-        hipLaunchKernelGGL((ffn_stage2<kFp8, kPacked, BM, PF>), dim3(t2), dim3(kFfnThreads), 0, stream, a,
+        hipLaunchKernelGGL((ffn_stage2<kW, kPacked, BM, PF>), dim3(t2), dim3(kFfnThreads), 0, stream, a,
                            h_in, (const float*)q.sa, nN2);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     return record_stage(ev, 4, stream);
 }
 
-template <bool kFp8, bool kPacked>
+template <int kW, bool kPacked>
 static hipError_t launch_mfma_layout(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
     switch (a.B) {
-        case 16: return launch_mfma_bm<kFp8, kPacked, 16>(a, ws, stream, ev);
-        case 32: return launch_mfma_bm<kFp8, kPacked, 32>(a, ws, stream, ev);
-        case 64: return launch_mfma_bm<kFp8, kPacked, 64>(a, ws, stream, ev);
-        case 128: return launch_mfma_bm<kFp8, kPacked, 128>(a, ws, stream, ev);
-        case 256: return launch_mfma_bm<kFp8, kPacked, 256>(a, ws, stream, ev);
+        case 16: return launch_mfma_bm<kW, kPacked, 16>(a, ws, stream, ev);
+        case 32: return launch_mfma_bm<kW, kPacked, 32>(a, ws, stream, ev);
+        case 64: return launch_mfma_bm<kW, kPacked, 64>(a, ws, stream, ev);
+        case 128: return launch_mfma_bm<kW, kPacked, 128>(a, ws, stream, ev);
+        case 256: return launch_mfma_bm<kW, kPacked, 256>(a, ws, stream, ev);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool kFp8>
+template <int kW>
 static hipError_t launch_mfma(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
-    return a.packed ? launch_mfma_layout<kFp8, true>(a, ws, stream, ev)
-                    : launch_mfma_layout<kFp8, false>(a, ws, stream, ev);
+    return a.packed ? launch_mfma_layout<kW, true>(a, ws, stream, ev)
+                    : launch_mfma_layout<kW, false>(a, ws, stream, ev);
 }
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
-    return launch_mfma<false>(a, ws, stream, ev);
+    return launch_mfma<kWBf16>(a, ws, stream, ev);
 }
 hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
-    return launch_mfma<true>(a, ws, stream, ev);
+    return launch_mfma<kWFp8>(a, ws, stream, ev);
+}
+hipError_t launch_ffn_fp4(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
+    return launch_mfma<kWFp4>(a, ws, stream, ev);
 }
 
 // ----------------------------------------------------------------- prepack --
 // One 16-byte chunk per thread, walked in packed order (coalesced writes):
 // chunk c -> (expert, N tile, K-step, wave, row set, quarter, lane), and the
 // canonical row / byte it comes from.  Row of (tile, wave, row set, lane):
-// ns * ns_stride + tile * tile_rows + wave * wave_rows + lane % 32.
+// ns * ns_stride + tile * tile_rows + wave * wave_rows + lane % 32.  A K-step
+// is 32*Q bytes of a row; lane half h holds bytes [h*16Q, (h+1)*16Q) of it.
 __global__ void __launch_bounds__(256)
-prepack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nchunks, int nN,
-               int nk, int64_t rows_total, int64_t row_bytes, int ns_stride, int tile_rows,
-               int wave_rows) {
+prepack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nchunks, int nN, int nk,
+               int log2q, int64_t rows_total, int64_t row_bytes, int ns_stride, int tile_rows, int wave_rows) {
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= nchunks) return;
+    const int Q = 1 << log2q;
     const int lane = (int)(c & 63);
-    const int q = (int)((c >> 6) & 3);
-    const int ns = (int)((c >> 8) & 1);
-    const int w = (int)((c >> 9) & 3);
-    const int64_t rest = c >> 11;
+    const int q = (int)((c >> 6) & (Q - 1));
+    const int ns = (int)((c >> (6 + log2q)) & 1);
+    const int w = (int)((c >> (7 + log2q)) & 3);
+    const int64_t rest = c >> (9 + log2q);
     const int k = (int)(rest % nk);
     const int t = (int)((rest / nk) % nN);
     const int64_t e = rest / ((int64_t)nk * nN);
     const int64_t row = (int64_t)ns * ns_stride + (int64_t)t * tile_rows + w * wave_rows + (lane & 31);
-    const int64_t byte = (int64_t)k * kStepBytes + (lane >> 5) * 64 + q * 16;
+    const int64_t byte = (int64_t)k * 32 * Q + (lane >> 5) * 16 * Q + q * 16;
     *(uint4*)(dst + c * 16) = *(const uint4*)(src + (e * rows_total + row) * row_bytes + byte);
 }
 
-hipError_t launch_prepack(int E, int H, int I, int esz, const void* w13, const void* w2, void* w13p,
+hipError_t launch_prepack(int E, int H, int I, int bits, const void* w13, const void* w2, void* w13p,
                           void* w2p, hipStream_t stream) {
-    // gate/up: rows [0,2I) of H*esz bytes; tiles of 128 intermediate columns;
-    // row set 0 = gate rows, 1 = up rows (I further on).
+    const int log2q = bits == 4 ? 1 : 2;        // quarters per lane and K-step: 2 (E2M1) or 4
+    const int step = 32 << log2q;               // weight bytes of a row per K-step
+    // gate/up: rows [0,2I) of H*bits/8 bytes; tiles of 128 intermediate
+    // columns; row set 0 = gate rows, 1 = up rows (I further on).
     {
-        const int64_t row_bytes = (int64_t)H * esz;
-        const int nk = (int)(row_bytes / kStepBytes), nN = I / 128;
-        const int64_t n = (int64_t)E * nN * nk * (kPackStepBytes / 16);
+        const int64_t row_bytes = (int64_t)H * bits / 8;
+        const int nk = (int)(row_bytes / step), nN = I / 128;
+        const int64_t n = (int64_t)E * nN * nk * 4 * 2 * (64 << log2q);
         hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                           (const uint8_t*)w13, (uint8_t*)w13p, n, nN, nk, (int64_t)2 * I, row_bytes, I, 128,
-                           32);
+                           (const uint8_t*)w13, (uint8_t*)w13p, n, nN, nk, log2q, (int64_t)2 * I, row_bytes, I,
+                           128, 32);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    // down: rows [0,H) of I*esz bytes; tiles of 256 output columns; a wave's
-    // two row sets are adjacent 32-row blocks.
+    // down: rows [0,H) of I*bits/8 bytes; tiles of 256 output columns; a
+    // wave's two row sets are adjacent 32-row blocks.
     {
-        const int64_t row_bytes = (int64_t)I * esz;
-        const int nk = (int)(row_bytes / kStepBytes), nN = H / 256;
-        const int64_t n = (int64_t)E * nN * nk * (kPackStepBytes / 16);
+        const int64_t row_bytes = (int64_t)I * bits / 8;
+        const int nk = (int)(row_bytes / step), nN = H / 256;
+        const int64_t n = (int64_t)E * nN * nk * 4 * 2 * (64 << log2q);
         hipLaunchKernelGGL(prepack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                           (const uint8_t*)w2, (uint8_t*)w2p, n, nN, nk, (int64_t)H, row_bytes, 32, 256, 64);
+                           (const uint8_t*)w2, (uint8_t*)w2p, n, nN, nk, log2q, (int64_t)H, row_bytes, 32, 256,
+                           64);
+    }
+    return hipGetLastError();
+}
+
+// E8M0 block scales [rows, nk*4] (nk K-steps of 128 elements) -> one 4-byte
+// word per (expert, N tile, K-step, wave, lane), walked in packed order: the
+// lane's two scale bytes of its half of the K-step for row set 0, then for
+// row set 1 (rows as in the weight packing).
+__global__ void __launch_bounds__(256)
+prepack_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nwords, int nN,
+                      int nk, int64_t rows_total, int ns_stride, int tile_rows, int wave_rows) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= nwords) return;
+    const int lane = (int)(c & 63);
+    const int w = (int)((c >> 6) & 3);
+    const int64_t rest = c >> 8;
+    const int k = (int)(rest % nk);
+    const int t = (int)((rest / nk) % nN);
+    const int64_t e = rest / ((int64_t)nk * nN);
+    const int64_t row0 = (int64_t)t * tile_rows + w * wave_rows + (lane & 31);
+    const int64_t byte = (int64_t)k * 4 + (lane >> 5) * 2;
+    const uint8_t* p0 = src + (e * rows_total + row0) * nk * 4 + byte;
+    const uint8_t* p1 = p0 + (int64_t)ns_stride * nk * 4;
+    *(uint32_t*)(dst + c * 4) = (uint32_t)p0[0] | ((uint32_t)p0[1] << 8) | ((uint32_t)p1[0] << 16) |
+                                ((uint32_t)p1[1] << 24);
+}
+
+hipError_t launch_prepack_scales(int E, int H, int I, const void* s13, const void* s2, void* s13p, void* s2p,
+                                 hipStream_t stream) {
+    {
+        const int nk = H / 128, nN = I / 128;
+        const int64_t n = (int64_t)E * nN * nk * (kPackScaleStepBytes / 4);
+        hipLaunchKernelGGL(prepack_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           (const uint8_t*)s13, (uint8_t*)s13p, n, nN, nk, (int64_t)2 * I, I, 128, 32);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    {
+        const int nk = I / 128, nN = H / 256;
+        const int64_t n = (int64_t)E * nN * nk * (kPackScaleStepBytes / 4);
+        hipLaunchKernelGGL(prepack_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           (const uint8_t*)s2, (uint8_t*)s2p, n, nN, nk, (int64_t)H, 32, 256, 64);
     }
     return hipGetLastError();
 }

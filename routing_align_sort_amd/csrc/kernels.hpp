@@ -43,15 +43,19 @@ struct FfnArgs {
     int64_t S, C;              // slots, capacity (rows of the sorted layout)
     const void* x;
     const void* w13;
-    const float* w13_scale;
+    const void* w13_scale;     // fp32 [E,2I] (E4M3) or E8M0 [E,2I,H/32] (E2M1); else unused
     const void* w2;
-    const float* w2_scale;
+    const void* w2_scale;      // fp32 [E,H] (E4M3) or E8M0 [E,H,I/32] (E2M1); else unused
     const int32_t* sorted_ids;
     const int32_t* expert_ids;
     const int32_t* post_padded;
     float* y_slots;
     int packed;                // weights in the layout written by launch_prepack
 };
+// Largest activation operand (bytes of x, or of the intermediate, as one
+// GEMM reads it) of the matrix-core kernels: they address it with 32-bit
+// offsets.
+constexpr int64_t kFfnMaxOperandBytes = (int64_t)1 << 32;
 // Workspace layout per dtype path (bytes, each region 256-byte aligned).
 int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C);
 // ev (nullable) = 5 caller-created events recorded at the stage boundaries:
@@ -59,11 +63,16 @@ int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_
 hipError_t launch_ffn_f32(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);
 hipError_t launch_ffn_bf16(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);
 hipError_t launch_ffn_fp8(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);
+hipError_t launch_ffn_fp4(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);
 
-// Rewrites canonical W13 [E,2I,H] and W2 [E,H,I] (esz bytes per element) into
-// the packed layout the MFMA kernels stream (same sizes).
-hipError_t launch_prepack(int E, int H, int I, int esz, const void* w13, const void* w2, void* w13p,
+// Rewrites canonical W13 [E,2I,H] and W2 [E,H,I] (bits per element: 16, 8
+// or 4) into the packed layout the MFMA kernels stream (same sizes).
+hipError_t launch_prepack(int E, int H, int I, int bits, const void* w13, const void* w2, void* w13p,
                           void* w2p, hipStream_t stream);
+// Rewrites canonical E8M0 block scales [E,2I,H/32] and [E,H,I/32] into the
+// packed order the E2M1 kernels stream (same sizes).
+hipError_t launch_prepack_scales(int E, int H, int I, const void* s13, const void* s2, void* s13p, void* s2p,
+                                 hipStream_t stream);
 
 inline hipError_t record_stage(hipEvent_t const* ev, int i, hipStream_t s) {
     return ev ? hipEventRecord(ev[i], s) : hipSuccess;

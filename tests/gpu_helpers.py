@@ -6,7 +6,7 @@ import moe_synth as ms
 import oracle
 import routing_align_sort_amd as moe
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 6e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 6e-2, "e2m1": 6e-2}
 
 
 def device():
@@ -30,13 +30,23 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu().contiguous()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
-    if t.dtype == torch.float8_e4m3fn:
+    if t.dtype in (torch.float8_e4m3fn, moe.FP4, moe.E8M0):
         return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
-ODT = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "e4m3"}
-INTER = {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3"}
+# the generator's MXFP4 weights are uint8 (code pairs); the binding views them
+# as float4_e2m1fn_x2 with float8_e8m0fnu scales
+ODT = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float8_e4m3fn: "e4m3", torch.uint8: "e2m1"}
+INTER = {"f32": "f32", "bf16": "bf16", "e4m3": "e4m3", "e2m1": "e4m3"}
+
+
+def as_library_weights(L):
+    """(w13, w2, w13_scale, w2_scale) of a generated layer in the binding's dtypes."""
+    w13, w2, s13, s2 = L["w13"], L["w2"], L.get("w13_scale"), L.get("w2_scale")
+    if w13.dtype == torch.uint8:
+        return w13.view(moe.FP4), w2.view(moe.FP4), s13.view(moe.E8M0), s2.view(moe.E8M0)
+    return w13, w2, s13, s2
 
 
 def oracle_tokens(x, w13, w2, ids, w, toks, w13_scale=None, w2_scale=None):
@@ -79,9 +89,10 @@ def route_oracle(cfg, L, K=None):
 
 
 def make_gpu_layer(cfg, L, B=None, packed=None):
-    return moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B or cfg["B"], packed=packed,
+    w13, w2, s13, s2 = as_library_weights(L)
+    return moe.MoELayer(w13, w2, T=cfg["T"], K=cfg["K"], B=B or cfg["B"], packed=packed,
                         score=cfg["score"], n_group=cfg["n_group"], topk_group=cfg["topk_group"],
                         renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
-                        w13_scale=L.get("w13_scale"), w2_scale=L.get("w2_scale"),
+                        w13_scale=s13, w2_scale=s2,
                         x_dtype=L["x"].dtype,
                         out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16)

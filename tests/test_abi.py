@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -115,3 +115,44 @@ def test_ffn_validation_and_workspace(lib):
     assert lib.moe_combine(4, 2, 8, 6, P(8), P(8), P(8), 1, P(8), None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(4, 2, 8, 8, P(8), P(8), P(8), 7, P(8), None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(0, 2, 8, 8, None, None, None, 1, None, None) == moe.MOE_OK
+
+
+def test_mxfp4_validation(lib):
+    import torch
+    P = ctypes.c_void_p
+    # E2M1 weights take bf16 activations and the fp8 workspace layout
+    ws4 = moe.moe_grouped_ffn_workspace_bytes(64, 8, 256, 7168, 2048, 16, moe.FP4, torch.bfloat16)
+    ws8 = moe.moe_grouped_ffn_workspace_bytes(64, 8, 256, 7168, 2048, 16, torch.float8_e4m3fn,
+                                              torch.bfloat16)
+    assert ws4 == ws8
+    p = moe._FfnParams(64, 2, 8, 256, 256, 16, moe.MOE_FP4_E2M1, moe.MOE_BF16, 0)
+    st = lib.moe_grouped_ffn(ctypes.byref(p), P(8), P(8), None, P(8), P(8), P(8), P(8), P(8), P(8),
+                             P(8), 1 << 30, None)
+    assert st == moe.MOE_ERR_INVALID_ARG        # block scales are required
+    p.x_dtype = moe.MOE_FP4_E2M1
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1
+    # block-scale packing: only for E2M1, sizes as for the weights, no aliasing
+    f = moe._FfnParams(1, 1, 8, 256, 256, 16, moe.MOE_FP8_E4M3, moe.MOE_BF16, 1)
+    assert lib.moe_prepack_block_scales(ctypes.byref(f), P(8), P(8), P(16), P(24), None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    f.w_dtype = moe.MOE_FP4_E2M1; f.I = 192
+    assert lib.moe_prepack_block_scales(ctypes.byref(f), P(8), P(8), P(16), P(24), None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    f.I = 256
+    assert lib.moe_prepack_block_scales(ctypes.byref(f), P(8), P(8), P(8), P(24), None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_prepack_block_scales(ctypes.byref(f), None, P(8), P(16), P(24), None) == \
+        moe.MOE_ERR_INVALID_ARG
+
+
+def test_activation_operand_limit(lib):
+    import torch
+    # x of 2^20 tokens x 2048 bf16 = 4 GiB fits; one more token does not
+    assert moe.moe_grouped_ffn_workspace_bytes(1 << 20, 1, 8, 2048, 128, 16, torch.bfloat16,
+                                               torch.bfloat16) > 0
+    with pytest.raises(moe.MoEError):
+        moe.moe_grouped_ffn_workspace_bytes((1 << 20) + 1, 1, 8, 2048, 128, 16, torch.bfloat16,
+                                            torch.bfloat16)
+    # the quantised paths read one byte per element
+    assert moe.moe_grouped_ffn_workspace_bytes((1 << 20) + 1, 1, 8, 2048, 128, 16,
+                                               torch.float8_e4m3fn, torch.bfloat16) > 0

@@ -1,7 +1,8 @@
 """The grouped FFN and the whole layer (route -> align -> FFN -> combine) on the
 GPU against the oracle: max|gpu - oracle| <= tol * max|oracle| with tol 1e-4
-(fp32), 2e-2 (bf16), 6e-2 (fp8); full-size workloads are compared on a seeded
-sample of tokens, small ones on every token."""
+(fp32), 2e-2 (bf16), 6e-2 (fp8 and MXFP4 weights, both with fp8 activations);
+full-size workloads are compared on a seeded sample of tokens, small ones on
+every token."""
 import numpy as np
 import pytest
 import torch
@@ -68,11 +69,27 @@ def test_layer_small_fp8_all_tokens(B):
     check_layer(cfg, L, np.arange(cfg["T"]), B=B, label=f"small fp8 B={B}")
 
 
+@pytest.mark.parametrize("B", [16, 32, 64, 128, 256])
+def test_layer_small_mxfp4_all_tokens(B):
+    dev = device()
+    cfg = ms.scaled("prefill_fp4", T=333, H=768, I=384, E=12)
+    L = ms.make_layer(cfg, device=dev)
+    check_layer(cfg, L, np.arange(cfg["T"]), B=B, label=f"small mxfp4 B={B}")
+
+
+def test_layer_small_mxfp4_grouped_sigmoid():
+    dev = device()
+    cfg = ms.scaled("decode_fp4", T=96, H=512, I=256, E=16, K=4, n_group=4, topk_group=2)
+    L = ms.make_layer(cfg, device=dev)
+    for B in (16, 32):
+        check_layer(cfg, L, np.arange(cfg["T"]), B=B, label=f"small mxfp4 decode B={B}")
+
+
 def test_ffn_output_is_block_size_invariant():
     dev = device()
-    for name in ("decode_bf16", "prefill_fp8"):
+    for name in ("decode_bf16", "prefill_fp8", "prefill_fp4"):
         cfg = ms.scaled(name, T=200, H=256, I=256, E=8, K=2, n_group=2, topk_group=2)
-        if name == "prefill_fp8":
+        if name != "decode_bf16":
             cfg = ms.scaled(name, T=200, H=256, I=256, E=8)
         L = ms.make_layer(cfg, device=dev)
         ys = []
@@ -85,7 +102,7 @@ def test_ffn_output_is_block_size_invariant():
 
 def test_packed_weights_give_identical_results():
     dev = device()
-    for name in ("decode_bf16", "prefill_fp8"):
+    for name in ("decode_bf16", "prefill_fp8", "prefill_fp4"):
         over = dict(T=150, H=512, I=256, E=6)
         if name == "decode_bf16":
             over.update(K=3, n_group=2, topk_group=2)
@@ -130,6 +147,11 @@ def test_generator_device_matches_host():
     cfg = ms.scaled("decode_bf16", H=256, I=128, E=2)
     assert torch.equal(ms.make_layer(cfg, device=dev)["x"].cpu().view(torch.int16),
                        ms.make_layer(cfg, device="cpu")["x"].view(torch.int16))
+    cfg = ms.scaled("prefill_fp4", H=256, I=128, E=3)
+    g = ms.make_weights(cfg, device=dev)
+    h = ms.make_weights(cfg, device="cpu")
+    for k in ("w13", "w2", "w13_scale", "w2_scale"):
+        assert torch.equal(g[k].cpu(), h[k]), k
 
 
 # ----------------------------------------------------------- full-size shapes --
@@ -166,5 +188,27 @@ def test_layer_prefill_fp8_full_size():
     L = ms.make_layer(cfg, device=dev)
     for B in (32, 64, 128):
         check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill fp8 B={B}")
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_layer_decode_mxfp4_full_size():
+    dev = device()
+    cfg = ms.CONFIGS["decode_fp4"]
+    say("generating DeepSeek-V3-shaped MXFP4 decode weights (256 experts, 5.6 GB)")
+    L = ms.make_layer(cfg, device=dev)
+    for B in (16, 32):
+        check_layer(cfg, L, sample_tokens(cfg["T"], 8, B), B=B, label=f"decode mxfp4 B={B}")
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_layer_prefill_mxfp4_full_size():
+    dev = device()
+    cfg = ms.CONFIGS["prefill_fp4"]
+    say("generating prefill MXFP4 weights (32 experts, 0.7 GB)")
+    L = ms.make_layer(cfg, device=dev)
+    for B in (32, 64, 128):
+        check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill mxfp4 B={B}")
     del L
     torch.cuda.empty_cache()
