@@ -28,9 +28,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0                                   # MI355X HBM3E
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
-ESZ = {"f32": 4, "bf16": 2, "e4m3": 1}
-DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "e4m3": "fp8_e4m3"}
+# dense matrix-core peaks; E4M3 x E2M1 products run on the f8f6f4 instruction
+# with an E4M3 operand and are priced at the fp8 peak
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "e2m1": 5000.0, "f32": 157.3}
+ESZ = {"f32": 4, "bf16": 2, "e4m3": 1, "e2m1": 0.5}
+DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "e4m3": "fp8_e4m3", "e2m1": "fp8_e4m3 x mxfp4"}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -43,7 +45,8 @@ def layer_flops(slots: int, hidden: int, inter: int) -> int:
 
 def algorithmic_bytes(cfg, ids_np, E_slabs):
     """Bytes the method itself must move per kernel (each counted once):
-    gate/up: W13 of every expert hit (+ its fp32 row scales) and x;
+    gate/up: W13 of every expert hit (+ its fp32 row scales, or its E8M0
+    block scales: one byte per 32 weights) and x;
     down: W2 of every expert hit (+ scales) and the fp32 y_slots rows written;
     combine: y_slots read, out written (bf16 / fp32)."""
     import numpy as np
@@ -55,14 +58,16 @@ def algorithmic_bytes(cfg, ids_np, E_slabs):
     D = int(hit.size)
     S_valid = int(((flat >= 0) & (flat < E_slabs)).sum())
     xb = T * H * (4 if dt == "f32" else 2)
-    sc = 4 if dt == "e4m3" else 0
+    # scale bytes per weight row of W13 (H long) and of W2 (I long)
+    sc1 = 4 if dt == "e4m3" else H // 32 if dt == "e2m1" else 0
+    sc2 = 4 if dt == "e4m3" else I // 32 if dt == "e2m1" else 0
     out_b = T * H * (4 if dt == "f32" else 2)
     return {
         "experts_hit": D,
-        "stage1": D * 2 * I * H * e + D * 2 * I * sc + xb,
-        "stage2": D * H * I * e + D * H * sc + S_valid * H * 4,
+        "stage1": int(D * 2 * I * H * e) + D * 2 * I * sc1 + xb,
+        "stage2": int(D * H * I * e) + D * H * sc2 + S_valid * H * 4,
         "combine": S_valid * H * 4 + out_b,
-        "weights": D * 3 * I * H * e,
+        "weights": int(D * 3 * I * H * e) + D * (2 * I * sc1 + H * sc2),
         "slots": S_valid,
     }
 
@@ -80,10 +85,13 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
     import routing_align_sort_amd as moe
 
     L = ms.make_layer(cfg, device=dev, seed=seed)
-    layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"],
+    w13, w2, s13, s2 = L["w13"], L["w2"], L.get("w13_scale"), L.get("w2_scale")
+    if cfg["dtype"] == "e2m1":          # generator bytes -> the binding's MXFP4 dtypes
+        w13, w2, s13, s2 = w13.view(moe.FP4), w2.view(moe.FP4), s13.view(moe.E8M0), s2.view(moe.E8M0)
+    layer = moe.MoELayer(w13, w2, T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"],
                          n_group=cfg["n_group"], topk_group=cfg["topk_group"],
                          renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
-                         w13_scale=L.get("w13_scale"), w2_scale=L.get("w2_scale"),
+                         w13_scale=s13, w2_scale=s2,
                          x_dtype=L["x"].dtype,
                          out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16)
     x, logits, bias = L["x"], L["logits"], L["bias"]
@@ -351,7 +359,8 @@ def main():
         # the HBM-bound secondary shapes at their own block size; the
         # compute-bound 512-tokens-per-expert shapes at block 128
         for name, b2 in (("prefill_fp8", None), ("decode_bf16", None), ("prefill_bf16_512", 128),
-                         ("prefill_fp8_512", 128)):
+                         ("prefill_fp8_512", 128), ("decode_fp4", None), ("prefill_fp4", None),
+                         ("prefill_fp4_512", 128)):
             if name == args.workload:
                 continue
             c2 = ms.CONFIGS[name]
@@ -470,20 +479,22 @@ def mfma_probe(dev, reps=5):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     ev = moe.HipEvents(2 * reps)
     res = {}
-    for name, fp8, k in (("bf16", 0, 16), ("fp8", 1, 64)):
+    # (name, probe kind, K of the instruction, published dense peak in TFLOP/s)
+    for name, kind, k, peak in (("bf16", 0, 16, 2500.0), ("fp8", 1, 64, 5000.0),
+                                ("fp8_x_fp4", 2, 64, 5000.0), ("fp4", 3, 64, 10100.0)):
         flops = blocks * 4 * iters * 8 * 2 * 32 * 32 * k
-        lib.moe_probe_mfma(fp8, ctypes.c_void_p(out.data_ptr()), blocks, iters, stream)
+        lib.moe_probe_mfma(kind, ctypes.c_void_p(out.data_ptr()), blocks, iters, stream)
         torch.cuda.synchronize()
         for i in range(reps):
             ev.record(2 * i)
-            if lib.moe_probe_mfma(fp8, ctypes.c_void_p(out.data_ptr()), blocks, iters, stream) != 0:
+            if lib.moe_probe_mfma(kind, ctypes.c_void_p(out.data_ptr()), blocks, iters, stream) != 0:
                 raise RuntimeError("probe launch failed")
             ev.record(2 * i + 1)
         torch.cuda.synchronize()
         best = min(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)) * 1e-3
         tf = flops / best / 1e12
         res[name + "_tflops"] = round(tf, 1)
-        res[name + "_frac_of_peak"] = round(tf / MFMA_PEAK_TFLOPS["bf16" if name == "bf16" else "e4m3"], 4)
+        res[name + "_frac_of_peak"] = round(tf / peak, 4)
     ev.close()
     return res
 
@@ -615,7 +626,8 @@ def run_cpu_baseline(cfg, B, dev, budget_s=12.0):
     def ffn(toks):
         t1 = time.perf_counter()
         oracle.moe_layer(xh[toks], w13, w2, ids[toks], w[toks], w_dtype=wdt, x_dtype=xdt,
-                         inter=wdt, w13_scale=s13, w2_scale=s2, E=E_slabs)
+                         inter="e4m3" if wdt == "e2m1" else wdt, w13_scale=s13, w2_scale=s2,
+                         E=E_slabs)
         return time.perf_counter() - t1
 
     n0 = int(min(T, 4 * oracle.num_threads()))   # enough tokens to occupy every oracle thread

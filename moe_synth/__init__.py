@@ -235,6 +235,9 @@ CONFIGS = {
     "prefill_fp4": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e2m1", score="softmax",
                         bias=False, n_group=1, topk_group=1, renormalize=False,
                         routing="uniform", B=64),
+    "prefill_fp4_512": dict(T=2048, H=7168, I=2048, E=32, K=8, dtype="e2m1", score="softmax",
+                            bias=False, n_group=1, topk_group=1, renormalize=True,
+                            routing="uniform8", B=128),
 }
 
 ROUTER_SIGMA = 0.02

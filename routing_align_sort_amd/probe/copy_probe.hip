@@ -48,10 +48,11 @@ extern "C" int moe_probe_read(const void* src, void* out, size_t bytes, void* st
 }
 
 // Matrix-core throughput with no memory traffic: every wave runs `iters`
-// rounds of 8 independent 32x32 MFMA accumulation chains (bf16 32x32x16, or
-// fp8 32x32x64 with unit scales) on register operands, then folds the
-// accumulators into one word per wave so the work cannot be dropped.
-template <bool kFp8>
+// rounds of 8 independent 32x32 MFMA accumulation chains on register
+// operands (kind 0: bf16 32x32x16; 1: E4M3 x E4M3, 2: E4M3 x E2M1, 3: E2M1 x
+// E2M1, each 32x32x64 with unit scales), then folds the accumulators into one
+// word per wave so the work cannot be dropped.
+template <int kKind>
 __global__ void __launch_bounds__(256) mfma_probe_kernel(float* __restrict__ out, int iters) {
     typedef float f32x16 __attribute__((ext_vector_type(16)));
     typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -60,13 +61,17 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(float* __restrict__ out
     for (int c = 0; c < 8; ++c)
         for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
     const int lane = threadIdx.x & 63;
-    if constexpr (kFp8) {
+    if constexpr (kKind > 0) {
+        constexpr int ta = kKind == 3 ? 4 : 0;
+        constexpr int tb = kKind >= 2 ? 4 : 0;
         i32x8 a, b;
         for (int i = 0; i < 8; ++i) { a[i] = 0x38383838 ^ (lane + i); b[i] = 0x30303030 ^ (lane * 3 + i); }
+        if (ta == 4) for (int i = 4; i < 8; ++i) a[i] = 0;
+        if (tb == 4) for (int i = 4; i < 8; ++i) b[i] = 0;
         for (int it = 0; it < iters; ++it)
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 0, 0, 0, 127, 0, 127);
+                acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], ta, tb, 0, 127, 0, 127);
     } else {
         bf16x8 a, b;
         for (int i = 0; i < 8; ++i) { a[i] = (__bf16)(0.001f * (lane + i)); b[i] = (__bf16)(0.002f * (lane - i)); }
@@ -80,13 +85,16 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(float* __restrict__ out
     if (lane == 0) out[blockIdx.x * 4 + threadIdx.x / 64] = s;
 }
 
-// FLOPs per launch = blocks * 4 waves * iters * 8 * (2*32*32*K), K = 16 (bf16) or 64 (fp8).
-extern "C" int moe_probe_mfma(int fp8, float* out, int blocks, int iters, void* stream) {
+// FLOPs per launch = blocks * 4 waves * iters * 8 * (2*32*32*K), K = 16 (bf16) or 64.
+extern "C" int moe_probe_mfma(int kind, float* out, int blocks, int iters, void* stream) {
     if (!out || blocks <= 0 || iters <= 0) return 1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (fp8)
-        hipLaunchKernelGGL(mfma_probe_kernel<true>, dim3(blocks), dim3(256), 0, s, out, iters);
-    else
-        hipLaunchKernelGGL(mfma_probe_kernel<false>, dim3(blocks), dim3(256), 0, s, out, iters);
+    switch (kind) {
+        case 0: hipLaunchKernelGGL(mfma_probe_kernel<0>, dim3(blocks), dim3(256), 0, s, out, iters); break;
+        case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3(blocks), dim3(256), 0, s, out, iters); break;
+        case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, dim3(blocks), dim3(256), 0, s, out, iters); break;
+        case 3: hipLaunchKernelGGL(mfma_probe_kernel<3>, dim3(blocks), dim3(256), 0, s, out, iters); break;
+        default: return 1;
+    }
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
