@@ -78,6 +78,12 @@ def _load():
     lib.oracle_expert_ffn.restype = i32
     lib.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
     lib.oracle_combine.restype = i32
+    lib.oracle_permute_rows.argtypes = [P, i32, i64, i32, P, i64, P]
+    lib.oracle_permute_rows.restype = i32
+    lib.oracle_row_of_slot.argtypes = [P, i64, i64, P]
+    lib.oracle_row_of_slot.restype = i32
+    lib.oracle_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, P]
+    lib.oracle_unpermute_combine.restype = i32
     lib.oracle_num_threads.restype = i32
     _lib = lib
     return lib
@@ -278,3 +284,42 @@ def moe_layer(x, w13, w2, topk_ids, topk_weights, *, w_dtype, x_dtype, inter,
     y = expert_ffn(x, w13, w2, topk_ids, w_dtype=w_dtype, x_dtype=x_dtype, inter=inter,
                    w13_scale=w13_scale, w2_scale=w2_scale)
     return combine(y, topk_weights, topk_ids, E), y
+
+
+def permute_rows(x, sorted_ids, K: int):
+    """Rows of x (any dtype, [T, ...]) moved into the padded expert order:
+    row r is x[sorted_ids[r] // K] where sorted_ids[r] < T*K, else zeros."""
+    xa = np.ascontiguousarray(x)
+    T = xa.shape[0]
+    row_bytes = xa.dtype.itemsize * (int(np.prod(xa.shape[1:])) if xa.ndim > 1 else 1)
+    srt = _c(sorted_ids, np.int32)
+    C = srt.shape[0]
+    out = np.empty((C,) + xa.shape[1:], xa.dtype)
+    rc = _load().oracle_permute_rows(_ptr(xa), T, row_bytes, K, _ptr(srt), C, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_permute_rows: invalid arguments")
+    return out
+
+
+def row_of_slot(sorted_ids, S: int):
+    """Inverse of the padded layout: the row holding each slot, -1 if none."""
+    srt = _c(sorted_ids, np.int32)
+    out = np.empty(S, np.int32)
+    rc = _load().oracle_row_of_slot(_ptr(srt), srt.shape[0], S, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_row_of_slot: invalid arguments")
+    return out
+
+
+def unpermute_combine(y_perm, topk_weights, row_of_slot_):
+    """out[t] = sum_k w[t,k] * y_perm[row_of_slot[t*K+k]] (double, ascending k, -1 skipped)."""
+    y = _c(y_perm, np.float32)
+    w = _c(topk_weights, np.float32)
+    rs = _c(row_of_slot_, np.int32)
+    T, K = w.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.float64)
+    rc = _load().oracle_unpermute_combine(T, K, H, _ptr(y), _ptr(w), _ptr(rs), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_unpermute_combine: invalid arguments")
+    return out

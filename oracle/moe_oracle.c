@@ -502,3 +502,62 @@ int oracle_combine(int T, int K, int E, int H, const float *y_slots,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Permute / unpermute around the grouped FFN                                */
+/* ------------------------------------------------------------------------ */
+/*
+ * [DIG] opening paragraphs, the TransformerEngine paragraph and its "MoE
+ * Permute example" figure: besides ordering token slots by expert, a permute
+ * step moves the rows and records where each source row went; the reverse
+ * movement (unpermute) is its gradient.  [GCM] abstract: under expert
+ * parallelism a layer pays a token dispatch, the grouped GEMMs and a combine.
+ * Reading: the destination order is Align & Sort's padded layout, so every
+ * expert's rows are contiguous (one contiguous send range per destination
+ * GPU); padding rows are zero.
+ *   x_perm[r]      = x[sorted[r] / K]   (r < C, sorted[r] < S), else zeros
+ *   row_of_slot[i] = the r with sorted[r] = i, or -1 if slot i is not placed
+ *   out[t]         = sum over k ascending of w[t,k] * y_perm[row_of_slot[t*K+k]],
+ *                    slots with row -1 skipped, in double
+ */
+int oracle_permute_rows(const uint8_t *x, int T, int64_t row_bytes, int K, const int32_t *sorted,
+                        int64_t C, uint8_t *x_perm)
+{
+    if (T < 0 || K < 1 || row_bytes < 0 || C < 0) return 1;
+    int64_t S = (int64_t)T * K;
+    for (int64_t r = 0; r < C; r++) {
+        uint8_t *dst = x_perm + r * row_bytes;
+        if (sorted[r] >= 0 && sorted[r] < S)
+            memcpy(dst, x + (int64_t)(sorted[r] / K) * row_bytes, (size_t)row_bytes);
+        else
+            memset(dst, 0, (size_t)row_bytes);
+    }
+    return 0;
+}
+
+int oracle_row_of_slot(const int32_t *sorted, int64_t C, int64_t S, int32_t *row_of_slot)
+{
+    if (C < 0 || S < 0) return 1;
+    for (int64_t i = 0; i < S; i++) row_of_slot[i] = -1;
+    for (int64_t r = 0; r < C; r++)
+        if (sorted[r] >= 0 && sorted[r] < S) row_of_slot[sorted[r]] = (int32_t)r;
+    return 0;
+}
+
+int oracle_unpermute_combine(int T, int K, int H, const float *y_perm, const float *topk_weights,
+                             const int32_t *row_of_slot, double *out)
+{
+    if (T < 0 || K < 1 || H < 1) return 1;
+    for (int t = 0; t < T; t++)
+        for (int h = 0; h < H; h++) {
+            double acc = 0.0;
+            for (int k = 0; k < K; k++) {
+                int64_t i = (int64_t)t * K + k;
+                int32_t r = row_of_slot[i];
+                if (r < 0) continue;
+                acc += (double)topk_weights[i] * (double)y_perm[(int64_t)r * H + h];
+            }
+            out[(size_t)t * H + h] = acc;
+        }
+    return 0;
+}
