@@ -10,6 +10,13 @@
  *   moe_grouped_ffn  x, expert weights, the sorted layout -> y_slots [T*K, H]
  *   moe_combine      y_slots, topk weights   -> out [T,H]
  *
+ * or, with the rows moved into the sorted order first (the layout a
+ * dispatch to expert-owning GPUs sends):
+ *
+ *   moe_permute_rows       x, the sorted layout -> x_perm [C,H], row_of_slot
+ *   moe_grouped_ffn        (row_layout MOE_ROWS_SORTED) x_perm -> y_perm [C,H]
+ *   moe_unpermute_combine  y_perm, row_of_slot, topk weights -> out [T,H]
+ *
  * Conventions shared by every call
  * --------------------------------
  * - Pointers named as device pointers must point to device memory of the
@@ -43,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
@@ -185,12 +192,22 @@ moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32
  * MOE_ERR_UNSUPPORTED.
  */
 typedef enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layout_t;
+/*
+ * row_layout MOE_ROWS_BY_TOKEN: x is [T,H] and is gathered through
+ * sorted_token_ids; y_slots is [T*K,H] by slot.  MOE_ROWS_SORTED (the
+ * receiving side of an expert-parallel dispatch): x is [C,H] already in the
+ * sorted order (as moe_permute_rows writes it: row r holds the token of slot
+ * sorted_token_ids[r]) and y_slots is [C,H] in the same order, row r written
+ * only where sorted_token_ids[r] < T*K.  Not for fp32.
+ */
+typedef enum { MOE_ROWS_BY_TOKEN = 0, MOE_ROWS_SORTED = 1 } moe_row_layout_t;
 
 typedef struct {
     int32_t T, K, E, H, I, B;
     int32_t w_dtype;           /* moe_dtype_t */
     int32_t x_dtype;           /* moe_dtype_t */
     int32_t weight_layout;     /* moe_weight_layout_t of w13 and w2 */
+    int32_t row_layout;        /* moe_row_layout_t of x and y_slots */
 } moe_ffn_params_t;
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);
@@ -256,6 +273,44 @@ moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t *p, const void *x, 
 moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float *y_slots,
                          const float *topk_weights, const int32_t *topk_ids, int32_t out_dtype,
                          void *out, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Permute / unpermute (the dispatch-side data movement)                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * Defined by the dignews.cc page, opening paragraphs: the TransformerEngine
+ * paragraph and its "MoE Permute example" figure (a permute moves the rows
+ * into expert order and records where each source row went; unpermute is the
+ * reverse), and the GC-MoE abstract (expert parallelism pays a token
+ * dispatch, the grouped GEMMs and a combine).  The destination order is
+ * moe_align_sort's padded layout, so each expert's rows -- and each
+ * destination GPU's range of experts -- are contiguous.
+ *
+ * moe_permute_rows, for r < C = moe_align_sort_capacity(T,K,E,B):
+ *   x_perm[r] = x[sorted_token_ids[r] / K] if sorted_token_ids[r] < T*K,
+ *               else a zero row;
+ *   x_perm_scale[r] = x_scale[that token] or 0 (both NULL to skip);
+ *   row_of_slot[i] = r with sorted_token_ids[r] = i, or -1 when topk_ids[i]
+ *   is outside [0,E) (i < T*K).
+ * x device [T, row_bytes] (any element type, row_bytes > 0 and a multiple of
+ * 16); topk_ids and sorted_token_ids as given to / produced by moe_align_sort
+ * with the same T,K,E,B; x_perm device [C, row_bytes]; x_scale device fp32
+ * [T]; x_perm_scale device fp32 [C]; row_of_slot device int32 [T*K].
+ *
+ * moe_unpermute_combine: out[t,h] = sum over k = 0..K-1 in ascending order,
+ * skipping row_of_slot[t*K+k] < 0, of topk_weights[t,k] * y_perm[row, h] in
+ * fp32 -- the same arithmetic as moe_combine, so on y_perm[r] =
+ * y_slots[sorted_token_ids[r]] both give the same bits.  y_perm device fp32
+ * [C,H]; out device [T,H] in out_dtype (MOE_F32 or MOE_BF16).  Limits: H a
+ * multiple of 4.
+ */
+moe_status_t moe_permute_rows(const void *x, int32_t T, int32_t K, int32_t E, int32_t B,
+                              int64_t row_bytes, const int32_t *topk_ids,
+                              const int32_t *sorted_token_ids, const float *x_scale, void *x_perm,
+                              float *x_perm_scale, int32_t *row_of_slot, void *stream);
+moe_status_t moe_unpermute_combine(int32_t T, int32_t K, int32_t H, const float *y_perm,
+                                   const float *topk_weights, const int32_t *row_of_slot,
+                                   int32_t out_dtype, void *out, void *stream);
 
 #ifdef __cplusplus
 }

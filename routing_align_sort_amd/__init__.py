@@ -40,13 +40,13 @@ class _FfnParams(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("B", ctypes.c_int32),
                 ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("row_layout", ctypes.c_int32)]
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
             "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_prepack_weights",
-            "moe_prepack_block_scales", "moe_combine")
+            "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine")
 
 
 def load_library(path: str = LIB_PATH):
@@ -82,6 +82,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_prepack_block_scales.restype = i32
     lib.moe_combine.argtypes = [i32, i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_combine.restype = i32
+    lib.moe_permute_rows.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, P, P, P, P]
+    lib.moe_permute_rows.restype = i32
+    lib.moe_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, i32, P, P]
+    lib.moe_unpermute_combine.restype = i32
     _lib = lib
     return lib
 
@@ -206,11 +210,13 @@ def weight_dims(w13):
 
 
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PACKED = 0, 1
+MOE_ROWS_BY_TOKEN, MOE_ROWS_SORTED = 0, 1
 
 
-def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False):
+def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False, rows_sorted=False):
     return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype],
-                      MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_CANONICAL)
+                      MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_CANONICAL,
+                      MOE_ROWS_SORTED if rows_sorted else MOE_ROWS_BY_TOKEN)
 
 
 def moe_prepack_weights(w13, w2, *, stream=None):
@@ -243,8 +249,8 @@ def moe_prepack_block_scales(w13_scale, w2_scale, H, I, *, stream=None):
     return p13, p2
 
 
-def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype) -> int:
-    p = _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype)
+def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype, rows_sorted=False) -> int:
+    p = _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, rows_sorted=rows_sorted)
     c = int(load_library().moe_grouped_ffn_workspace_bytes(ctypes.byref(p)))
     if c < 0:
         raise MoEError("moe_grouped_ffn_workspace_bytes", MOE_ERR_UNSUPPORTED)
@@ -253,13 +259,19 @@ def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype) -> int:
 
 def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, *, K, B,
                     w13_scale=None, w2_scale=None, y_slots=None, workspace=None, stream=None,
-                    stage_events=None, packed=False):
+                    stage_events=None, packed=False, T=None):
     """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots fp32 [T*K, H].
 
+    With ``T`` given and x of C = capacity rows, x is taken in the sorted row
+    order (as moe_permute_rows writes it) and the result is [C, H] in that
+    order (row layout MOE_ROWS_SORTED).
     stage_events: optional 5 raw hipEvent_t handles (ints) recorded at the stage
     boundaries (the profiling entry point)."""
     lib = load_library()
-    T, H = x.shape
+    rows_sorted = T is not None
+    Tx, H = x.shape
+    if not rows_sorted:
+        T = Tx
     E, I, H2 = weight_dims(w13)
     fp4 = w13.dtype == FP4
     if H2 != H or tuple(w2.shape) != (E, H, I // 2 if fp4 else I):
@@ -276,11 +288,16 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     if fp4:
         _need(w13_scale, E8M0, "w13_scale", E * 2 * I * (H // 32))
         _need(w2_scale, E8M0, "w2_scale", E * H * (I // 32))
+    ny = T * K
+    if rows_sorted:
+        ny = moe_align_sort_capacity(T, K, E, B)
+        if Tx != ny:
+            raise ValueError(f"x in the sorted row order must have {ny} rows, got {Tx}")
     if y_slots is None:
-        y_slots = torch.empty((T * K, H), dtype=torch.float32, device=x.device)
-    _need(y_slots, torch.float32, "y_slots", T * K * H)
-    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed)
-    need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype)
+        y_slots = torch.empty((ny, H), dtype=torch.float32, device=x.device)
+    _need(y_slots, torch.float32, "y_slots", ny * H)
+    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed, rows_sorted)
+    need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype, rows_sorted)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -314,17 +331,71 @@ def moe_combine(y_slots, topk_weights, topk_ids, E, *, out_dtype=torch.bfloat16,
     return out
 
 
+# ------------------------------------------------------- permute/unpermute --
+def moe_permute_rows(x, topk_ids, sorted_token_ids, E, B, *, x_scale=None, x_perm=None,
+                     x_perm_scale=None, row_of_slot=None, stream=None):
+    """Rows of x [T, ...] moved into the padded expert order of moe_align_sort:
+    returns (x_perm [C, ...], row_of_slot int32 [T*K], x_perm_scale or None)."""
+    lib = load_library()
+    T, K = topk_ids.shape
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(x, x.dtype, "x")
+    if x.shape[0] != T:
+        raise ValueError("x and topk_ids disagree on the token count")
+    C = moe_align_sort_capacity(T, K, E, B)
+    _need(sorted_token_ids, torch.int32, "sorted_token_ids", C)
+    row_bytes = x[0].numel() * x.element_size() if T > 0 else 16
+    if x_perm is None:
+        x_perm = torch.empty((C,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    _need(x_perm, x.dtype, "x_perm", C * x[0].numel() if T > 0 else None)
+    if row_of_slot is None:
+        row_of_slot = torch.empty(T * K, dtype=torch.int32, device=x.device)
+    _need(row_of_slot, torch.int32, "row_of_slot", T * K)
+    if x_scale is not None:
+        _need(x_scale, torch.float32, "x_scale", T)
+        if x_perm_scale is None:
+            x_perm_scale = torch.empty(C, dtype=torch.float32, device=x.device)
+        _need(x_perm_scale, torch.float32, "x_perm_scale", C)
+    _check("moe_permute_rows", lib.moe_permute_rows(
+        _ptr(x), T, K, E, B, row_bytes, _ptr(topk_ids), _ptr(sorted_token_ids), _ptr(x_scale),
+        _ptr(x_perm), _ptr(x_perm_scale if x_scale is not None else None), _ptr(row_of_slot),
+        _stream(stream)))
+    return x_perm, row_of_slot, (x_perm_scale if x_scale is not None else None)
+
+
+def moe_unpermute_combine(y_perm, topk_weights, row_of_slot, *, out_dtype=torch.bfloat16, out=None,
+                          stream=None):
+    """out[t] = sum_k w[t,k] * y_perm[row_of_slot[t*K+k]] (ascending k, rows < 0 skipped)."""
+    lib = load_library()
+    T, K = topk_weights.shape
+    H = y_perm.shape[1]
+    _need(y_perm, torch.float32, "y_perm")
+    _need(topk_weights, torch.float32, "topk_weights", T * K)
+    _need(row_of_slot, torch.int32, "row_of_slot", T * K)
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
+    _need(out, out_dtype, "out", T * H)
+    _check("moe_unpermute_combine", lib.moe_unpermute_combine(
+        T, K, H, _ptr(y_perm), _ptr(topk_weights), _ptr(row_of_slot), _DT[out_dtype], _ptr(out),
+        _stream(stream)))
+    return out
+
+
 # -------------------------------------------------------------- the layer --
 class MoELayer:
     """The four calls of one MoE layer over preallocated buffers.
 
     Holds the weights and every intermediate buffer so that ``forward`` only
     enqueues the four library calls (route -> align -> grouped FFN -> combine).
+    With rows="sorted" the token rows are first moved into the sorted order
+    (permute), the FFN reads and writes that order, and the combine reads back
+    through the inverse map (route -> align -> permute -> FFN -> unpermute).
     """
 
     def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
-                 w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None):
+                 w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None,
+                 rows="by_token"):
         dev = w13.device
         if packed is None:
             packed = w13.dtype != torch.float32
@@ -352,12 +423,19 @@ class MoELayer:
         self.expert_ids = torch.empty(C // B, dtype=torch.int32, device=dev)
         self.ntpp = torch.empty(1, dtype=torch.int32, device=dev)
         self.offsets = torch.empty(self.E_slabs + 1, dtype=torch.int32, device=dev)
+        if rows not in ("by_token", "sorted"):
+            raise ValueError("rows must be 'by_token' or 'sorted'")
+        self.rows_sorted = rows == "sorted"
         ws_a = moe_align_sort_workspace_bytes(T, self.KO, self.E_slabs, B)
         ws_f = moe_grouped_ffn_workspace_bytes(T, self.KO, self.E_slabs, self.H, self.I, B,
-                                               w13.dtype, x_dtype)
+                                               w13.dtype, x_dtype, self.rows_sorted)
         self.ws_align = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty(max(ws_f, 1), dtype=torch.uint8, device=dev)
-        self.y_slots = torch.empty((T * self.KO, self.H), dtype=torch.float32, device=dev)
+        ny = C if self.rows_sorted else T * self.KO
+        self.y_slots = torch.empty((ny, self.H), dtype=torch.float32, device=dev)
+        if self.rows_sorted:
+            self.x_perm = torch.empty((C, self.H), dtype=x_dtype, device=dev)
+            self.row_of_slot = torch.empty(T * self.KO, dtype=torch.int32, device=dev)
         self.out = torch.empty((T, self.H), dtype=out_dtype, device=dev)
 
     def route(self, logits, bias=None):
@@ -369,19 +447,34 @@ class MoELayer:
                               expert_ids=self.expert_ids, num_tokens_post_padded=self.ntpp,
                               expert_offsets=self.offsets, workspace=self.ws_align)
 
+    def permute(self, x):
+        return moe_permute_rows(x, self.topk_ids, self.sorted, self.E_slabs, self.B,
+                                x_perm=self.x_perm, row_of_slot=self.row_of_slot)
+
     def ffn(self, x, stage_events=None):
+        if self.rows_sorted:
+            return moe_grouped_ffn(self.x_perm, self.w13, self.w2, self.sorted, self.expert_ids,
+                                   self.ntpp, K=self.KO, B=self.B, w13_scale=self.w13_scale,
+                                   w2_scale=self.w2_scale, y_slots=self.y_slots,
+                                   workspace=self.ws_ffn, stage_events=stage_events,
+                                   packed=self.packed, T=self.T)
         return moe_grouped_ffn(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
                                K=self.KO, B=self.B, w13_scale=self.w13_scale,
                                w2_scale=self.w2_scale, y_slots=self.y_slots, workspace=self.ws_ffn,
                                stage_events=stage_events, packed=self.packed)
 
     def combine(self):
+        if self.rows_sorted:
+            return moe_unpermute_combine(self.y_slots, self.topk_weights, self.row_of_slot,
+                                         out_dtype=self.out_dtype, out=self.out)
         return moe_combine(self.y_slots, self.topk_weights, self.topk_ids, self.E_slabs,
                            out_dtype=self.out_dtype, out=self.out)
 
     def forward(self, x, logits, bias=None):
         self.route(logits, bias)
         self.align()
+        if self.rows_sorted:
+            self.permute(x)
         self.ffn(x)
         return self.combine()
 

@@ -101,15 +101,23 @@ static moe_status_t ffn_check(const moe_ffn_params_t* p) {
     if (p->weight_layout != MOE_LAYOUT_CANONICAL && p->weight_layout != MOE_LAYOUT_PACKED)
         return MOE_ERR_INVALID_ARG;
     if (f32 && p->weight_layout == MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
+    if (p->row_layout != MOE_ROWS_BY_TOKEN && p->row_layout != MOE_ROWS_SORTED) return MOE_ERR_INVALID_ARG;
+    if (f32 && p->row_layout == MOE_ROWS_SORTED) return MOE_ERR_UNSUPPORTED;
     if (!f32) {
         // the matrix-core kernels address each GEMM's activation operand
         // (x, then the intermediate) with 32-bit byte offsets
         const int64_t esz = bf16 ? 2 : 1;
         const int64_t C = capacity((int64_t)p->T * p->K, p->E, p->B);
-        if ((int64_t)p->T * p->H * esz > kFfnMaxOperandBytes || C * p->I * esz > kFfnMaxOperandBytes)
+        const int64_t xrows = p->row_layout == MOE_ROWS_SORTED ? C : p->T;
+        if (xrows * p->H * esz > kFfnMaxOperandBytes || C * p->I * esz > kFfnMaxOperandBytes)
             return MOE_ERR_UNSUPPORTED;
     }
     return MOE_OK;
+}
+
+// rows of x the FFN reads: tokens, or the sorted layout's capacity
+static int64_t ffn_x_rows(const moe_ffn_params_t* p) {
+    return p->row_layout == MOE_ROWS_SORTED ? capacity((int64_t)p->T * p->K, p->E, p->B) : p->T;
 }
 
 moe_status_t moe_prepack_weights(const moe_ffn_params_t* p, const void* w13, const void* w2,
@@ -138,7 +146,7 @@ moe_status_t moe_prepack_block_scales(const moe_ffn_params_t* p, const void* w13
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
     if (ffn_check(p) != MOE_OK) return -1;
     const int64_t C = capacity((int64_t)p->T * p->K, p->E, p->B);
-    return ffn_workspace_bytes(p->w_dtype, p->T, p->H, p->I, C);
+    return ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C);
 }
 
 static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
@@ -155,7 +163,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
         return MOE_ERR_INVALID_ARG;
     if ((p->w_dtype == MOE_FP8_E4M3 || p->w_dtype == MOE_FP4_E2M1) && (!w13_scale || !w2_scale))
         return MOE_ERR_INVALID_ARG;
-    const int64_t need = ffn_workspace_bytes(p->w_dtype, p->T, p->H, p->I, C);
+    const int64_t need = ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C);
     if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
     FfnArgs a;
     a.T = p->T; a.K = p->K; a.E = p->E; a.H = p->H; a.I = p->I; a.B = p->B;
@@ -164,6 +172,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.post_padded = num_tokens_post_padded;
     a.y_slots = y_slots;
     a.packed = p->weight_layout == MOE_LAYOUT_PACKED;
+    a.rows_sorted = p->row_layout == MOE_ROWS_SORTED;
     hipError_t e;
     if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream), ev);
     else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream), ev);
@@ -193,6 +202,31 @@ moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, 
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, y_slots, workspace, workspace_bytes, stream,
                        reinterpret_cast<hipEvent_t const*>(events));
+}
+
+moe_status_t moe_permute_rows(const void* x, int32_t T, int32_t K, int32_t E, int32_t B, int64_t row_bytes,
+                              const int32_t* topk_ids, const int32_t* sorted_token_ids, const float* x_scale,
+                              void* x_perm, float* x_perm_scale, int32_t* row_of_slot, void* stream) {
+    if (!align_args_ok(T, K, E, B) || row_bytes <= 0 || row_bytes % 16) return MOE_ERR_INVALID_ARG;
+    if ((x_scale == nullptr) != (x_perm_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+    const int64_t S = (int64_t)T * K;
+    if (S == 0) return MOE_OK;
+    const int64_t C = capacity(S, E, B);
+    if (!x || !topk_ids || !sorted_token_ids || !x_perm || !row_of_slot) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_permute_rows(x, row_bytes, K, E, S, C, sorted_token_ids, topk_ids, x_scale, x_perm,
+                                        x_perm_scale, row_of_slot, as_stream(stream)));
+}
+
+moe_status_t moe_unpermute_combine(int32_t T, int32_t K, int32_t H, const float* y_perm,
+                                   const float* topk_weights, const int32_t* row_of_slot, int32_t out_dtype,
+                                   void* out, void* stream) {
+    if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (H % 4) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!y_perm || !topk_weights || !row_of_slot || !out) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_unpermute_combine(T, K, H, y_perm, topk_weights, row_of_slot, out_dtype == MOE_BF16,
+                                             out, as_stream(stream)));
 }
 
 moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float* y_slots,

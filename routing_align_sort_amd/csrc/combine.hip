@@ -5,6 +5,10 @@
 // of its chosen experts' FFN outputs weighted by their gate values; the
 // GC-MoE abstract (zhuanzhiai.com) adds the shared expert, which here is the
 // appended column with weight 1.  The sum runs in ascending k in fp32.
+// Unpermute-combine reads the same rows from the permuted (padded expert
+// order) buffer through the inverse row map written by the permute: the
+// TransformerEngine paragraph of the same page names unpermute as the reverse
+// of the permute.
 //
 // A streaming kernel: each thread owns 4 consecutive hidden units of one
 // token, reads the K slot rows with 16-byte non-temporal loads (each y_slots
@@ -16,7 +20,10 @@ namespace moe {
 
 constexpr int kCombineThreads = 256;
 
-template <bool kBf16>
+// kMapped: the rows come from the permuted buffer through row_of_slot (a
+// row < 0 is a skipped slot); otherwise from y_slots by slot, skipping ids
+// outside [0,E).  The arithmetic is the same, so both give the same bits.
+template <bool kBf16, bool kMapped>
 __global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(int T, int K, int E, int H, int nchunk, const float* __restrict__ y,
                const float* __restrict__ w, const int32_t* __restrict__ ids, void* __restrict__ out) {
@@ -26,10 +33,16 @@ combine_kernel(int T, int K, int E, int H, int nchunk, const float* __restrict__
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int k = 0; k < K; ++k) {
         const int64_t i = (int64_t)t * K + k;
-        const int e = ids[i];
-        if (e < 0 || e >= E) continue;
+        int64_t row = i;
+        if (kMapped) {
+            row = ids[i];
+            if (row < 0) continue;
+        } else {
+            const int e = ids[i];
+            if (e < 0 || e >= E) continue;
+        }
         const float wk = w[i];
-        const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)(y + i * H + h));
+        const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)(y + row * H + h));
         acc[0] += wk * v[0];
         acc[1] += wk * v[1];
         acc[2] += wk * v[2];
@@ -45,18 +58,29 @@ combine_kernel(int T, int K, int E, int H, int nchunk, const float* __restrict__
     }
 }
 
-hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,
-                          const int32_t* ids, int out_bf16, void* out, hipStream_t stream) {
+template <bool kMapped>
+static hipError_t launch_combine_t(int T, int K, int E, int H, const float* y, const float* w,
+                                   const int32_t* idx, int out_bf16, void* out, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const int nchunk = (H / 4 + kCombineThreads - 1) / kCombineThreads;
     const dim3 grid((unsigned)((int64_t)T * nchunk));
     if (out_bf16)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(kCombineThreads), 0, stream, T, K, E, H,
-                           nchunk, y_slots, w, ids, out);
+        hipLaunchKernelGGL((combine_kernel<true, kMapped>), grid, dim3(kCombineThreads), 0, stream, T, K, E,
+                           H, nchunk, y, w, idx, out);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(kCombineThreads), 0, stream, T, K, E, H,
-                           nchunk, y_slots, w, ids, out);
+        hipLaunchKernelGGL((combine_kernel<false, kMapped>), grid, dim3(kCombineThreads), 0, stream, T, K, E,
+                           H, nchunk, y, w, idx, out);
     return hipGetLastError();
+}
+
+hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,
+                          const int32_t* ids, int out_bf16, void* out, hipStream_t stream) {
+    return launch_combine_t<false>(T, K, E, H, y_slots, w, ids, out_bf16, out, stream);
+}
+
+hipError_t launch_unpermute_combine(int T, int K, int H, const float* y_perm, const float* w,
+                                    const int32_t* row_of_slot, int out_bf16, void* out, hipStream_t stream) {
+    return launch_combine_t<true>(T, K, 0, H, y_perm, w, row_of_slot, out_bf16, out, stream);
 }
 
 }  // namespace moe

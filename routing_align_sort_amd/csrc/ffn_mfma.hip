@@ -509,8 +509,9 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
     if (tid < BM) {
         const int slot = a.sorted_ids[(int64_t)mb * BM + tid];
         const bool ok = slot < a.S;
-        const int t = ok ? slot / a.K : 0;
-        arow[tid] = ok ? t : -1;                          // token row of x, -1 = padding
+        // row of x: the token, or (x already in the sorted order) the row itself
+        const int t = ok ? (a.rows_sorted ? mb * BM + tid : slot / a.K) : 0;
+        arow[tid] = ok ? t : -1;                          // -1 = padding
         if (F::kQuantA) rowscale[tid] = ok ? q.sx[t] : 0.f;
     }
     __syncthreads();
@@ -634,7 +635,8 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
                         y0 = y0 * rs * s0;
                         y1 = y1 * rs * s1;
                     }
-                    float* dst = a.y_slots + (int64_t)slot * H + n0 + r32;
+                    const int64_t yrow = a.rows_sorted ? (int64_t)mb * BM + m : (int64_t)slot;
+                    float* dst = a.y_slots + yrow * H + n0 + r32;
                     dst[0] = y0;
                     dst[32] = y1;
                 }
@@ -761,9 +763,10 @@ static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream,
     const uint8_t* h_in = static_cast<const uint8_t*>(ws);
     if ((err = record_stage(ev, 0, stream)) != hipSuccess) return err;
     if (kQuant) {
-        q = fp8_ws(ws, a.T, a.H, a.I, a.C);
-        if (a.T > 0)
-            hipLaunchKernelGGL(quant_tokens_kernel, dim3(a.T), dim3(kQuantThreads), 0, stream,
+        const int64_t xrows = a.rows_sorted ? a.C : a.T;         // rows of x
+        q = fp8_ws(ws, xrows, a.H, a.I, a.C);
+        if (xrows > 0)
+            hipLaunchKernelGGL(quant_tokens_kernel, dim3((unsigned)xrows), dim3(kQuantThreads), 0, stream,
                                (const uint16_t*)a.x, a.H, q.xq, q.sx, q.amax, a.C);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         h_in = q.aq;

@@ -49,8 +49,9 @@ struct FfnArgs {
     const int32_t* sorted_ids;
     const int32_t* expert_ids;
     const int32_t* post_padded;
-    float* y_slots;
+    float* y_slots;            // [S,H] by slot, or [C,H] in the sorted row order
     int packed;                // weights in the layout written by launch_prepack
+    int rows_sorted;           // x is [C,H] in the sorted row order, y written in that order
 };
 // Largest activation operand (bytes of x, or of the intermediate, as one
 // GEMM reads it) of the matrix-core kernels: they address it with 32-bit
@@ -81,5 +82,12 @@ inline hipError_t record_stage(hipEvent_t const* ev, int i, hipStream_t s) {
 // ----------------------------------------------------------------- combine --
 hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,
                           const int32_t* ids, int out_bf16, void* out, hipStream_t stream);
+hipError_t launch_unpermute_combine(int T, int K, int H, const float* y_perm, const float* w,
+                                    const int32_t* row_of_slot, int out_bf16, void* out, hipStream_t stream);
+
+// ----------------------------------------------------------------- permute --
+hipError_t launch_permute_rows(const void* x, int64_t row_bytes, int K, int E, int64_t S, int64_t C,
+                               const int32_t* sorted, const int32_t* ids, const float* x_scale, void* x_perm,
+                               float* scale_perm, int32_t* row_of_slot, hipStream_t stream);
 
 }  // namespace moe

@@ -30,14 +30,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -156,3 +156,30 @@ def test_activation_operand_limit(lib):
     # the quantised paths read one byte per element
     assert moe.moe_grouped_ffn_workspace_bytes((1 << 20) + 1, 1, 8, 2048, 128, 16,
                                                torch.float8_e4m3fn, torch.bfloat16) > 0
+
+
+def test_permute_and_row_layout_validation(lib):
+    import torch
+    P = ctypes.c_void_p
+    # row bytes must be a positive multiple of 16; scales come in pairs
+    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 24, P(8), P(8), None, P(8), None, P(8), None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 32, P(8), P(8), P(8), P(8), None, P(8), None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 32, P(8), P(8), None, P(8), None, None, None)
+    assert st == moe.MOE_ERR_INVALID_ARG       # the inverse map is required
+    assert lib.moe_permute_rows(None, 0, 2, 8, 16, 32, None, None, None, None, None, None, None) == moe.MOE_OK
+    assert lib.moe_unpermute_combine(4, 2, 6, P(8), P(8), P(8), 1, P(8), None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_unpermute_combine(4, 2, 8, None, P(8), P(8), 1, P(8), None) == moe.MOE_ERR_INVALID_ARG
+    # the sorted row layout: not for fp32, unknown layouts rejected, x has C rows
+    p = moe._FfnParams(64, 2, 8, 256, 256, 16, 0, 0, 0, moe.MOE_ROWS_SORTED)
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1
+    p.w_dtype = p.x_dtype = 1; p.row_layout = 7
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1
+    p.w_dtype = 2; p.row_layout = moe.MOE_ROWS_SORTED
+    ws_sorted = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p))
+    p.row_layout = moe.MOE_ROWS_BY_TOKEN
+    ws_token = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p))
+    C = oracle.align_capacity(128, 8, 16)
+    assert ws_sorted - ws_token == (C * 256 + 255) // 256 * 256 - 64 * 256 + \
+        (C * 4 + 255) // 256 * 256 - (64 * 4 + 255) // 256 * 256   # x codes and scales per row

@@ -1,0 +1,128 @@
+"""Permute / unpermute and the FFN in the sorted row order on the GPU.
+
+The permuted rows, the inverse row map and the per-row scales are compared bit
+for bit with the oracle.  The layer run through permute -> FFN on sorted rows
+-> unpermute-combine must give the same bits as the layer that gathers rows
+inside the FFN (the GEMMs see the same operands in the same order and the two
+combines share their arithmetic), and both are within tolerance of the
+oracle."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+import routing_align_sort_amd as moe
+from gpu_helpers import TOL, device, make_gpu_layer, oracle_tokens, rel_err, route_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+def ids_with_invalid(rng, T, K, E, p_bad=0.05):
+    ids = rng.integers(0, E, (T, K)).astype(np.int32)
+    bad = rng.random((T, K)) < p_bad
+    ids[bad] = rng.choice([-1, E, E + 7], size=int(bad.sum()))
+    return ids
+
+
+@pytest.mark.parametrize("T,K,E,B,width,dt", [
+    (1, 1, 1, 16, 16, torch.uint8), (37, 3, 5, 16, 48, torch.uint8), (300, 8, 64, 32, 512, torch.bfloat16),
+    (2048, 1, 32, 64, 7168, torch.bfloat16), (16384, 8, 256, 64, 64, torch.float32),
+    (999, 2, 33, 128, 7168, torch.uint8)])
+def test_permute_rows_match_oracle(T, K, E, B, width, dt):
+    dev = device()
+    rng = np.random.default_rng(T + width)
+    ids = ids_with_invalid(rng, T, K, E)
+    tid = torch.tensor(ids, device=dev)
+    al = moe.moe_align_sort(tid, E, B)
+    if dt == torch.float32:
+        x = torch.tensor(rng.standard_normal((T, width)).astype(np.float32), device=dev)
+    else:
+        x = torch.tensor(rng.integers(0, 255, (T, width * (2 if dt == torch.bfloat16 else 1))).astype(np.uint8),
+                         device=dev).view(dt)
+    scale = torch.tensor(rng.random(T).astype(np.float32) + 0.5, device=dev)
+    xp, ros, sp = moe.moe_permute_rows(x, tid, al["sorted_token_ids"], E, B, x_scale=scale)
+    torch.cuda.synchronize()
+    srt = al["sorted_token_ids"].cpu().numpy()
+    xh = x.cpu().view(torch.uint8).numpy() if dt != torch.float32 else x.cpu().numpy()
+    want = oracle.permute_rows(xh, srt, K)
+    got = xp.cpu().view(torch.uint8).numpy() if dt != torch.float32 else xp.cpu().numpy()
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+    assert np.array_equal(ros.cpu().numpy(), oracle.row_of_slot(srt, T * K))
+    assert np.array_equal(sp.cpu().numpy(), oracle.permute_rows(scale.cpu().numpy(), srt, K))
+    say(f"permute T={T} K={K} E={E} B={B} row {got.shape[1] * got.itemsize} B: bit-exact")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_unpermute_combine_equals_combine(out_dtype):
+    dev = device()
+    rng = np.random.default_rng(5)
+    T, K, E, B, H = 513, 6, 40, 32, 1024
+    ids = ids_with_invalid(rng, T, K, E)
+    tid = torch.tensor(ids, device=dev)
+    al = moe.moe_align_sort(tid, E, B)
+    y_slots = torch.tensor(rng.standard_normal((T * K, H)).astype(np.float32), device=dev)
+    w = torch.tensor(rng.random((T, K)).astype(np.float32), device=dev)
+    # slot rows moved into the sorted order (row r holds slot sorted[r])
+    srt = al["sorted_token_ids"]
+    C = srt.numel()
+    placed = srt < T * K
+    y_perm = torch.zeros((C, H), dtype=torch.float32, device=dev)
+    y_perm[placed] = y_slots[srt[placed].long()]
+    _, ros, _ = moe.moe_permute_rows(torch.zeros((T, 16), dtype=torch.uint8, device=dev), tid, srt, E, B)
+    a = moe.moe_unpermute_combine(y_perm, w, ros, out_dtype=out_dtype)
+    b = moe.moe_combine(y_slots, w, tid, E, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    ref = oracle.unpermute_combine(y_perm.cpu().numpy(), w.cpu().numpy(), ros.cpu().numpy())
+    assert rel_err(a.float().cpu().numpy(), ref) <= (1e-6 if out_dtype == torch.float32 else 8e-3)
+
+
+def sorted_vs_gather(cfg, L, B):
+    dev = device()
+    g = make_gpu_layer(cfg, L, B)
+    out_g = g.forward(L["x"], L["logits"], L["bias"]).clone()
+    yg = g.y_slots.clone()
+    w13, w2, s13, s2 = L["w13"], L["w2"], L.get("w13_scale"), L.get("w2_scale")
+    if cfg["dtype"] == "e2m1":
+        w13, w2, s13, s2 = w13.view(moe.FP4), w2.view(moe.FP4), s13.view(moe.E8M0), s2.view(moe.E8M0)
+    s = moe.MoELayer(w13, w2, T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"], n_group=cfg["n_group"],
+                     topk_group=cfg["topk_group"], renormalize=cfg["renormalize"],
+                     shared=bool(cfg.get("shared")), w13_scale=s13, w2_scale=s2, x_dtype=L["x"].dtype,
+                     out_dtype=torch.bfloat16, rows="sorted")
+    out_s = s.forward(L["x"], L["logits"], L["bias"])
+    torch.cuda.synchronize()
+    srt = s.sorted
+    placed = srt < s.T * s.KO
+    assert torch.equal(s.sorted, g.sorted)
+    assert torch.equal(s.y_slots[placed], yg[srt[placed].long()])       # same rows, same bits
+    assert torch.equal(out_s, out_g)
+    return s, out_s
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8", "prefill_fp4"])
+def test_layer_sorted_rows_equal_gathered_rows(name):
+    dev = device()
+    if name == "decode_bf16":
+        cfg = ms.scaled(name, T=150, H=512, I=256, E=16, K=4, n_group=4, topk_group=2)
+    else:
+        cfg = ms.scaled(name, T=201, H=768, I=384, E=12)
+    L = ms.make_layer(cfg, device=dev)
+    for B in (16, 64, 128):
+        s, out = sorted_vs_gather(cfg, L, B)
+        ids, w = route_oracle(cfg, L)
+        ref, _ = oracle_tokens(L["x"], L["w13"], L["w2"], ids, w, np.arange(cfg["T"]),
+                               L.get("w13_scale"), L.get("w2_scale"))
+        err = rel_err(out.float().cpu().numpy(), ref)
+        say(f"{name} sorted rows B={B}: bit-identical to the gathered path, rel err {err:.3e}")
+        assert err <= TOL[cfg["dtype"]]
+
+
+def test_layer_sorted_rows_full_size_prefill():
+    dev = device()
+    cfg = ms.CONFIGS["prefill_bf16"]
+    L = ms.make_layer(cfg, device=dev)
+    sorted_vs_gather(cfg, L, 64)
+    say("prefill bf16 full size: sorted rows bit-identical to gathered rows")
+    del L
+    torch.cuda.empty_cache()
