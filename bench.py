@@ -76,9 +76,14 @@ def _mean(v):
     return sum(v) / len(v) if v else 0.0
 
 
-def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
+def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=1, graph=True):
     """Generate one workload, run `warmup` + `steps` layer passes with events
-    around every kernel; return timings and what the roofline needs."""
+    around every kernel; return timings and what the roofline needs.
+    rows="sorted": the layer permutes the token rows into the sorted order
+    first and combines back through the inverse map.
+    rotate > 1: that many distinct input sets (x, logits; seeds seed..) are
+    resident and step s uses set s % rotate, so no step reads the input the
+    previous step just read (a fresh activation per layer, as in a model)."""
     import torch
 
     import moe_synth as ms
@@ -93,30 +98,37 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
                          renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
                          w13_scale=s13, w2_scale=s2,
                          x_dtype=L["x"].dtype,
-                         out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16)
+                         out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16,
+                         rows=rows)
     x, logits, bias = L["x"], L["logits"], L["bias"]
-    for _ in range(warmup):
-        layer.forward(x, logits, bias)
+    inputs = [(x, logits)]
+    for j in range(1, rotate):
+        Lj = ms.make_layer(cfg, device=dev, seed=seed + j, weights=False)
+        inputs.append((Lj["x"], Lj["logits"]))
+    for s in range(warmup):
+        layer.forward(*inputs[s % rotate], bias)
     torch.cuda.synchronize()
     # 1. the layer as a caller runs it: the four calls back to back, nothing
     #    else on the stream; wall clock between device synchronisations
     t0 = time.perf_counter()
-    for _ in range(steps):
-        layer.forward(x, logits, bias)
+    for s in range(steps):
+        layer.forward(*inputs[s % rotate], bias)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # 2. the same four calls captured once in a HIP graph and replayed
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        layer.forward(x, logits, bias)
-    g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
+    wall_graph = float("nan")
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(x, logits, bias)
         g.replay()
-    torch.cuda.synchronize()
-    wall_graph = time.perf_counter() - t0
-    del g
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall_graph = time.perf_counter() - t0
+        del g
     # 3. per-stage durations: events around every kernel (each event adds a
     #    few us of stream time, so these steps are not the wall-clock figure)
     NE = 9
@@ -124,16 +136,20 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0):
     torch.cuda.synchronize()
     for s in range(steps):
         b = NE * s
+        xs, ls = inputs[s % rotate]
         ev.record(b + 0)
-        layer.route(logits, bias)
+        layer.route(ls, bias)
         ev.record(b + 1)
         layer.align()
         ev.record(b + 2)
-        layer.ffn(x, stage_events=ev.handles[b + 3:b + 8])
+        if layer.rows_sorted:
+            layer.permute(xs)
+        layer.ffn(xs, stage_events=ev.handles[b + 3:b + 8])
         layer.combine()
         ev.record(b + 8)
     torch.cuda.synchronize()
-    names = ["route", "align", None, "quant", "gate_up", "requant", "down", "combine"]
+    names = ["route", "align", "permute" if layer.rows_sorted else None, "quant", "gate_up", "requant",
+             "down", "combine"]
     per = {n: [] for n in names if n}
     total = []
     for s in range(steps):
@@ -171,7 +187,7 @@ def summarize(cfg, B, r):
         "block_size_m": B,
         "tokens_per_s": cfg["T"] * steps / r["wall_s"],
         "us_per_step": r["wall_s"] / steps * 1e6,
-        "graph_us_per_step": r["wall_graph_s"] / steps * 1e6,
+        "graph_us_per_step": r["wall_graph_s"] / steps * 1e6 if r["wall_graph_s"] == r["wall_graph_s"] else None,
         "event_timed_us_per_step": r["us_step_events"],
         "us": {k: round(v, 2) for k, v in us.items()},
         "experts_hit": ab["experts_hit"],
@@ -352,6 +368,13 @@ def main():
     del r
     torch.cuda.empty_cache()
     if not args.no_extras:
+        # the same steps over 32 rotating resident input sets (940 MB, beyond
+        # the 256 MB last-level cache): no step reads an x left in that cache
+        rr = run_layer_timed(cfg, B, args.steps, args.warmup, dev, rotate=32, graph=False)
+        line["layer"]["us_per_step_rotating_inputs"] = round(rr["wall_s"] / args.steps * 1e6, 1)
+        line["layer"]["gate_up_us_rotating_inputs"] = round(rr["us"]["gate_up"], 2)
+        del rr
+        torch.cuda.empty_cache()
         line["hbm_probe"] = hbm_probe(dev)
         line["mfma_probe"] = mfma_probe(dev)
         line["align_sort_16k"] = align_only(dev)
@@ -383,11 +406,94 @@ def main():
             sweep[str(b2)] = {"us_per_step": round(sm["us_per_step"], 1), "gate_up_us": sm["us"]["gate_up"],
                               "down_us": sm["us"]["down"], "grouped_gemm_tflops": round(sm["grouped_gemm_tflops"], 1)}
         line["block_size_sweep"] = sweep
+        line["permute_path"] = permute_path(dev)
+        line["ffn_input_state"] = ffn_input_state(dev)
     if args.copy_probe:
         copy_probe(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(cfg, B, dev)
     print(json.dumps(line), flush=True)
+
+
+def permute_path(dev):
+    """The layer with the token rows moved into the sorted order first (what an
+    expert-parallel dispatch sends) against the layer that gathers inside the
+    FFN, on the prefill bf16 and fp8 workloads, both over 32 rotating input
+    sets (no step finds its input in the last-level cache): step time of both, and the permute and unpermute-combine kernels
+    with their HBM rates on algorithmic bytes (permute: each placed row read
+    once, each row below num_tokens_post_padded written; unpermute-combine:
+    every placed row read, out written)."""
+    import torch
+
+    import moe_synth as ms
+    res = {}
+    for name in ("prefill_bf16", "prefill_fp8"):
+        cfg = ms.CONFIGS[name]
+        B = cfg["B"]
+        r = run_layer_timed(cfg, B, 16, 8, dev, rows="sorted", rotate=32, graph=False)
+        layer = r["layer"]
+        C, H = layer.C, layer.H
+        S_valid = int((layer.sorted < layer.T * layer.KO).sum().item())
+        xb = 2                                          # bf16 rows are moved in both workloads
+        P = int(layer.ntpp.item())
+        perm_bytes = S_valid * H * xb + P * H * xb
+        unperm_bytes = S_valid * H * 4 + cfg["T"] * H * 2
+        base = run_layer_timed(cfg, B, 16, 8, dev, rotate=32, graph=False)
+        res[name] = {
+            "block_size_m": B,
+            "us_per_step_sorted_rows": round(r["wall_s"] / r["steps"] * 1e6, 1),
+            "us_per_step_gathered_rows": round(base["wall_s"] / base["steps"] * 1e6, 1),
+            "gate_up_us_sorted_rows": round(r["us"]["gate_up"], 1),
+            "gate_up_us_gathered_rows": round(base["us"]["gate_up"], 1),
+            "permute_us": round(r["us"]["permute"], 2),
+            "permute_gbs": round(perm_bytes / (r["us"]["permute"] * 1e-6) / 1e9, 1),
+            "unpermute_combine_us": round(r["us"]["combine"], 2),
+            "unpermute_combine_gbs": round(unperm_bytes / (r["us"]["combine"] * 1e-6) / 1e9, 1),
+            "stage_us": {k: round(v, 2) for k, v in r["us"].items()},
+        }
+        del r, base, layer
+        torch.cuda.empty_cache()
+    return res
+
+
+def ffn_input_state(dev, n=15):
+    """The grouped FFN of the headline workload (both GEMMs, event-timed,
+    median of n) after three different things ran before it: nothing but the
+    previous step (its x read before), a kernel that rewrote x (as the
+    previous layer of a model does), and a kernel that wrote 512 MB
+    elsewhere.  Separates the cost of reading an input from the cost of
+    following a kernel that wrote a lot."""
+    import torch
+
+    import moe_synth as ms
+    import routing_align_sort_amd as moe
+    cfg = ms.CONFIGS["prefill_bf16"]
+    L = ms.make_layer(cfg, device=dev)
+    x, logits = L["x"], L["logits"]
+    xsrc = x.clone()
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=1, B=cfg["B"], score="softmax",
+                         renormalize=False)
+    layer.forward(x, logits)
+    torch.cuda.synchronize()
+
+    def run(before):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for i in range(n):
+            before()
+            torch.cuda._sleep(20000)          # keep the host's launch latency out of the events
+            ev[2 * i].record()
+            layer.ffn(x)
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        return round(sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(n))[n // 2], 1)
+
+    res = {"ffn_us_after_previous_step": run(lambda: None),
+           "ffn_us_after_x_rewritten": run(lambda: x.copy_(xsrc)),
+           "ffn_us_after_512MB_written": run(lambda: scrub.add_(1))}
+    del layer, scrub, L
+    torch.cuda.empty_cache()
+    return res
 
 
 COPY_PROBE_BYTES = 1 << 30

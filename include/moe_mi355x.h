@@ -197,8 +197,9 @@ typedef enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layo
  * sorted_token_ids; y_slots is [T*K,H] by slot.  MOE_ROWS_SORTED (the
  * receiving side of an expert-parallel dispatch): x is [C,H] already in the
  * sorted order (as moe_permute_rows writes it: row r holds the token of slot
- * sorted_token_ids[r]) and y_slots is [C,H] in the same order, row r written
- * only where sorted_token_ids[r] < T*K.  Not for fp32.
+ * sorted_token_ids[r]; rows from num_tokens_post_padded on are never read)
+ * and y_slots is [C,H] in the same order, row r written only where
+ * sorted_token_ids[r] < T*K.  Not for fp32.
  */
 typedef enum { MOE_ROWS_BY_TOKEN = 0, MOE_ROWS_SORTED = 1 } moe_row_layout_t;
 
@@ -286,16 +287,18 @@ moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float
  * moe_align_sort's padded layout, so each expert's rows -- and each
  * destination GPU's range of experts -- are contiguous.
  *
- * moe_permute_rows, for r < C = moe_align_sort_capacity(T,K,E,B):
+ * moe_permute_rows, for r < P = *num_tokens_post_padded (read on the device):
  *   x_perm[r] = x[sorted_token_ids[r] / K] if sorted_token_ids[r] < T*K,
  *               else a zero row;
  *   x_perm_scale[r] = x_scale[that token] or 0 (both NULL to skip);
+ * rows from P to C = moe_align_sort_capacity(T,K,E,B) are not written; and
  *   row_of_slot[i] = r with sorted_token_ids[r] = i, or -1 when topk_ids[i]
  *   is outside [0,E) (i < T*K).
  * x device [T, row_bytes] (any element type, row_bytes > 0 and a multiple of
- * 16); topk_ids and sorted_token_ids as given to / produced by moe_align_sort
- * with the same T,K,E,B; x_perm device [C, row_bytes]; x_scale device fp32
- * [T]; x_perm_scale device fp32 [C]; row_of_slot device int32 [T*K].
+ * 16); topk_ids, sorted_token_ids and num_tokens_post_padded as given to /
+ * produced by moe_align_sort with the same T,K,E,B; x_perm device
+ * [C, row_bytes]; x_scale device fp32 [T]; x_perm_scale device fp32 [C];
+ * row_of_slot device int32 [T*K].
  *
  * moe_unpermute_combine: out[t,h] = sum over k = 0..K-1 in ascending order,
  * skipping row_of_slot[t*K+k] < 0, of topk_weights[t,k] * y_perm[row, h] in
@@ -306,8 +309,9 @@ moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float
  */
 moe_status_t moe_permute_rows(const void *x, int32_t T, int32_t K, int32_t E, int32_t B,
                               int64_t row_bytes, const int32_t *topk_ids,
-                              const int32_t *sorted_token_ids, const float *x_scale, void *x_perm,
-                              float *x_perm_scale, int32_t *row_of_slot, void *stream);
+                              const int32_t *sorted_token_ids, const int32_t *num_tokens_post_padded,
+                              const float *x_scale, void *x_perm, float *x_perm_scale,
+                              int32_t *row_of_slot, void *stream);
 moe_status_t moe_unpermute_combine(int32_t T, int32_t K, int32_t H, const float *y_perm,
                                    const float *topk_weights, const int32_t *row_of_slot,
                                    int32_t out_dtype, void *out, void *stream);

@@ -286,16 +286,22 @@ def moe_layer(x, w13, w2, topk_ids, topk_weights, *, w_dtype, x_dtype, inter,
     return combine(y, topk_weights, topk_ids, E), y
 
 
-def permute_rows(x, sorted_ids, K: int):
-    """Rows of x (any dtype, [T, ...]) moved into the padded expert order:
-    row r is x[sorted_ids[r] // K] where sorted_ids[r] < T*K, else zeros."""
+def permute_rows(x, sorted_ids, K: int, P=None, out=None):
+    """Rows of x (any dtype, [T, ...]) moved into the padded expert order: for
+    r < P (default: every row of sorted_ids), row r is x[sorted_ids[r] // K]
+    where sorted_ids[r] < T*K, else zeros; rows from P on keep the contents of
+    ``out`` (zeros when not given)."""
     xa = np.ascontiguousarray(x)
     T = xa.shape[0]
     row_bytes = xa.dtype.itemsize * (int(np.prod(xa.shape[1:])) if xa.ndim > 1 else 1)
     srt = _c(sorted_ids, np.int32)
     C = srt.shape[0]
-    out = np.empty((C,) + xa.shape[1:], xa.dtype)
-    rc = _load().oracle_permute_rows(_ptr(xa), T, row_bytes, K, _ptr(srt), C, _ptr(out))
+    P = C if P is None else int(P)
+    if out is None:
+        out = np.zeros((C,) + xa.shape[1:], xa.dtype)
+    else:
+        out = np.array(out, dtype=xa.dtype, copy=True).reshape((C,) + xa.shape[1:])
+    rc = _load().oracle_permute_rows(_ptr(xa), T, row_bytes, K, _ptr(srt), P, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_permute_rows: invalid arguments")
     return out

@@ -514,18 +514,19 @@ int oracle_combine(int T, int K, int E, int H, const float *y_slots,
  * parallelism a layer pays a token dispatch, the grouped GEMMs and a combine.
  * Reading: the destination order is Align & Sort's padded layout, so every
  * expert's rows are contiguous (one contiguous send range per destination
- * GPU); padding rows are zero.
- *   x_perm[r]      = x[sorted[r] / K]   (r < C, sorted[r] < S), else zeros
+ * GPU); padding rows are zero; rows from P = num_tokens_post_padded on hold
+ * no expert's data and are left as they were.
+ *   x_perm[r]      = x[sorted[r] / K]   (r < P, sorted[r] < S), else zeros (r < P)
  *   row_of_slot[i] = the r with sorted[r] = i, or -1 if slot i is not placed
  *   out[t]         = sum over k ascending of w[t,k] * y_perm[row_of_slot[t*K+k]],
  *                    slots with row -1 skipped, in double
  */
 int oracle_permute_rows(const uint8_t *x, int T, int64_t row_bytes, int K, const int32_t *sorted,
-                        int64_t C, uint8_t *x_perm)
+                        int64_t P, uint8_t *x_perm)
 {
-    if (T < 0 || K < 1 || row_bytes < 0 || C < 0) return 1;
+    if (T < 0 || K < 1 || row_bytes < 0 || P < 0) return 1;
     int64_t S = (int64_t)T * K;
-    for (int64_t r = 0; r < C; r++) {
+    for (int64_t r = 0; r < P; r++) {
         uint8_t *dst = x_perm + r * row_bytes;
         if (sorted[r] >= 0 && sorted[r] < S)
             memcpy(dst, x + (int64_t)(sorted[r] / K) * row_bytes, (size_t)row_bytes);

@@ -82,7 +82,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_prepack_block_scales.restype = i32
     lib.moe_combine.argtypes = [i32, i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_combine.restype = i32
-    lib.moe_permute_rows.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, P, P, P, P]
+    lib.moe_permute_rows.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, P, P, P, P, P]
     lib.moe_permute_rows.restype = i32
     lib.moe_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_unpermute_combine.restype = i32
@@ -332,10 +332,11 @@ def moe_combine(y_slots, topk_weights, topk_ids, E, *, out_dtype=torch.bfloat16,
 
 
 # ------------------------------------------------------- permute/unpermute --
-def moe_permute_rows(x, topk_ids, sorted_token_ids, E, B, *, x_scale=None, x_perm=None,
-                     x_perm_scale=None, row_of_slot=None, stream=None):
+def moe_permute_rows(x, topk_ids, sorted_token_ids, num_tokens_post_padded, E, B, *, x_scale=None,
+                     x_perm=None, x_perm_scale=None, row_of_slot=None, stream=None):
     """Rows of x [T, ...] moved into the padded expert order of moe_align_sort:
-    returns (x_perm [C, ...], row_of_slot int32 [T*K], x_perm_scale or None)."""
+    returns (x_perm [C, ...], row_of_slot int32 [T*K], x_perm_scale or None).
+    Rows of x_perm from num_tokens_post_padded on are not written."""
     lib = load_library()
     T, K = topk_ids.shape
     _need(topk_ids, torch.int32, "topk_ids")
@@ -344,6 +345,7 @@ def moe_permute_rows(x, topk_ids, sorted_token_ids, E, B, *, x_scale=None, x_per
         raise ValueError("x and topk_ids disagree on the token count")
     C = moe_align_sort_capacity(T, K, E, B)
     _need(sorted_token_ids, torch.int32, "sorted_token_ids", C)
+    _need(num_tokens_post_padded, torch.int32, "num_tokens_post_padded", 1)
     row_bytes = x[0].numel() * x.element_size() if T > 0 else 16
     if x_perm is None:
         x_perm = torch.empty((C,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
@@ -357,7 +359,8 @@ def moe_permute_rows(x, topk_ids, sorted_token_ids, E, B, *, x_scale=None, x_per
             x_perm_scale = torch.empty(C, dtype=torch.float32, device=x.device)
         _need(x_perm_scale, torch.float32, "x_perm_scale", C)
     _check("moe_permute_rows", lib.moe_permute_rows(
-        _ptr(x), T, K, E, B, row_bytes, _ptr(topk_ids), _ptr(sorted_token_ids), _ptr(x_scale),
+        _ptr(x), T, K, E, B, row_bytes, _ptr(topk_ids), _ptr(sorted_token_ids),
+        _ptr(num_tokens_post_padded), _ptr(x_scale),
         _ptr(x_perm), _ptr(x_perm_scale if x_scale is not None else None), _ptr(row_of_slot),
         _stream(stream)))
     return x_perm, row_of_slot, (x_perm_scale if x_scale is not None else None)
@@ -448,7 +451,7 @@ class MoELayer:
                               expert_offsets=self.offsets, workspace=self.ws_align)
 
     def permute(self, x):
-        return moe_permute_rows(x, self.topk_ids, self.sorted, self.E_slabs, self.B,
+        return moe_permute_rows(x, self.topk_ids, self.sorted, self.ntpp, self.E_slabs, self.B,
                                 x_perm=self.x_perm, row_of_slot=self.row_of_slot)
 
     def ffn(self, x, stage_events=None):

@@ -205,16 +205,18 @@ moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, 
 }
 
 moe_status_t moe_permute_rows(const void* x, int32_t T, int32_t K, int32_t E, int32_t B, int64_t row_bytes,
-                              const int32_t* topk_ids, const int32_t* sorted_token_ids, const float* x_scale,
-                              void* x_perm, float* x_perm_scale, int32_t* row_of_slot, void* stream) {
+                              const int32_t* topk_ids, const int32_t* sorted_token_ids,
+                              const int32_t* num_tokens_post_padded, const float* x_scale, void* x_perm,
+                              float* x_perm_scale, int32_t* row_of_slot, void* stream) {
     if (!align_args_ok(T, K, E, B) || row_bytes <= 0 || row_bytes % 16) return MOE_ERR_INVALID_ARG;
     if ((x_scale == nullptr) != (x_perm_scale == nullptr)) return MOE_ERR_INVALID_ARG;
     const int64_t S = (int64_t)T * K;
     if (S == 0) return MOE_OK;
     const int64_t C = capacity(S, E, B);
-    if (!x || !topk_ids || !sorted_token_ids || !x_perm || !row_of_slot) return MOE_ERR_INVALID_ARG;
-    return from_hip(launch_permute_rows(x, row_bytes, K, E, S, C, sorted_token_ids, topk_ids, x_scale, x_perm,
-                                        x_perm_scale, row_of_slot, as_stream(stream)));
+    if (!x || !topk_ids || !sorted_token_ids || !num_tokens_post_padded || !x_perm || !row_of_slot)
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_permute_rows(x, row_bytes, K, E, S, C, sorted_token_ids, num_tokens_post_padded,
+                                        topk_ids, x_scale, x_perm, x_perm_scale, row_of_slot, as_stream(stream)));
 }
 
 moe_status_t moe_unpermute_combine(int32_t T, int32_t K, int32_t H, const float* y_perm,

@@ -87,7 +87,8 @@ hipError_t launch_unpermute_combine(int T, int K, int H, const float* y_perm, co
 
 // ----------------------------------------------------------------- permute --
 hipError_t launch_permute_rows(const void* x, int64_t row_bytes, int K, int E, int64_t S, int64_t C,
-                               const int32_t* sorted, const int32_t* ids, const float* x_scale, void* x_perm,
-                               float* scale_perm, int32_t* row_of_slot, hipStream_t stream);
+                               const int32_t* sorted, const int32_t* post_padded, const int32_t* ids,
+                               const float* x_scale, void* x_perm, float* scale_perm, int32_t* row_of_slot,
+                               hipStream_t stream);
 
 }  // namespace moe

@@ -162,13 +162,16 @@ def test_permute_and_row_layout_validation(lib):
     import torch
     P = ctypes.c_void_p
     # row bytes must be a positive multiple of 16; scales come in pairs
-    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 24, P(8), P(8), None, P(8), None, P(8), None)
+    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 24, P(8), P(8), P(8), None, P(8), None, P(8), None)
     assert st == moe.MOE_ERR_INVALID_ARG
-    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 32, P(8), P(8), P(8), P(8), None, P(8), None)
+    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 32, P(8), P(8), P(8), P(8), P(8), None, P(8), None)
     assert st == moe.MOE_ERR_INVALID_ARG
-    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 32, P(8), P(8), None, P(8), None, None, None)
+    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 32, P(8), P(8), P(8), None, P(8), None, None, None)
     assert st == moe.MOE_ERR_INVALID_ARG       # the inverse map is required
-    assert lib.moe_permute_rows(None, 0, 2, 8, 16, 32, None, None, None, None, None, None, None) == moe.MOE_OK
+    st = lib.moe_permute_rows(P(8), 4, 2, 8, 16, 32, P(8), P(8), None, None, P(8), None, P(8), None)
+    assert st == moe.MOE_ERR_INVALID_ARG       # and the padded row count
+    assert lib.moe_permute_rows(None, 0, 2, 8, 16, 32, None, None, None, None, None, None, None,
+                                None) == moe.MOE_OK
     assert lib.moe_unpermute_combine(4, 2, 6, P(8), P(8), P(8), 1, P(8), None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(4, 2, 8, None, P(8), P(8), 1, P(8), None) == moe.MOE_ERR_INVALID_ARG
     # the sorted row layout: not for fp32, unknown layouts rejected, x has C rows

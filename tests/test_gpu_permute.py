@@ -41,16 +41,23 @@ def test_permute_rows_match_oracle(T, K, E, B, width, dt):
         x = torch.tensor(rng.integers(0, 255, (T, width * (2 if dt == torch.bfloat16 else 1))).astype(np.uint8),
                          device=dev).view(dt)
     scale = torch.tensor(rng.random(T).astype(np.float32) + 0.5, device=dev)
-    xp, ros, sp = moe.moe_permute_rows(x, tid, al["sorted_token_ids"], E, B, x_scale=scale)
+    C = al["sorted_token_ids"].numel()
+    # rows past the padded count must keep what was there
+    xp0 = torch.full((C, x[0].numel() * x.element_size()), 7, dtype=torch.uint8, device=dev)
+    xp0 = xp0.view(dt).view((C,) + tuple(x.shape[1:]))
+    sp0 = torch.full((C,), -3.0, dtype=torch.float32, device=dev)
+    xp, ros, sp = moe.moe_permute_rows(x, tid, al["sorted_token_ids"], al["num_tokens_post_padded"], E, B,
+                                       x_scale=scale, x_perm=xp0.clone(), x_perm_scale=sp0.clone())
     torch.cuda.synchronize()
     srt = al["sorted_token_ids"].cpu().numpy()
-    xh = x.cpu().view(torch.uint8).numpy() if dt != torch.float32 else x.cpu().numpy()
-    want = oracle.permute_rows(xh, srt, K)
-    got = xp.cpu().view(torch.uint8).numpy() if dt != torch.float32 else xp.cpu().numpy()
-    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+    P = int(al["num_tokens_post_padded"].item())
+    u8 = lambda t: t.cpu().contiguous().view(torch.uint8).numpy()
+    want = oracle.permute_rows(u8(x), srt, K, P=P, out=u8(xp0))
+    assert np.array_equal(u8(xp), want)
     assert np.array_equal(ros.cpu().numpy(), oracle.row_of_slot(srt, T * K))
-    assert np.array_equal(sp.cpu().numpy(), oracle.permute_rows(scale.cpu().numpy(), srt, K))
-    say(f"permute T={T} K={K} E={E} B={B} row {got.shape[1] * got.itemsize} B: bit-exact")
+    assert np.array_equal(sp.cpu().numpy(),
+                          oracle.permute_rows(scale.cpu().numpy(), srt, K, P=P, out=sp0.cpu().numpy()))
+    say(f"permute T={T} K={K} E={E} B={B} row {u8(x).shape[1]} B, P={P} of C={C}: bit-exact")
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
@@ -69,7 +76,8 @@ def test_unpermute_combine_equals_combine(out_dtype):
     placed = srt < T * K
     y_perm = torch.zeros((C, H), dtype=torch.float32, device=dev)
     y_perm[placed] = y_slots[srt[placed].long()]
-    _, ros, _ = moe.moe_permute_rows(torch.zeros((T, 16), dtype=torch.uint8, device=dev), tid, srt, E, B)
+    _, ros, _ = moe.moe_permute_rows(torch.zeros((T, 16), dtype=torch.uint8, device=dev), tid, srt,
+                                     al["num_tokens_post_padded"], E, B)
     a = moe.moe_unpermute_combine(y_perm, w, ros, out_dtype=out_dtype)
     b = moe.moe_combine(y_slots, w, tid, E, out_dtype=out_dtype)
     torch.cuda.synchronize()

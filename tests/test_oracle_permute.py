@@ -88,3 +88,18 @@ def test_permute_moves_bytes_of_any_width():
         xp = oracle.permute_rows(x, al["sorted_token_ids"], 2)
         placed = al["sorted_token_ids"] < 66
         assert np.array_equal(xp[placed], x[al["sorted_token_ids"][placed] // 2])
+
+
+def test_rows_past_the_padded_count_are_left_alone():
+    rng = np.random.default_rng(11)
+    ids, al = random_case(rng, 40, 2, 16, 8, 0.0)
+    srt, P = al["sorted_token_ids"], al["num_tokens_post_padded"]
+    C = srt.shape[0]
+    assert P < C
+    x = rng.integers(1, 200, (40, 32)).astype(np.uint8)
+    before = np.full((C, 32), 0xAB, np.uint8)
+    xp = oracle.permute_rows(x, srt, 2, P=P, out=before)
+    assert (xp[P:] == 0xAB).all()
+    full = oracle.permute_rows(x, srt, 2)
+    assert np.array_equal(xp[:P], full[:P])
+    assert not full[P:].any()
