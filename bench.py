@@ -297,6 +297,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--B", type=int, default=None)
+    ap.add_argument("--rows", default="by_token", choices=("by_token", "sorted"),
+                    help="sorted: permute the token rows into the sorted order before the FFN "
+                         "and combine back through the inverse map")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the align-only and secondary-workload figures")
@@ -335,7 +338,7 @@ def main():
     cfg = ms.CONFIGS[args.workload]
     B = args.B or cfg["B"]
 
-    r = run_layer_timed(cfg, B, args.steps, args.warmup, dev)
+    r = run_layer_timed(cfg, B, args.steps, args.warmup, dev, rows=args.rows)
     summ = summarize(cfg, B, r)
     ab = algorithmic_bytes(cfg, r["ids"], r["E_slabs"])
     ms_per_step = r["wall_s"] / args.steps * 1e3
@@ -361,7 +364,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; random-init expert weights)",
         "config": {"workload": describe(args.workload, cfg, B), "tokens": cfg["T"],
                    "experts": cfg["E"], "top_k": cfg["K"], "hidden": cfg["H"], "inter": cfg["I"],
-                   "block_size_m": B, "shared_expert": bool(cfg.get("shared"))},
+                   "block_size_m": B, "shared_expert": bool(cfg.get("shared")), "rows": args.rows},
         "layer": summ,
         "roofline": roofline,
     }
