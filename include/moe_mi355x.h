@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
@@ -202,6 +202,22 @@ typedef enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_PACKED = 1 } moe_weight_layo
  * sorted_token_ids[r] < T*K.  Not for fp32.
  */
 typedef enum { MOE_ROWS_BY_TOKEN = 0, MOE_ROWS_SORTED = 1 } moe_row_layout_t;
+/*
+ * schedule MOE_SCHEDULE_TWO_LAUNCH: the gate/up GEMM, (E4M3 paths) the
+ * intermediate's requantisation and the down GEMM run as separate launches.
+ * MOE_SCHEDULE_FUSED (the one-stage form; the aiter issue's Estimated
+ * Performance Scaling assumptions note that a fused MoE may keep the
+ * intermediate out of global memory, and the dignews.cc page's CK section
+ * fuses the MoE's steps into one device pipeline): one persistent launch in
+ * which a block's down tiles start as soon as its gate/up tiles are done, and
+ * the last of those requantises the block.
+ * Both give the same bits.  The fused launch waits on other workgroups
+ * with a bounded poll; if a poll gives up (other work holding the device for
+ * about a second) it sets a status word in the workspace, at byte offset
+ * moe_grouped_ffn_workspace_bytes(p with schedule = MOE_SCHEDULE_TWO_LAUNCH)
+ * + 32, and the result is not valid.  Not for fp32.
+ */
+typedef enum { MOE_SCHEDULE_TWO_LAUNCH = 0, MOE_SCHEDULE_FUSED = 1 } moe_schedule_t;
 
 typedef struct {
     int32_t T, K, E, H, I, B;
@@ -209,6 +225,7 @@ typedef struct {
     int32_t x_dtype;           /* moe_dtype_t */
     int32_t weight_layout;     /* moe_weight_layout_t of w13 and w2 */
     int32_t row_layout;        /* moe_row_layout_t of x and y_slots */
+    int32_t schedule;          /* moe_schedule_t */
 } moe_ffn_params_t;
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);

@@ -40,7 +40,8 @@ class _FfnParams(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("B", ctypes.c_int32),
                 ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32), ("row_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("row_layout", ctypes.c_int32),
+                ("schedule", ctypes.c_int32)]
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
@@ -211,12 +212,14 @@ def weight_dims(w13):
 
 MOE_LAYOUT_CANONICAL, MOE_LAYOUT_PACKED = 0, 1
 MOE_ROWS_BY_TOKEN, MOE_ROWS_SORTED = 0, 1
+MOE_SCHEDULE_TWO_LAUNCH, MOE_SCHEDULE_FUSED = 0, 1
 
 
-def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False, rows_sorted=False):
+def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False, rows_sorted=False, fused=False):
     return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype],
                       MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_CANONICAL,
-                      MOE_ROWS_SORTED if rows_sorted else MOE_ROWS_BY_TOKEN)
+                      MOE_ROWS_SORTED if rows_sorted else MOE_ROWS_BY_TOKEN,
+                      MOE_SCHEDULE_FUSED if fused else MOE_SCHEDULE_TWO_LAUNCH)
 
 
 def moe_prepack_weights(w13, w2, *, stream=None):
@@ -249,8 +252,9 @@ def moe_prepack_block_scales(w13_scale, w2_scale, H, I, *, stream=None):
     return p13, p2
 
 
-def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype, rows_sorted=False) -> int:
-    p = _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, rows_sorted=rows_sorted)
+def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype, rows_sorted=False,
+                                    fused=False) -> int:
+    p = _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, rows_sorted=rows_sorted, fused=fused)
     c = int(load_library().moe_grouped_ffn_workspace_bytes(ctypes.byref(p)))
     if c < 0:
         raise MoEError("moe_grouped_ffn_workspace_bytes", MOE_ERR_UNSUPPORTED)
@@ -259,12 +263,13 @@ def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype, rows_sor
 
 def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, *, K, B,
                     w13_scale=None, w2_scale=None, y_slots=None, workspace=None, stream=None,
-                    stage_events=None, packed=False, T=None):
+                    stage_events=None, packed=False, T=None, fused=False):
     """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots fp32 [T*K, H].
 
     With ``T`` given and x of C = capacity rows, x is taken in the sorted row
     order (as moe_permute_rows writes it) and the result is [C, H] in that
     order (row layout MOE_ROWS_SORTED).
+    fused: both GEMMs in one persistent launch (schedule MOE_SCHEDULE_FUSED).
     stage_events: optional 5 raw hipEvent_t handles (ints) recorded at the stage
     boundaries (the profiling entry point)."""
     lib = load_library()
@@ -296,8 +301,8 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     if y_slots is None:
         y_slots = torch.empty((ny, H), dtype=torch.float32, device=x.device)
     _need(y_slots, torch.float32, "y_slots", ny * H)
-    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed, rows_sorted)
-    need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype, rows_sorted)
+    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed, rows_sorted, fused)
+    need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype, rows_sorted, fused)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -398,7 +403,7 @@ class MoELayer:
     def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
                  w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None,
-                 rows="by_token"):
+                 rows="by_token", schedule="two_launch"):
         dev = w13.device
         if packed is None:
             packed = w13.dtype != torch.float32
@@ -429,9 +434,15 @@ class MoELayer:
         if rows not in ("by_token", "sorted"):
             raise ValueError("rows must be 'by_token' or 'sorted'")
         self.rows_sorted = rows == "sorted"
+        if schedule not in ("two_launch", "fused"):
+            raise ValueError("schedule must be 'two_launch' or 'fused'")
+        self.fused = schedule == "fused"
         ws_a = moe_align_sort_workspace_bytes(T, self.KO, self.E_slabs, B)
         ws_f = moe_grouped_ffn_workspace_bytes(T, self.KO, self.E_slabs, self.H, self.I, B,
-                                               w13.dtype, x_dtype, self.rows_sorted)
+                                               w13.dtype, x_dtype, self.rows_sorted, self.fused)
+        # where the one-stage schedule reports a wait that gave up (int32, 0 = fine)
+        self.status_offset = moe_grouped_ffn_workspace_bytes(
+            T, self.KO, self.E_slabs, self.H, self.I, B, w13.dtype, x_dtype, self.rows_sorted) + 32
         self.ws_align = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
         self.ws_ffn = torch.empty(max(ws_f, 1), dtype=torch.uint8, device=dev)
         ny = C if self.rows_sorted else T * self.KO
@@ -460,11 +471,17 @@ class MoELayer:
                                    self.ntpp, K=self.KO, B=self.B, w13_scale=self.w13_scale,
                                    w2_scale=self.w2_scale, y_slots=self.y_slots,
                                    workspace=self.ws_ffn, stage_events=stage_events,
-                                   packed=self.packed, T=self.T)
+                                   packed=self.packed, T=self.T, fused=self.fused)
         return moe_grouped_ffn(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
                                K=self.KO, B=self.B, w13_scale=self.w13_scale,
                                w2_scale=self.w2_scale, y_slots=self.y_slots, workspace=self.ws_ffn,
-                               stage_events=stage_events, packed=self.packed)
+                               stage_events=stage_events, packed=self.packed, fused=self.fused)
+
+    def fused_status(self):
+        """The one-stage schedule's status word (0 = every wait was satisfied); syncs."""
+        if not self.fused:
+            return 0
+        return int(self.ws_ffn[self.status_offset:self.status_offset + 4].view(torch.int32).item())
 
     def combine(self):
         if self.rows_sorted:

@@ -103,6 +103,8 @@ static moe_status_t ffn_check(const moe_ffn_params_t* p) {
     if (f32 && p->weight_layout == MOE_LAYOUT_PACKED) return MOE_ERR_UNSUPPORTED;
     if (p->row_layout != MOE_ROWS_BY_TOKEN && p->row_layout != MOE_ROWS_SORTED) return MOE_ERR_INVALID_ARG;
     if (f32 && p->row_layout == MOE_ROWS_SORTED) return MOE_ERR_UNSUPPORTED;
+    if (p->schedule != MOE_SCHEDULE_TWO_LAUNCH && p->schedule != MOE_SCHEDULE_FUSED) return MOE_ERR_INVALID_ARG;
+    if (f32 && p->schedule == MOE_SCHEDULE_FUSED) return MOE_ERR_UNSUPPORTED;
     if (!f32) {
         // the matrix-core kernels address each GEMM's activation operand
         // (x, then the intermediate) with 32-bit byte offsets
@@ -146,7 +148,7 @@ moe_status_t moe_prepack_block_scales(const moe_ffn_params_t* p, const void* w13
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
     if (ffn_check(p) != MOE_OK) return -1;
     const int64_t C = capacity((int64_t)p->T * p->K, p->E, p->B);
-    return ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C);
+    return ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C, p->schedule == MOE_SCHEDULE_FUSED);
 }
 
 static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
@@ -163,7 +165,8 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
         return MOE_ERR_INVALID_ARG;
     if ((p->w_dtype == MOE_FP8_E4M3 || p->w_dtype == MOE_FP4_E2M1) && (!w13_scale || !w2_scale))
         return MOE_ERR_INVALID_ARG;
-    const int64_t need = ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C);
+    const int64_t need =
+        ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C, p->schedule == MOE_SCHEDULE_FUSED);
     if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
     FfnArgs a;
     a.T = p->T; a.K = p->K; a.E = p->E; a.H = p->H; a.I = p->I; a.B = p->B;
@@ -173,6 +176,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     a.y_slots = y_slots;
     a.packed = p->weight_layout == MOE_LAYOUT_PACKED;
     a.rows_sorted = p->row_layout == MOE_ROWS_SORTED;
+    a.fused = p->schedule == MOE_SCHEDULE_FUSED;
     hipError_t e;
     if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream), ev);
     else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream), ev);

@@ -39,6 +39,7 @@
 //   a few M blocks in that XCD's L2, and M blocks of one expert stay close in
 //   time so repeated weight tiles hit L2 (the pid remapping idea of the AITER
 //   section of the dignews.cc page, "AMD GPU ... 7x faster ...").
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -493,16 +494,24 @@ constexpr int ffn_la() {
     return full ? PF + 1 : 1;
 }
 
+// LDS of one workgroup: the activation tile and the per-row tables.
+template <int BM>
+struct FfnSmem {
+    __attribute__((aligned(16))) uint8_t lds[Tile<BM>::LDS_BYTES];
+    int arow[BM];
+    int slots[BM];
+    float rowscale[BM];
+};
+
+// One gate/up tile: M block mb, intermediate columns [nt*128, nt*128+128).
 template <int kW, bool kPacked, int BM, int PF>
-__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
-ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
+__device__ __forceinline__ void stage1_tile(const FfnArgs& a, uint16_t* __restrict__ h_out, const Fp8Ws& q,
+                                            int mb, int nt, FfnSmem<BM>& sm) {
     using TL = Tile<BM>;
     using F = Fmt<kW>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
-    __shared__ int arow[BM];
-    __shared__ float rowscale[BM];
-    int mb, nt;
-    if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
+    uint8_t* lds = sm.lds;
+    int* arow = sm.arow;
+    float* rowscale = sm.rowscale;
     const int e = a.expert_ids[mb];
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int H = a.H, I = a.I;
@@ -572,18 +581,26 @@ ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
         }
 }
 
-// ------------------------------------------------------------------ stage 2 --
 template <int kW, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
-ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
-    using TL = Tile<BM>;
-    using F = Fmt<kW>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[TL::LDS_BYTES];
-    __shared__ int arow[BM];
-    __shared__ int slots[BM];
-    __shared__ float rowscale[BM];
+ffn_stage1(FfnArgs a, uint16_t* __restrict__ h_out, Fp8Ws q, int nN) {
+    __shared__ FfnSmem<BM> sm;
     int mb, nt;
     if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
+    stage1_tile<kW, kPacked, BM, PF>(a, h_out, q, mb, nt, sm);
+}
+
+// ------------------------------------------------------------------ stage 2 --
+// One down tile: M block mb, output columns [nt*256, nt*256+256).
+template <int kW, bool kPacked, int BM, int PF>
+__device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __restrict__ h_in,
+                                            const float* __restrict__ sa, int mb, int nt, FfnSmem<BM>& sm) {
+    using TL = Tile<BM>;
+    using F = Fmt<kW>;
+    uint8_t* lds = sm.lds;
+    int* arow = sm.arow;
+    int* slots = sm.slots;
+    float* rowscale = sm.rowscale;
     const int e = a.expert_ids[mb];
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int H = a.H, I = a.I;
@@ -642,6 +659,15 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
                 }
             }
         }
+}
+
+template <int kW, bool kPacked, int BM, int PF>
+__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
+ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
+    __shared__ FfnSmem<BM> sm;
+    int mb, nt;
+    if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
+    stage2_tile<kW, kPacked, BM, PF>(a, h_in, sa, mb, nt, sm);
 }
 
 // --------------------------------------------------------- fp8 quantisation --
@@ -708,13 +734,10 @@ quant_tokens_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__
     }
 }
 
-// One workgroup per sorted row of the intermediate: fp32 a -> E4M3 + scale.
-__global__ void __launch_bounds__(kQuantThreads)
-requant_rows_kernel(const float* __restrict__ a, const uint32_t* __restrict__ amax_rows,
-                    const int32_t* __restrict__ post_padded, int I, uint8_t* __restrict__ aq,
-                    float* __restrict__ sa) {
-    const int64_t r = blockIdx.x;
-    if (r >= post_padded[0]) return;
+// Row r of the fp32 intermediate -> E4M3 codes + scale, by a workgroup of
+// kQuantThreads threads.
+__device__ __forceinline__ void requant_row(const float* __restrict__ a, const uint32_t* __restrict__ amax_rows,
+                                            int I, uint8_t* __restrict__ aq, float* __restrict__ sa, int64_t r) {
     const float m = __uint_as_float(amax_rows[r]);
     const float inv = (m > 0.f) ? 448.0f / m : 0.f;
     if (threadIdx.x == 0) sa[r] = (m > 0.f) ? m / 448.0f : 1.0f;
@@ -729,14 +752,181 @@ requant_rows_kernel(const float* __restrict__ a, const uint32_t* __restrict__ am
     }
 }
 
+// One workgroup per sorted row of the intermediate: fp32 a -> E4M3 + scale.
+__global__ void __launch_bounds__(kQuantThreads)
+requant_rows_kernel(const float* __restrict__ a, const uint32_t* __restrict__ amax_rows,
+                    const int32_t* __restrict__ post_padded, int I, uint8_t* __restrict__ aq,
+                    float* __restrict__ sa) {
+    const int64_t r = blockIdx.x;
+    if (r >= post_padded[0]) return;
+    requant_row(a, amax_rows, I, aq, sa, r);
+}
+
+
+// ------------------------------------------------------- one-stage schedule --
+// Both GEMMs in one persistent launch.  Workgroups claim tiles from eight
+// queues, one per XCD (the M blocks are split into eight contiguous ranges,
+// and a queue lists its range's gate/up tiles, then its down tiles), starting
+// with the queue of their own XCD and then taking from the others.  A down
+// tile of M block mb waits until mb's intermediate is complete: the gate/up
+// tile that finishes mb last (a per-block counter) requantises the block's
+// rows (E4M3 paths) and raises the block's ready flag.
+// Progress: a queue hands out indices in order, so a workgroup that claims a
+// down tile of a block finds every gate/up tile of that block already
+// claimed by a running workgroup, and gate/up tiles never wait.  Every wait
+// is still bounded: past kFusedSpinLimit polls it sets the status word and
+// proceeds (the result is then wrong, and the status says so).
+// Ordering across XCDs (each has its own L2): every wave waits for its stores
+// before the barrier, then one thread writes the L2 back (agent-scope
+// release), waits for the write-back, and bumps the counter; a waiter
+// invalidates its caches (agent-scope acquire) and waits for that before
+// releasing its workgroup.
+constexpr int kXcds = 8;
+constexpr int kFusedSpinLimit = 1 << 20;
+constexpr unsigned kWaitVmem = 0xF70;            // s_waitcnt vmcnt(0)
+
+struct FusedCtl {
+    int* claim;        // [kXcds] next index of each queue
+    int* done;         // [C/16]  gate/up tiles finished per M block
+    int* ready;        // [C/16]  the block's intermediate is complete
+    int* status;       // [1]     nonzero: a wait gave up
+};
+
+// The XCD this wave runs on (hardware register XCC_ID).
+__device__ __forceinline__ int xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcds - 1); }
+
+// Tile idx of a queue holding nb M blocks x nN tiles: groups of GROUP_M
+// blocks, M block fastest, as in ffn_tile.
+__device__ __forceinline__ void queue_tile(int idx, int nb, int nN, int* mb, int* nt) {
+    const int per_group = MOE_FFN_GROUP_M * nN;
+    const int g = idx / per_group;
+    const int first = g * MOE_FFN_GROUP_M;
+    const int gsize = min(nb - first, MOE_FFN_GROUP_M);
+    const int r = idx - g * per_group;
+    *mb = first + r % gsize;
+    *nt = r / gsize;
+}
+
+__global__ void __launch_bounds__(256) fused_reset_kernel(FusedCtl c, int nblk) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < kXcds) c.claim[i] = 0;
+    if (i == 0) c.status[0] = 0;
+    if (i < nblk) {
+        c.done[i] = 0;
+        c.ready[i] = 0;
+    }
+}
+
+template <int kW, bool kPacked, int BM, int PF>
+__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
+ffn_fused(FfnArgs a, uint16_t* __restrict__ h, Fp8Ws q, int nN1, int nN2, FusedCtl ctl) {
+    constexpr bool kQuant = Fmt<kW>::kQuantA;
+    __shared__ FfnSmem<BM> sm;
+    __shared__ int s_idx, s_last;
+    const int nmb = a.post_padded[0] / BM;
+    const int home = xcc_id();
+    const uint8_t* h_in = kQuant ? q.aq : (const uint8_t*)h;
+    for (int p = 0; p < kXcds; ++p) {
+        const int x = (home + p) & (kXcds - 1);
+        const int mb0 = (int)((int64_t)x * nmb / kXcds);
+        const int nb = (int)((int64_t)(x + 1) * nmb / kXcds) - mb0;
+        const int n1 = nb * nN1, n2 = nb * nN2;
+        for (;;) {
+            __syncthreads();                               // s_idx of the last tile is consumed
+            if (threadIdx.x == 0) s_idx = atomicAdd(ctl.claim + x, 1);
+            __syncthreads();
+            const int idx = s_idx;
+            if (idx >= n1 + n2) break;
+            int mb, nt;
+            if (idx < n1) {
+                queue_tile(idx, nb, nN1, &mb, &nt);
+                mb += mb0;
+                stage1_tile<kW, kPacked, BM, PF>(a, h, q, mb, nt, sm);
+                __builtin_amdgcn_s_waitcnt(kWaitVmem);    // this wave's stores and atomics are done
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+                    const int old = __hip_atomic_fetch_add(ctl.done + mb, 1, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                    s_last = old == nN1 - 1;
+                    if (s_last) {
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                        __builtin_amdgcn_s_waitcnt(kWaitVmem);
+                    }
+                }
+                __syncthreads();
+                if (s_last) {
+                    if constexpr (kQuant) {
+                        for (int i = 0; i < BM; ++i)
+                            requant_row(q.a, q.amax, a.I, q.aq, q.sa, (int64_t)mb * BM + i);
+                        __builtin_amdgcn_s_waitcnt(kWaitVmem);
+                        __syncthreads();
+                    }
+                    if (threadIdx.x == 0) {
+                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                        __builtin_amdgcn_s_waitcnt(kWaitVmem);
+                        __hip_atomic_store(ctl.ready + mb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            } else {
+                queue_tile(idx - n1, nb, nN2, &mb, &nt);
+                mb += mb0;
+                if (threadIdx.x == 0) {
+                    int polls = 0;
+                    while (__hip_atomic_load(ctl.ready + mb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                        if (++polls > kFusedSpinLimit) {
+                            atomicOr(ctl.status, 1);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(8);
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+                }
+                __syncthreads();
+                stage2_tile<kW, kPacked, BM, PF>(a, h_in, q.sa, mb, nt, sm);
+            }
+        }
+    }
+}
+
 // -------------------------------------------------------------------- host --
 static inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
 
-int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C) {
+static int64_t ffn_base_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C) {
     if (w_dtype == 0) return align256(C * I * 4);
     if (w_dtype == 1) return align256(C * I * 2);
     return align256(T * H) + align256(T * 4) + align256(C * I * 4) + align256(C * 4) + align256(C * I) +
            align256(C * 4);
+}
+
+// The one-stage schedule's control block: queue counters, status, and two
+// words per M block (blocks hold at least 16 rows).
+static int64_t fused_ctl_ints(int64_t C) { return kXcds + 8 + 2 * (C / 16 + 1); }
+
+int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C, int fused) {
+    return ffn_base_bytes(w_dtype, T, H, I, C) + (fused ? align256(fused_ctl_ints(C) * 4) : 0);
+}
+
+static FusedCtl fused_ctl(void* ws, int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C) {
+    int* p = (int*)((uint8_t*)ws + ffn_base_bytes(w_dtype, T, H, I, C));
+    FusedCtl c;
+    c.claim = p;
+    c.status = p + kXcds;
+    c.done = p + kXcds + 8;
+    c.ready = c.done + (C / 16 + 1);
+    return c;
+}
+
+// Workgroups of one kernel that fit on the device at once (the persistent grid).
+template <typename Kern>
+static int resident_workgroups(Kern kern) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFfnThreads, 0) != hipSuccess) return 0;
+    return cus * per_cu;
 }
 
 static Fp8Ws fp8_ws(void* ws, int64_t T, int64_t H, int64_t I, int64_t C) {
@@ -752,8 +942,45 @@ static Fp8Ws fp8_ws(void* ws, int64_t T, int64_t H, int64_t I, int64_t C) {
 }
 
 template <int kW, bool kPacked, int BM>
+static hipError_t launch_fused_bm(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev,
+                                  int w_dtype) {
+    constexpr int PF = ffn_pf<kW, BM>();
+    constexpr bool kQuant = Fmt<kW>::kQuantA;
+    const int nN1 = a.I / 128, nN2 = a.H / 256;
+    const int64_t nblk = a.C / BM;
+    const int64_t xrows = a.rows_sorted ? a.C : a.T;
+    hipError_t err;
+    Fp8Ws q{};
+    if ((err = record_stage(ev, 0, stream)) != hipSuccess) return err;
+    if (kQuant) {
+        q = fp8_ws(ws, xrows, a.H, a.I, a.C);
+        if (xrows > 0)
+            hipLaunchKernelGGL(quant_tokens_kernel, dim3((unsigned)xrows), dim3(kQuantThreads), 0, stream,
+                               (const uint16_t*)a.x, a.H, q.xq, q.sx, q.amax, a.C);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    const FusedCtl ctl = fused_ctl(ws, w_dtype, xrows, a.H, a.I, a.C);
+    hipLaunchKernelGGL(fused_reset_kernel, dim3((unsigned)((nblk + 255) / 256 + 1)), dim3(256), 0, stream, ctl,
+                       (int)nblk);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = record_stage(ev, 1, stream)) != hipSuccess) return err;
+    auto kern = ffn_fused<kW, kPacked, BM, PF>;
+    static const int resident = resident_workgroups(kern);
+    const int64_t tiles = nblk * (nN1 + nN2);
+    const int grid = (int)std::min<int64_t>(tiles, resident > 0 ? resident : 256);
+    if (grid > 0)
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kFfnThreads), 0, stream, a, (uint16_t*)ws, q, nN1, nN2, ctl);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // one launch: the gate/up interval covers both GEMMs, the others are empty
+    for (int i = 2; i < 5; ++i)
+        if ((err = record_stage(ev, i, stream)) != hipSuccess) return err;
+    return hipSuccess;
+}
+
+template <int kW, bool kPacked, int BM>
 static hipError_t launch_mfma_bm(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev) {
     constexpr int PF = ffn_pf<kW, BM>();
+    if (a.fused) return launch_fused_bm<kW, kPacked, BM>(a, ws, stream, ev, kW == kWBf16 ? 1 : kW == kWFp8 ? 2 : 3);
     constexpr bool kQuant = Fmt<kW>::kQuantA;
     const int nMB = (int)(a.C / BM);
     const int nN1 = a.I / 128, nN2 = a.H / 256;

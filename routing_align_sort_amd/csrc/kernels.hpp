@@ -52,13 +52,15 @@ struct FfnArgs {
     float* y_slots;            // [S,H] by slot, or [C,H] in the sorted row order
     int packed;                // weights in the layout written by launch_prepack
     int rows_sorted;           // x is [C,H] in the sorted row order, y written in that order
+    int fused;                 // both GEMMs in one persistent launch
 };
 // Largest activation operand (bytes of x, or of the intermediate, as one
 // GEMM reads it) of the matrix-core kernels: they address it with 32-bit
 // offsets.
 constexpr int64_t kFfnMaxOperandBytes = (int64_t)1 << 32;
 // Workspace layout per dtype path (bytes, each region 256-byte aligned).
-int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C);
+// T here is the number of x rows; fused adds the one-stage control block.
+int64_t ffn_workspace_bytes(int w_dtype, int64_t T, int64_t H, int64_t I, int64_t C, int fused);
 // ev (nullable) = 5 caller-created events recorded at the stage boundaries:
 // before quantisation, before gate/up, after gate/up, before down, after down.
 hipError_t launch_ffn_f32(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev);

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -186,3 +186,18 @@ def test_permute_and_row_layout_validation(lib):
     C = oracle.align_capacity(128, 8, 16)
     assert ws_sorted - ws_token == (C * 256 + 255) // 256 * 256 - 64 * 256 + \
         (C * 4 + 255) // 256 * 256 - (64 * 4 + 255) // 256 * 256   # x codes and scales per row
+
+
+def test_schedule_validation(lib):
+    P = ctypes.c_void_p
+    p = moe._FfnParams(64, 2, 8, 256, 256, 16, 1, 1, 0, 0, moe.MOE_SCHEDULE_FUSED)
+    two = moe._FfnParams(64, 2, 8, 256, 256, 16, 1, 1, 0, 0, moe.MOE_SCHEDULE_TWO_LAUNCH)
+    # the one-stage control block: queue counters, status and two words per block
+    C = oracle.align_capacity(128, 8, 16)
+    extra = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) - \
+        lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(two))
+    assert extra == ((8 + 8 + 2 * (C // 16 + 1)) * 4 + 255) // 256 * 256
+    p.schedule = 5
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1
+    p.schedule = moe.MOE_SCHEDULE_FUSED; p.w_dtype = p.x_dtype = 0
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1     # not for fp32
