@@ -76,7 +76,8 @@ def _mean(v):
     return sum(v) / len(v) if v else 0.0
 
 
-def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=1, graph=True):
+def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=1, graph=True,
+                    schedule="two_launch"):
     """Generate one workload, run `warmup` + `steps` layer passes with events
     around every kernel; return timings and what the roofline needs.
     rows="sorted": the layer permutes the token rows into the sorted order
@@ -99,7 +100,7 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=
                          w13_scale=s13, w2_scale=s2,
                          x_dtype=L["x"].dtype,
                          out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16,
-                         rows=rows)
+                         rows=rows, schedule=schedule)
     x, logits, bias = L["x"], L["logits"], L["bias"]
     inputs = [(x, logits)]
     for j in range(1, rotate):
@@ -300,6 +301,8 @@ def main():
     ap.add_argument("--rows", default="by_token", choices=("by_token", "sorted"),
                     help="sorted: permute the token rows into the sorted order before the FFN "
                          "and combine back through the inverse map")
+    ap.add_argument("--schedule", default="two_launch", choices=("two_launch", "fused"),
+                    help="fused: both GEMMs in one persistent launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the align-only and secondary-workload figures")
@@ -338,7 +341,7 @@ def main():
     cfg = ms.CONFIGS[args.workload]
     B = args.B or cfg["B"]
 
-    r = run_layer_timed(cfg, B, args.steps, args.warmup, dev, rows=args.rows)
+    r = run_layer_timed(cfg, B, args.steps, args.warmup, dev, rows=args.rows, schedule=args.schedule)
     summ = summarize(cfg, B, r)
     ab = algorithmic_bytes(cfg, r["ids"], r["E_slabs"])
     ms_per_step = r["wall_s"] / args.steps * 1e3
@@ -364,7 +367,8 @@ def main():
         "data": "synthetic (seeded counter-based generator; random-init expert weights)",
         "config": {"workload": describe(args.workload, cfg, B), "tokens": cfg["T"],
                    "experts": cfg["E"], "top_k": cfg["K"], "hidden": cfg["H"], "inter": cfg["I"],
-                   "block_size_m": B, "shared_expert": bool(cfg.get("shared")), "rows": args.rows},
+                   "block_size_m": B, "shared_expert": bool(cfg.get("shared")), "rows": args.rows,
+                   "schedule": args.schedule},
         "layer": summ,
         "roofline": roofline,
     }
@@ -411,6 +415,7 @@ def main():
         line["block_size_sweep"] = sweep
         line["permute_path"] = permute_path(dev)
         line["ffn_input_state"] = ffn_input_state(dev)
+        line["one_stage_schedule"] = one_stage(dev)
     if args.copy_probe:
         copy_probe(dev)
     if not args.no_cpu_baseline:
@@ -456,6 +461,27 @@ def permute_path(dev):
         }
         del r, base, layer
         torch.cuda.empty_cache()
+    return res
+
+
+def one_stage(dev):
+    """Layer step time with both GEMMs in one persistent launch against two
+    launches (back-to-back steps, no events), per workload at its block size."""
+    import torch
+
+    import moe_synth as ms
+    res = {}
+    for name, B in (("prefill_bf16", 64), ("prefill_fp8", 64), ("decode_bf16", 16), ("decode_fp4", 16),
+                    ("prefill_fp4", 64), ("prefill_bf16_512", 128), ("prefill_fp8_512", 128)):
+        cfg = ms.CONFIGS[name]
+        row = {"block_size_m": B}
+        for sched in ("two_launch", "fused"):
+            r = run_layer_timed(cfg, B, 10, 3, dev, graph=False, schedule=sched)
+            row[sched + "_us_per_step"] = round(r["wall_s"] / r["steps"] * 1e6, 1)
+            row[sched + "_ffn_event_us"] = round(sum(r["us"][k] for k in ("quant", "gate_up", "requant", "down")), 1)
+            del r
+            torch.cuda.empty_cache()
+        res[name] = row
     return res
 
 

@@ -807,6 +807,37 @@ __device__ __forceinline__ void queue_tile(int idx, int nb, int nN, int* mb, int
     *nt = r / gsize;
 }
 
+// The BM rows of M block mb: fp32 intermediate -> E4M3 codes + per-row
+// scales, by one workgroup, with the same arithmetic as requant_row.  The
+// row scales go through LDS first, then every thread converts 8 elements at a
+// time across all rows, so many loads are in flight at once.
+template <int BM>
+__device__ __forceinline__ void requant_block(const Fp8Ws& q, int I, int mb, float* inv_lds) {
+    const int tid = threadIdx.x;
+    if (tid < BM) {
+        const int64_t r = (int64_t)mb * BM + tid;
+        const float m = __uint_as_float(q.amax[r]);
+        inv_lds[tid] = (m > 0.f) ? 448.0f / m : 0.f;
+        q.sa[r] = (m > 0.f) ? m / 448.0f : 1.0f;
+    }
+    __syncthreads();
+    const int per_row = I / 8;
+    const float* base = q.a + (int64_t)mb * BM * I;
+    uint8_t* obase = q.aq + (int64_t)mb * BM * I;
+#pragma unroll 4
+    for (int c = tid; c < BM * per_row; c += kFfnThreads) {
+        const int i = c / per_row;
+        const int64_t off = (int64_t)i * I + (int64_t)(c - i * per_row) * 8;
+        const float inv = inv_lds[i];
+        const f32x4_t v0 = *(const f32x4_t*)(base + off);
+        const f32x4_t v1 = *(const f32x4_t*)(base + off + 4);
+        uint2 o;
+        o.x = e4m3_pack4(v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv);
+        o.y = e4m3_pack4(v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv);
+        *(uint2*)(obase + off) = o;
+    }
+}
+
 __global__ void __launch_bounds__(256) fused_reset_kernel(FusedCtl c, int nblk) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i < kXcds) c.claim[i] = 0;
@@ -822,21 +853,26 @@ __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
 ffn_fused(FfnArgs a, uint16_t* __restrict__ h, Fp8Ws q, int nN1, int nN2, FusedCtl ctl) {
     constexpr bool kQuant = Fmt<kW>::kQuantA;
     __shared__ FfnSmem<BM> sm;
-    __shared__ int s_idx, s_last;
+    __shared__ int s_idx, s_last, s_next;
     const int nmb = a.post_padded[0] / BM;
     const int home = xcc_id();
     const uint8_t* h_in = kQuant ? q.aq : (const uint8_t*)h;
-    for (int p = 0; p < kXcds; ++p) {
-        const int x = (home + p) & (kXcds - 1);
+    int x = home;
+    for (;;) {
         const int mb0 = (int)((int64_t)x * nmb / kXcds);
         const int nb = (int)((int64_t)(x + 1) * nmb / kXcds) - mb0;
         const int n1 = nb * nN1, n2 = nb * nN2;
-        for (;;) {
-            __syncthreads();                               // s_idx of the last tile is consumed
-            if (threadIdx.x == 0) s_idx = atomicAdd(ctl.claim + x, 1);
-            __syncthreads();
-            const int idx = s_idx;
-            if (idx >= n1 + n2) break;
+        __syncthreads();                                   // s_idx of the last queue is consumed
+        if (threadIdx.x == 0) s_idx = atomicAdd(ctl.claim + x, 1);
+        __syncthreads();
+        int idx = s_idx;
+        while (idx < n1 + n2) {
+            // claim the queue's next tile now, so the round trip overlaps this
+            // tile.  Within one queue this cannot deadlock: a workgroup that
+            // holds a gate/up tile ahead is itself on an earlier gate/up tile
+            // (which never waits), and nobody waits on a down tile.
+            int ahead = 0;
+            if (threadIdx.x == 0) ahead = atomicAdd(ctl.claim + x, 1);
             int mb, nt;
             if (idx < n1) {
                 queue_tile(idx, nb, nN1, &mb, &nt);
@@ -858,8 +894,7 @@ ffn_fused(FfnArgs a, uint16_t* __restrict__ h, Fp8Ws q, int nN1, int nN2, FusedC
                 __syncthreads();
                 if (s_last) {
                     if constexpr (kQuant) {
-                        for (int i = 0; i < BM; ++i)
-                            requant_row(q.a, q.amax, a.I, q.aq, q.sa, (int64_t)mb * BM + i);
+                        requant_block<BM>(q, a.I, mb, sm.rowscale);
                         __builtin_amdgcn_s_waitcnt(kWaitVmem);
                         __syncthreads();
                     }
@@ -887,7 +922,32 @@ ffn_fused(FfnArgs a, uint16_t* __restrict__ h, Fp8Ws q, int nN1, int nN2, FusedC
                 __syncthreads();
                 stage2_tile<kW, kPacked, BM, PF>(a, h_in, q.sa, mb, nt, sm);
             }
+            __syncthreads();                               // the tile's LDS reads are done
+            if (threadIdx.x == 0) s_idx = ahead;
+            __syncthreads();
+            idx = s_idx;
         }
+        // queue x is empty: one look at every queue's counter, then the
+        // nearest queue (from home) that still has tiles, or done
+        if (threadIdx.x < kWave) {
+            bool more = false;
+            if (threadIdx.x < kXcds) {
+                const int y = threadIdx.x;
+                const int nby = (int)((int64_t)(y + 1) * nmb / kXcds) - (int)((int64_t)y * nmb / kXcds);
+                more = __hip_atomic_load(ctl.claim + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       nby * (nN1 + nN2);
+            }
+            const uint64_t m = __ballot(more);
+            if (threadIdx.x == 0) {
+                int next = -1;
+                for (int p = 1; p <= kXcds && next < 0; ++p)
+                    if ((m >> ((home + p) & (kXcds - 1))) & 1) next = (home + p) & (kXcds - 1);
+                s_next = next;
+            }
+        }
+        __syncthreads();
+        x = s_next;
+        if (x < 0) break;
     }
 }
 
