@@ -84,6 +84,11 @@ def _load():
     lib.oracle_row_of_slot.restype = i32
     lib.oracle_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_unpermute_combine.restype = i32
+    lib.oracle_ffn_backward.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
+                                        P, P, P, P]
+    lib.oracle_ffn_backward.restype = i32
+    lib.oracle_route_backward.argtypes = [i32, i32, i32, i32, i32, f64, i32, P, P, P, P]
+    lib.oracle_route_backward.restype = i32
     lib.oracle_num_threads.restype = i32
     _lib = lib
     return lib
@@ -328,4 +333,51 @@ def unpermute_combine(y_perm, topk_weights, row_of_slot_):
     rc = _load().oracle_unpermute_combine(T, K, H, _ptr(y), _ptr(w), _ptr(rs), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_unpermute_combine: invalid arguments")
+    return out
+
+
+def ffn_backward(x, w13, w2, topk_ids, topk_weights, y_slots, d_out, *, w_dtype, x_dtype, inter):
+    """Gradients of the layer (expert FFNs + combine) for an upstream d_out [T,H]:
+    (dx [T,H], dW13 [E,2I,H], dW2 [E,H,I], d_w [T,K]), all float64.
+    w_dtype / x_dtype "f32" or "bf16" (bits); inter "f64" (no rounding) or "bf16"."""
+    wcode, wnp = _WDT[w_dtype]
+    xcode, xnp = _XDT[x_dtype]
+    if wcode > 1:
+        raise ValueError("the backward covers fp32 and bf16 weights")
+    x = _c(x, xnp)
+    w13 = _c(w13, wnp)
+    w2 = _c(w2, wnp)
+    ids = _c(topk_ids, np.int32)
+    w = _c(topk_weights, np.float32)
+    y = _c(y_slots, np.float32)
+    dout = _c(d_out, np.float32)
+    T, H = x.shape
+    K = ids.shape[1]
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    dx = np.empty((T, H), np.float64)
+    dw13 = np.empty((E, I2, H), np.float64)
+    dw2 = np.empty((E, H, I), np.float64)
+    dwk = np.empty((T, K), np.float64)
+    rc = _load().oracle_ffn_backward(T, K, E, H, I, wcode, xcode, _INTER[inter], _ptr(x), _ptr(w13),
+                                     _ptr(w2), _ptr(ids), _ptr(w), _ptr(y), _ptr(dout), _ptr(dx),
+                                     _ptr(dw13), _ptr(dw2), _ptr(dwk))
+    if rc != 0:
+        raise ValueError("oracle_ffn_backward: invalid arguments")
+    return dx, dw13, dw2, dwk
+
+
+def route_backward(logits, topk_ids, d_w, K: int, *, score="softmax", renormalize=True,
+                   routed_scaling=1.0, append_shared=False):
+    """d_logits [T,E] (float64) for d_w over the routed columns, the selection held fixed."""
+    lg = _c(logits, np.float32)
+    ids = _c(topk_ids, np.int32)
+    dw = _c(d_w, np.float32)
+    T, E = lg.shape
+    out = np.empty((T, E), np.float64)
+    rc = _load().oracle_route_backward(T, E, K, {"softmax": 0, "sigmoid": 1}[score], int(bool(renormalize)),
+                                       float(routed_scaling), int(bool(append_shared)), _ptr(lg),
+                                       _ptr(ids), _ptr(dw), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_route_backward: invalid arguments")
     return out

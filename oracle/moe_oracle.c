@@ -562,3 +562,151 @@ int oracle_unpermute_combine(int T, int K, int H, const float *y_perm, const flo
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward (training)                                                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * [DIG] the Megatron section (for training, the permute gets its gradient
+ * operation, unpermute) and the TransformerEngine paragraph; [XMOE] abstract
+ * (MoE training on AMD GPUs).  The pages give no formulas, so the backward is
+ * the exact derivative of the forward above, in double:
+ *   d_w[t,k]   = sum_h d_out[t,h] * y_slots[t*K+k,h]      (the forward's y)
+ *   d_y        = w[t,k] * d_out[t]
+ *   dW2[e,h,j] += d_y[h] * a~_j       a~ = the intermediate as the forward
+ *                                      rounds it (inter 0: none, 2: bf16)
+ *   d_a_j      = sum_h d_y[h] * W2[e,h,j]   (the rounding passed straight
+ *                                             through: d a~ / d a = 1)
+ *   d_g_j      = d_a_j * u_j * SiLU'(g_j),  SiLU'(g) = s(g) (1 + g (1 - s(g)))
+ *   d_u_j      = d_a_j * SiLU(g_j)
+ *   dW13[e,j,h] += d_g_j x_h,  dW13[e,I+j,h] += d_u_j x_h
+ *   dx[t,h]    += sum_j d_g_j W13[e,j,h] + d_u_j W13[e,I+j,h]
+ * over every slot with an id in [0,E).  fp32 or bf16 weights and activations
+ * (w_dtype = x_dtype 0 or 1), decoded exactly.  Outputs are overwritten.
+ */
+int oracle_ffn_backward(int T, int K, int E, int H, int I, int w_dtype, int x_dtype, int inter,
+                        const void *x, const void *w13, const void *w2, const int32_t *topk_ids,
+                        const float *topk_weights, const float *y_slots, const float *d_out,
+                        double *dx, double *dw13, double *dw2, double *d_w)
+{
+    if (T < 0 || K < 1 || E < 1 || H < 1 || I < 1) return 1;
+    if (w_dtype < 0 || w_dtype > 1 || x_dtype < 0 || x_dtype > 1) return 1;
+    if (inter != 0 && inter != 2) return 1;
+    memset(dx, 0, sizeof(double) * (size_t)T * H);
+    memset(dw13, 0, sizeof(double) * (size_t)E * 2 * I * H);
+    memset(dw2, 0, sizeof(double) * (size_t)E * H * I);
+    double *xt = (double *)malloc(sizeof(double) * (size_t)H);
+    double *g = (double *)malloc(sizeof(double) * (size_t)I);
+    double *u = (double *)malloc(sizeof(double) * (size_t)I);
+    double *at = (double *)malloc(sizeof(double) * (size_t)I);
+    double *dy = (double *)malloc(sizeof(double) * (size_t)H);
+    double *da = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int t = 0; t < T; t++) {
+        for (int h = 0; h < H; h++) {
+            size_t xi = (size_t)t * H + h;
+            xt[h] = x_dtype == 0 ? (double)((const float *)x)[xi] : oracle_bf16_decode(((const uint16_t *)x)[xi]);
+        }
+        for (int k = 0; k < K; k++) {
+            int64_t i = (int64_t)t * K + k;
+            int e = topk_ids[i];
+            d_w[i] = 0.0;
+            if (e < 0 || e >= E) continue;
+            double dwi = 0.0;
+            for (int h = 0; h < H; h++) dwi += (double)d_out[(size_t)t * H + h] * (double)y_slots[i * H + h];
+            d_w[i] = dwi;
+            for (int h = 0; h < H; h++) dy[h] = (double)topk_weights[i] * (double)d_out[(size_t)t * H + h];
+            /* the forward's gate, up and intermediate */
+            for (int j = 0; j < I; j++) {
+                size_t rg = (size_t)e * 2 * I + j, ru = rg + I;
+                double gj = 0.0, uj = 0.0;
+                for (int h = 0; h < H; h++) {
+                    gj += xt[h] * load_w(w_dtype, w13, NULL, rg, h, H);
+                    uj += xt[h] * load_w(w_dtype, w13, NULL, ru, h, H);
+                }
+                g[j] = gj;
+                u[j] = uj;
+                double a = gj / (1.0 + exp(-gj)) * uj;
+                at[j] = inter == 2 ? oracle_bf16_decode(oracle_bf16_encode((float)a)) : a;
+            }
+            /* down projection: weight gradient and the intermediate's gradient */
+            for (int j = 0; j < I; j++) da[j] = 0.0;
+            for (int h = 0; h < H; h++) {
+                size_t rd = (size_t)e * H + h;
+                for (int j = 0; j < I; j++) {
+                    dw2[rd * I + j] += dy[h] * at[j];
+                    da[j] += dy[h] * load_w(w_dtype, w2, NULL, rd, j, I);
+                }
+            }
+            /* SwiGLU, then the gate/up projections */
+            for (int j = 0; j < I; j++) {
+                double s = 1.0 / (1.0 + exp(-g[j]));
+                double dg = da[j] * u[j] * s * (1.0 + g[j] * (1.0 - s));
+                double du = da[j] * g[j] * s;
+                size_t rg = (size_t)e * 2 * I + j, ru = rg + I;
+                for (int h = 0; h < H; h++) {
+                    dw13[rg * H + h] += dg * xt[h];
+                    dw13[ru * H + h] += du * xt[h];
+                    dx[(size_t)t * H + h] += dg * load_w(w_dtype, w13, NULL, rg, h, H) +
+                                             du * load_w(w_dtype, w13, NULL, ru, h, H);
+                }
+            }
+        }
+    }
+    free(xt); free(g); free(u); free(at); free(dy); free(da);
+    return 0;
+}
+
+/*
+ * Routing backward: d_logits [T,E] from d_w [T,K], the selection held fixed
+ * (it is piecewise constant in the logits; the bias only selects).  With
+ * s_e = softmax(logits)_e or sigmoid(logits_e) in double, the forward's
+ * weights of the routed columns are w_k = c * s_{e_k} / N, c = routed_scaling,
+ * N = the sum of s over the chosen experts when renormalising, else 1.  An
+ * appended shared column (id E, weight 1) has no gradient.
+ *   dL/ds_e = c * (d_w_k / N - [renormalise] sum_j d_w_j s_{e_j} / N^2)  for e = e_k
+ *   softmax: d l_i = s_i (dL/ds_i - sum_e dL/ds_e s_e);  sigmoid: d l_i = dL/ds_i s_i (1 - s_i)
+ */
+int oracle_route_backward(int T, int E, int K, int score_mode, int renormalize, double routed_scaling,
+                          int append_shared, const float *logits, const int32_t *topk_ids,
+                          const float *d_w, double *d_logits)
+{
+    if (T < 0 || E < 1 || K < 1) return 1;
+    int KO = K + (append_shared ? 1 : 0);
+    double *s = (double *)malloc(sizeof(double) * (size_t)E);
+    double *gs = (double *)malloc(sizeof(double) * (size_t)E);
+    for (int t = 0; t < T; t++) {
+        const float *l = logits + (size_t)t * E;
+        if (score_mode == 0) {
+            double mx = -INFINITY, z = 0.0;
+            for (int e = 0; e < E; e++) if ((double)l[e] > mx) mx = (double)l[e];
+            for (int e = 0; e < E; e++) { s[e] = exp((double)l[e] - mx); z += s[e]; }
+            for (int e = 0; e < E; e++) s[e] /= z;
+        } else {
+            for (int e = 0; e < E; e++) s[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+        }
+        double N = 1.0, sdw = 0.0;
+        if (renormalize) {
+            N = 0.0;
+            for (int k = 0; k < K; k++) N += s[topk_ids[(size_t)t * KO + k]];
+        }
+        for (int k = 0; k < K; k++)
+            sdw += (double)d_w[(size_t)t * KO + k] * s[topk_ids[(size_t)t * KO + k]];
+        for (int e = 0; e < E; e++) gs[e] = 0.0;
+        for (int k = 0; k < K; k++) {
+            int e = topk_ids[(size_t)t * KO + k];
+            double v = (double)d_w[(size_t)t * KO + k] / N;
+            if (renormalize) v -= sdw / (N * N);
+            gs[e] += routed_scaling * v;
+        }
+        double *dl = d_logits + (size_t)t * E;
+        if (score_mode == 0) {
+            double dot = 0.0;
+            for (int e = 0; e < E; e++) dot += gs[e] * s[e];
+            for (int e = 0; e < E; e++) dl[e] = s[e] * (gs[e] - dot);
+        } else {
+            for (int e = 0; e < E; e++) dl[e] = gs[e] * s[e] * (1.0 - s[e]);
+        }
+    }
+    free(s); free(gs);
+    return 0;
+}
