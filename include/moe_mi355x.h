@@ -333,6 +333,55 @@ moe_status_t moe_unpermute_combine(int32_t T, int32_t K, int32_t H, const float 
                                    const float *topk_weights, const int32_t *row_of_slot,
                                    int32_t out_dtype, void *out, void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Backward (training)                                                       */
+/* ------------------------------------------------------------------------ */
+/*
+ * Defined by the dignews.cc page's Megatron section (for training, the
+ * permute gets its gradient operation, unpermute) and TransformerEngine
+ * paragraph, and the X-MoE abstract (MoE training on AMD GPUs).  The pages
+ * give no formulas: these are the exact derivatives of the forward above,
+ * with the top-k selection held fixed and the intermediate's rounding passed
+ * straight through.
+ *
+ * moe_ffn_backward, for the upstream gradient d_out of moe_combine's output:
+ *   d_topk_weights[t,k] = <d_out[t], y_slots[t*K+k]>     (0 for skipped slots)
+ *   dy = topk_weights[t,k] * d_out[t],  a~ = the bf16 intermediate
+ *   dw2[e]  = sum over e's slots of dy^T a~
+ *   d_a = dy w2[e],  d_g = d_a u SiLU'(g),  d_u = d_a SiLU(g)
+ *   dw13[e] = sum over e's slots of [d_g d_u]^T x
+ *   dx[t]   = sum over t's slots of [d_g d_u] w13[e]
+ * p as for moe_grouped_ffn with bf16 weights and activations, canonical
+ * weight layout, MOE_ROWS_BY_TOKEN, MOE_SCHEDULE_TWO_LAUNCH; B in
+ * {64,128,256}; H and I multiples of 256.  x, w13, w2, topk_ids,
+ * topk_weights: the forward's inputs; sorted_token_ids, expert_ids,
+ * num_tokens_post_padded and expert_offsets [E+1]: moe_align_sort's outputs
+ * (expert_offsets required here); y_slots: the forward's moe_grouped_ffn
+ * output; d_out device fp32 [T,H].  Outputs (device fp32, overwritten): dx
+ * [T,H], dw13 [E,2I,H], dw2 [E,H,I], d_topk_weights [T,K].  GEMM operands are
+ * bf16 (dy and [d_g d_u] rounded once), accumulation fp32.  workspace: at
+ * least moe_ffn_backward_workspace_bytes(p) bytes, 256-byte aligned.
+ *
+ * moe_route_backward: d_logits [T,E] (device fp32) for d_topk_weights over
+ * the routed columns (an appended shared column has no gradient):
+ *   s = softmax(logits) or sigmoid(logits) (double), w_k = c s_{e_k} / N,
+ *   N = sum of s over the chosen experts when renormalising, else 1;
+ *   dL/ds_e = c (d_w_k / N - [renormalise] sum_j d_w_j s_{e_j} / N^2);
+ *   softmax: d_logits = s (dL/ds - <dL/ds, s>); sigmoid: dL/ds s (1 - s).
+ * p as given to moe_route_topk; topk_ids [T,K(+1)] its output.
+ */
+int64_t moe_ffn_backward_workspace_bytes(const moe_ffn_params_t *p);
+moe_status_t moe_ffn_backward(const moe_ffn_params_t *p, const void *x, const void *w13, const void *w2,
+                              const int32_t *topk_ids, const float *topk_weights,
+                              const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                              const int32_t *num_tokens_post_padded, const int32_t *expert_offsets,
+                              const float *y_slots, const float *d_out, float *dx, float *dw13,
+                              float *dw2, float *d_topk_weights, void *workspace,
+                              size_t workspace_bytes, void *stream);
+moe_status_t moe_route_backward(const moe_route_params_t *p, const float *logits,
+                                const int32_t *topk_ids, const float *d_topk_weights, float *d_logits,
+                                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

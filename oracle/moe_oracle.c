@@ -592,30 +592,32 @@ int oracle_ffn_backward(int T, int K, int E, int H, int I, int w_dtype, int x_dt
     if (T < 0 || K < 1 || E < 1 || H < 1 || I < 1) return 1;
     if (w_dtype < 0 || w_dtype > 1 || x_dtype < 0 || x_dtype > 1) return 1;
     if (inter != 0 && inter != 2) return 1;
-    memset(dx, 0, sizeof(double) * (size_t)T * H);
-    memset(dw13, 0, sizeof(double) * (size_t)E * 2 * I * H);
-    memset(dw2, 0, sizeof(double) * (size_t)E * H * I);
-    double *xt = (double *)malloc(sizeof(double) * (size_t)H);
-    double *g = (double *)malloc(sizeof(double) * (size_t)I);
-    double *u = (double *)malloc(sizeof(double) * (size_t)I);
-    double *at = (double *)malloc(sizeof(double) * (size_t)I);
-    double *dy = (double *)malloc(sizeof(double) * (size_t)H);
-    double *da = (double *)malloc(sizeof(double) * (size_t)I);
-    for (int t = 0; t < T; t++) {
-        for (int h = 0; h < H; h++) {
-            size_t xi = (size_t)t * H + h;
-            xt[h] = x_dtype == 0 ? (double)((const float *)x)[xi] : oracle_bf16_decode(((const uint16_t *)x)[xi]);
-        }
-        for (int k = 0; k < K; k++) {
-            int64_t i = (int64_t)t * K + k;
+    int64_t S = (int64_t)T * K;
+    /* per slot: the forward's intermediate and the slot's gradient vectors */
+    double *xd = (double *)malloc(sizeof(double) * (size_t)T * H);
+    double *at = (double *)calloc((size_t)S * I, sizeof(double));
+    double *dg = (double *)calloc((size_t)S * I, sizeof(double));
+    double *du = (double *)calloc((size_t)S * I, sizeof(double));
+    double *dy = (double *)calloc((size_t)S * H, sizeof(double));
+    if (!xd || !at || !dg || !du || !dy) { free(xd); free(at); free(dg); free(du); free(dy); return 1; }
+    for (int64_t q = 0; q < (int64_t)T * H; q++)
+        xd[q] = x_dtype == 0 ? (double)((const float *)x)[q] : oracle_bf16_decode(((const uint16_t *)x)[q]);
+#pragma omp parallel
+    {
+        double *g = (double *)malloc(sizeof(double) * (size_t)I);
+        double *u = (double *)malloc(sizeof(double) * (size_t)I);
+        double *da = (double *)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic)
+        for (int64_t i = 0; i < S; i++) {
+            int t = (int)(i / K);
             int e = topk_ids[i];
             d_w[i] = 0.0;
             if (e < 0 || e >= E) continue;
+            const double *xt = xd + (size_t)t * H;
             double dwi = 0.0;
             for (int h = 0; h < H; h++) dwi += (double)d_out[(size_t)t * H + h] * (double)y_slots[i * H + h];
             d_w[i] = dwi;
-            for (int h = 0; h < H; h++) dy[h] = (double)topk_weights[i] * (double)d_out[(size_t)t * H + h];
-            /* the forward's gate, up and intermediate */
+            for (int h = 0; h < H; h++) dy[i * H + h] = (double)topk_weights[i] * (double)d_out[(size_t)t * H + h];
             for (int j = 0; j < I; j++) {
                 size_t rg = (size_t)e * 2 * I + j, ru = rg + I;
                 double gj = 0.0, uj = 0.0;
@@ -626,33 +628,62 @@ int oracle_ffn_backward(int T, int K, int E, int H, int I, int w_dtype, int x_dt
                 g[j] = gj;
                 u[j] = uj;
                 double a = gj / (1.0 + exp(-gj)) * uj;
-                at[j] = inter == 2 ? oracle_bf16_decode(oracle_bf16_encode((float)a)) : a;
+                at[i * I + j] = inter == 2 ? oracle_bf16_decode(oracle_bf16_encode((float)a)) : a;
+                da[j] = 0.0;
             }
-            /* down projection: weight gradient and the intermediate's gradient */
-            for (int j = 0; j < I; j++) da[j] = 0.0;
-            for (int h = 0; h < H; h++) {
-                size_t rd = (size_t)e * H + h;
-                for (int j = 0; j < I; j++) {
-                    dw2[rd * I + j] += dy[h] * at[j];
-                    da[j] += dy[h] * load_w(w_dtype, w2, NULL, rd, j, I);
-                }
-            }
-            /* SwiGLU, then the gate/up projections */
+            for (int h = 0; h < H; h++)
+                for (int j = 0; j < I; j++)
+                    da[j] += dy[i * H + h] * load_w(w_dtype, w2, NULL, (size_t)e * H + h, j, I);
             for (int j = 0; j < I; j++) {
-                double s = 1.0 / (1.0 + exp(-g[j]));
-                double dg = da[j] * u[j] * s * (1.0 + g[j] * (1.0 - s));
-                double du = da[j] * g[j] * s;
+                double sg = 1.0 / (1.0 + exp(-g[j]));
+                dg[i * I + j] = da[j] * u[j] * sg * (1.0 + g[j] * (1.0 - sg));
+                du[i * I + j] = da[j] * g[j] * sg;
+            }
+        }
+        free(g); free(u); free(da);
+    }
+    /* weight gradients: each element summed over the expert's slots in ascending order */
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t r = 0; r < (int64_t)E * H; r++) {
+        int e = (int)(r / H), h = (int)(r % H);
+        double *out = dw2 + (size_t)r * I;
+        for (int j = 0; j < I; j++) out[j] = 0.0;
+        for (int64_t i = 0; i < S; i++) {
+            if (topk_ids[i] != e) continue;
+            for (int j = 0; j < I; j++) out[j] += dy[i * H + h] * at[i * I + j];
+        }
+    }
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t r = 0; r < (int64_t)E * 2 * I; r++) {
+        int e = (int)(r / (2 * I)), j = (int)(r % (2 * I));
+        const double *src = j < I ? dg : du;
+        int jj = j < I ? j : j - I;
+        double *out = dw13 + (size_t)r * H;
+        for (int h = 0; h < H; h++) out[h] = 0.0;
+        for (int64_t i = 0; i < S; i++) {
+            if (topk_ids[i] != e) continue;
+            const double *xt = xd + (size_t)(i / K) * H;
+            for (int h = 0; h < H; h++) out[h] += src[i * I + jj] * xt[h];
+        }
+    }
+    /* the activations' gradient: slots in ascending k, then j */
+#pragma omp parallel for schedule(dynamic)
+    for (int t = 0; t < T; t++) {
+        double *out = dx + (size_t)t * H;
+        for (int h = 0; h < H; h++) out[h] = 0.0;
+        for (int k = 0; k < K; k++) {
+            int64_t i = (int64_t)t * K + k;
+            int e = topk_ids[i];
+            if (e < 0 || e >= E) continue;
+            for (int j = 0; j < I; j++) {
                 size_t rg = (size_t)e * 2 * I + j, ru = rg + I;
-                for (int h = 0; h < H; h++) {
-                    dw13[rg * H + h] += dg * xt[h];
-                    dw13[ru * H + h] += du * xt[h];
-                    dx[(size_t)t * H + h] += dg * load_w(w_dtype, w13, NULL, rg, h, H) +
-                                             du * load_w(w_dtype, w13, NULL, ru, h, H);
-                }
+                for (int h = 0; h < H; h++)
+                    out[h] += dg[i * I + j] * load_w(w_dtype, w13, NULL, rg, h, H) +
+                              du[i * I + j] * load_w(w_dtype, w13, NULL, ru, h, H);
             }
         }
     }
-    free(xt); free(g); free(u); free(at); free(dy); free(da);
+    free(xd); free(at); free(dg); free(du); free(dy);
     return 0;
 }
 

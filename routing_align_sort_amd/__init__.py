@@ -47,7 +47,8 @@ class _FfnParams(ctypes.Structure):
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
             "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_prepack_weights",
-            "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine")
+            "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine",
+            "moe_ffn_backward_workspace_bytes", "moe_ffn_backward", "moe_route_backward")
 
 
 def load_library(path: str = LIB_PATH):
@@ -87,6 +88,12 @@ def load_library(path: str = LIB_PATH):
     lib.moe_permute_rows.restype = i32
     lib.moe_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_unpermute_combine.restype = i32
+    lib.moe_ffn_backward_workspace_bytes.argtypes = [ctypes.POINTER(_FfnParams)]
+    lib.moe_ffn_backward_workspace_bytes.restype = i64
+    lib.moe_ffn_backward.argtypes = [ctypes.POINTER(_FfnParams)] + [P] * 16 + [sz, P]
+    lib.moe_ffn_backward.restype = i32
+    lib.moe_route_backward.argtypes = [ctypes.POINTER(_RouteParams), P, P, P, P, P]
+    lib.moe_route_backward.restype = i32
     _lib = lib
     return lib
 
@@ -389,6 +396,69 @@ def moe_unpermute_combine(y_perm, topk_weights, row_of_slot, *, out_dtype=torch.
     return out
 
 
+# ---------------------------------------------------------------- backward --
+def moe_ffn_backward_workspace_bytes(T, K, E, H, I, B) -> int:
+    p = _ffn_params(T, K, E, H, I, B, torch.bfloat16, torch.bfloat16)
+    c = int(load_library().moe_ffn_backward_workspace_bytes(ctypes.byref(p)))
+    if c < 0:
+        raise MoEError("moe_ffn_backward_workspace_bytes", MOE_ERR_UNSUPPORTED)
+    return c
+
+
+def moe_ffn_backward(x, w13, w2, topk_ids, topk_weights, sorted_token_ids, expert_ids,
+                     num_tokens_post_padded, expert_offsets, y_slots, d_out, *, B, workspace=None,
+                     stream=None):
+    """Gradients of moe_combine(moe_grouped_ffn(...)) for the upstream d_out [T,H]
+    (bf16 weights, canonical layout): returns (dx, dw13, dw2, d_topk_weights), fp32."""
+    lib = load_library()
+    T, H = x.shape
+    E, I2, _ = w13.shape
+    I = I2 // 2
+    K = topk_ids.shape[1]
+    for t, n, dt in ((x, "x", torch.bfloat16), (w13, "w13", torch.bfloat16), (w2, "w2", torch.bfloat16),
+                     (topk_ids, "topk_ids", torch.int32), (topk_weights, "topk_weights", torch.float32),
+                     (sorted_token_ids, "sorted_token_ids", torch.int32), (expert_ids, "expert_ids", torch.int32),
+                     (num_tokens_post_padded, "num_tokens_post_padded", torch.int32),
+                     (expert_offsets, "expert_offsets", torch.int32), (y_slots, "y_slots", torch.float32),
+                     (d_out, "d_out", torch.float32)):
+        _need(t, dt, n)
+    dev = x.device
+    dx = torch.empty((T, H), dtype=torch.float32, device=dev)
+    dw13 = torch.empty((E, I2, H), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((E, H, I), dtype=torch.float32, device=dev)
+    dwk = torch.empty((T, K), dtype=torch.float32, device=dev)
+    p = _ffn_params(T, K, E, H, I, B, torch.bfloat16, torch.bfloat16)
+    need = moe_ffn_backward_workspace_bytes(T, K, E, H, I, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("moe_ffn_backward", lib.moe_ffn_backward(
+        ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
+        _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(expert_offsets),
+        _ptr(y_slots), _ptr(d_out), _ptr(dx), _ptr(dw13), _ptr(dw2), _ptr(dwk), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return dx, dw13, dw2, dwk
+
+
+def moe_route_backward(logits, topk_ids, d_topk_weights, K, *, score="softmax", renormalize=True,
+                       routed_scaling=1.0, append_shared=False, d_logits=None, stream=None):
+    """d_logits [T,E] fp32 for the gradient of the routed columns' weights (selection fixed)."""
+    lib = load_library()
+    T, E = logits.shape
+    _need(logits, torch.float32, "logits")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(d_topk_weights, torch.float32, "d_topk_weights", topk_ids.numel())
+    if d_logits is None:
+        d_logits = torch.empty((T, E), dtype=torch.float32, device=logits.device)
+    _need(d_logits, torch.float32, "d_logits", T * E)
+    p = _RouteParams(T, E, K, {"softmax": 0, "sigmoid": 1}[score], 1, 1, int(bool(renormalize)),
+                     float(routed_scaling), int(bool(append_shared)))
+    _check("moe_route_backward", lib.moe_route_backward(ctypes.byref(p), _ptr(logits), _ptr(topk_ids),
+                                                        _ptr(d_topk_weights), _ptr(d_logits),
+                                                        _stream(stream)))
+    return d_logits
+
+
 # -------------------------------------------------------------- the layer --
 class MoELayer:
     """The four calls of one MoE layer over preallocated buffers.
@@ -409,6 +479,7 @@ class MoELayer:
             packed = w13.dtype != torch.float32
         self.packed = bool(packed)
         E, I, H = weight_dims(w13)
+        self.w13_canonical, self.w2_canonical = w13, w2        # what the backward reads
         if self.packed:
             w13, w2 = moe_prepack_weights(w13, w2)
             if w13.dtype == FP4:
@@ -489,6 +560,17 @@ class MoELayer:
                                          out_dtype=self.out_dtype, out=self.out)
         return moe_combine(self.y_slots, self.topk_weights, self.topk_ids, self.E_slabs,
                            out_dtype=self.out_dtype, out=self.out)
+
+    def backward(self, x, logits, d_out, workspace=None):
+        """Gradients after forward(x, logits): (dx, dw13, dw2, d_logits), fp32."""
+        dx, dw13, dw2, dwk = moe_ffn_backward(
+            x, self.w13_canonical, self.w2_canonical, self.topk_ids, self.topk_weights, self.sorted,
+            self.expert_ids, self.ntpp, self.offsets, self.y_slots, d_out, B=self.B, workspace=workspace)
+        d_logits = moe_route_backward(logits, self.topk_ids, dwk, self.K, score=self.route_kw["score"],
+                                      renormalize=self.route_kw["renormalize"],
+                                      routed_scaling=self.route_kw["routed_scaling"],
+                                      append_shared=self.shared)
+        return dx, dw13, dw2, d_logits, dwk
 
     def forward(self, x, logits, bias=None):
         self.route(logits, bias)

@@ -208,6 +208,70 @@ moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, 
                        reinterpret_cast<hipEvent_t const*>(events));
 }
 
+static moe_status_t bwd_check(const moe_ffn_params_t* p) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 0 || p->K < 1 || p->E < 1 || p->H < 1 || p->I < 1 || !align_args_ok(p->T, p->K, p->E, p->B))
+        return MOE_ERR_INVALID_ARG;
+    if (p->w_dtype != MOE_BF16 || p->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->weight_layout != MOE_LAYOUT_CANONICAL || p->row_layout != MOE_ROWS_BY_TOKEN ||
+        p->schedule != MOE_SCHEDULE_TWO_LAUNCH)
+        return MOE_ERR_UNSUPPORTED;
+    if ((p->B != 64 && p->B != 128 && p->B != 256) || p->E > kAlignMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (p->H % 256 || p->I % 256) return MOE_ERR_UNSUPPORTED;
+    const int64_t C = capacity((int64_t)p->T * p->K, p->E, p->B);
+    // 32-bit activation offsets inside a GEMM tile: 256 rows of the transposed activations
+    if (C * 2 * 256 > kFfnMaxOperandBytes || C * p->H * 2 > kFfnMaxOperandBytes) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int64_t moe_ffn_backward_workspace_bytes(const moe_ffn_params_t* p) {
+    if (bwd_check(p) != MOE_OK) return -1;
+    const int64_t C = capacity((int64_t)p->T * p->K, p->E, p->B);
+    return ffn_backward_workspace_bytes(p->T, p->K, p->E, p->H, p->I, C);
+}
+
+moe_status_t moe_ffn_backward(const moe_ffn_params_t* p, const void* x, const void* w13, const void* w2,
+                              const int32_t* topk_ids, const float* topk_weights, const int32_t* sorted_token_ids,
+                              const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                              const int32_t* expert_offsets, const float* y_slots, const float* d_out, float* dx,
+                              float* dw13, float* dw2, float* d_topk_weights, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    const moe_status_t st = bwd_check(p);
+    if (st != MOE_OK) return st;
+    if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !sorted_token_ids || !expert_ids ||
+        !num_tokens_post_padded || !expert_offsets || !y_slots || !d_out || !dx || !dw13 || !dw2 ||
+        !d_topk_weights)
+        return MOE_ERR_INVALID_ARG;
+    const int64_t S = (int64_t)p->T * p->K;
+    const int64_t C = capacity(S, p->E, p->B);
+    const int64_t need = ffn_backward_workspace_bytes(p->T, p->K, p->E, p->H, p->I, C);
+    if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    BwdArgs a;
+    a.T = p->T; a.K = p->K; a.E = p->E; a.H = p->H; a.I = p->I; a.B = p->B; a.S = S; a.C = C;
+    a.x = (const uint16_t*)x; a.w13 = (const uint16_t*)w13; a.w2 = (const uint16_t*)w2;
+    a.ids = topk_ids; a.w = topk_weights; a.sorted = sorted_token_ids; a.expert_ids = expert_ids;
+    a.post_padded = num_tokens_post_padded; a.offsets = expert_offsets; a.y_slots = y_slots; a.d_out = d_out;
+    a.dx = dx; a.dw13 = dw13; a.dw2 = dw2; a.d_w = d_topk_weights;
+    return from_hip(launch_ffn_backward(a, workspace, as_stream(stream)));
+}
+
+moe_status_t moe_route_backward(const moe_route_params_t* p, const float* logits, const int32_t* topk_ids,
+                                const float* d_topk_weights, float* d_logits, void* stream) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 0 || p->E < 1 || p->K < 1 || p->K > p->E || (p->score != MOE_SCORE_SOFTMAX && p->score != MOE_SCORE_SIGMOID))
+        return MOE_ERR_INVALID_ARG;
+    if (p->E > kRouteMaxExperts || p->K > kRouteMaxK) return MOE_ERR_UNSUPPORTED;
+    if (p->T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !d_topk_weights || !d_logits) return MOE_ERR_INVALID_ARG;
+    RouteArgs a;
+    a.T = p->T; a.E = p->E; a.K = p->K; a.score = p->score;
+    a.n_group = p->n_group; a.topk_group = p->topk_group;
+    a.renormalize = p->renormalize != 0; a.append_shared = p->append_shared != 0;
+    a.routed_scaling = p->routed_scaling;
+    a.logits = logits; a.bias = nullptr; a.topk_ids = const_cast<int32_t*>(topk_ids); a.topk_weights = nullptr;
+    return from_hip(launch_route_backward(a, d_topk_weights, d_logits, as_stream(stream)));
+}
+
 moe_status_t moe_permute_rows(const void* x, int32_t T, int32_t K, int32_t E, int32_t B, int64_t row_bytes,
                               const int32_t* topk_ids, const int32_t* sorted_token_ids,
                               const int32_t* num_tokens_post_padded, const float* x_scale, void* x_perm,

@@ -1105,6 +1105,90 @@ hipError_t launch_ffn_fp4(const FfnArgs& a, void* ws, hipStream_t stream, hipEve
     return launch_mfma<kWFp4>(a, ws, stream, ev);
 }
 
+// ------------------------------------------------------- backward GEMMs --
+// Grouped NT GEMM for the backward: C[m][n] = sum_k A[m][k] * B[n][k], bf16
+// operands (canonical rows, K contiguous), fp32 results, on the K loop above.
+// by_block: group g is M block g of the sorted layout (g < P/BM): A rows
+//   g*BM.., B = the block's expert slab (b + expert_ids[g] * b_group), C rows
+//   g*BM..; K fixed.
+// per expert: group g is expert g with segment [off[g], off[g+1]) of the
+//   sorted layout, a contiguous column range of the transposed activations:
+//   A rows m (pitch lda) and B rows n (pitch ldb) both start at column
+//   off[g]; K = the segment length (a multiple of 64); C = c + g * c_group.
+//   An expert with no rows gets zeros.
+template <int BM, int PF>
+__global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kWBf16, BM>()))
+nt_gemm_kernel(NtGemmArgs g) {
+    using TL = Tile<BM>;
+    __shared__ FfnSmem<BM> sm;
+    const int nN = g.N / 256;
+    const int mtiles = g.by_block ? 1 : g.M / BM;
+    int t = blockIdx.x;
+    const int nt = t % nN;
+    t /= nN;
+    const int mt = t % mtiles;
+    const int grp = t / mtiles;
+    int64_t a_off, b_off, c_off;
+    int K;
+    if (g.by_block) {
+        if (grp >= g.post_padded[0] / BM) return;
+        a_off = (int64_t)grp * BM * g.lda;
+        b_off = (int64_t)g.expert_ids[grp] * g.b_group;
+        c_off = (int64_t)grp * BM * g.ldc;
+        K = g.K;
+    } else {
+        const int lo = g.offsets[grp], hi = g.offsets[grp + 1];
+        a_off = (int64_t)mt * BM * g.lda + lo;
+        b_off = lo;
+        c_off = (int64_t)grp * g.c_group + (int64_t)mt * BM * g.ldc;
+        K = hi - lo;
+    }
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id(), r32 = lane & 31;
+    if (tid < BM) sm.arow[tid] = tid;
+    __syncthreads();
+    const int n0 = nt * 256 + w * 64;                       // this wave's output columns
+    const uint8_t* bb = (const uint8_t*)(g.b + b_off);
+    const uint8_t* const brow[2] = {bb + (int64_t)(n0 + r32) * g.ldb * 2 + (lane >> 5) * 64,
+                                    bb + (int64_t)(n0 + 32 + r32) * g.ldb * 2 + (lane >> 5) * 64};
+    const uint8_t* const srow[2] = {nullptr, nullptr};
+    f32x16_t acc[TL::MT][2];
+    zero_acc(acc);
+    const int nk = K / 64;                                  // K-steps of 64 bf16 elements
+    if (nk > 0)
+        kloop<kWBf16, false, false, BM, 2, PF, ffn_la<kWBf16, BM, PF>()>(
+            (const uint8_t*)(g.a + a_off), sm.arow, g.lda * 2, brow, srow, nk, sm.lds, acc);
+#pragma unroll
+    for (int m2 = 0; m2 < TL::MT; ++m2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = m2 * 32 + acc_row(i, lane);
+            if (m < BM) {
+                float* dst = g.c + c_off + (int64_t)m * g.ldc + n0 + r32;
+                dst[0] = acc[m2][0][i];
+                dst[32] = acc[m2][1][i];
+            }
+        }
+}
+
+template <int BM>
+static hipError_t launch_nt_bm(const NtGemmArgs& g, int64_t groups, hipStream_t stream) {
+    constexpr int PF = ffn_pf<kWBf16, BM>();
+    const int64_t tiles = groups * (g.by_block ? 1 : g.M / BM) * (g.N / 256);
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL((nt_gemm_kernel<BM, PF>), dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g);
+    return hipGetLastError();
+}
+
+// groups: the capacity's M blocks (by_block, BM = block_size_m) or the experts
+hipError_t launch_nt_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream) {
+    switch (BM) {
+        case 64: return launch_nt_bm<64>(g, groups, stream);
+        case 128: return launch_nt_bm<128>(g, groups, stream);
+        case 256: return launch_nt_bm<256>(g, groups, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // ----------------------------------------------------------------- prepack --
 // One 16-byte chunk per thread, walked in packed order (coalesced writes):
 // chunk c -> (expert, N tile, K-step, wave, row set, quarter, lane), and the

@@ -81,6 +81,47 @@ inline hipError_t record_stage(hipEvent_t const* ev, int i, hipStream_t s) {
     return ev ? hipEventRecord(ev[i], s) : hipSuccess;
 }
 
+// --------------------------------------------------------------- backward --
+// Grouped NT GEMM C[m][n] = sum_k A[m][k] B[n][k] (bf16 in, fp32 out); see
+// nt_gemm_kernel for the two groupings.
+struct NtGemmArgs {
+    const uint16_t* a;
+    int64_t lda;
+    const uint16_t* b;
+    int64_t ldb, b_group;
+    float* c;
+    int64_t ldc, c_group;
+    int M, N, K;
+    const int32_t* expert_ids;
+    const int32_t* post_padded;
+    const int32_t* offsets;
+    int by_block;
+};
+hipError_t launch_nt_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream);
+
+struct BwdArgs {
+    int T, K, E, H, I, B;
+    int64_t S, C;
+    const uint16_t* x;           // [T,H] bf16
+    const uint16_t* w13;         // [E,2I,H] bf16
+    const uint16_t* w2;          // [E,H,I] bf16
+    const int32_t* ids;          // [T,K]
+    const float* w;              // [T,K]
+    const int32_t* sorted;       // [C]
+    const int32_t* expert_ids;   // [C/B]
+    const int32_t* post_padded;  // [1]
+    const int32_t* offsets;      // [E+1]
+    const float* y_slots;        // [S,H] the forward's
+    const float* d_out;          // [T,H]
+    float* dx;                   // [T,H]
+    float* dw13;                 // [E,2I,H]
+    float* dw2;                  // [E,H,I]
+    float* d_w;                  // [T,K]
+};
+int64_t ffn_backward_workspace_bytes(int64_t T, int64_t K, int64_t E, int64_t H, int64_t I, int64_t C);
+hipError_t launch_ffn_backward(const BwdArgs& a, void* ws, hipStream_t stream);
+hipError_t launch_route_backward(const RouteArgs& a, const float* d_w, float* d_logits, hipStream_t stream);
+
 // ----------------------------------------------------------------- combine --
 hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,
                           const int32_t* ids, int out_bf16, void* out, hipStream_t stream);

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
@@ -201,3 +201,23 @@ def test_schedule_validation(lib):
     assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1
     p.schedule = moe.MOE_SCHEDULE_FUSED; p.w_dtype = p.x_dtype = 0
     assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1     # not for fp32
+
+
+def test_backward_validation(lib):
+    P = ctypes.c_void_p
+    ok = moe._FfnParams(256, 2, 8, 512, 256, 64, moe.MOE_BF16, moe.MOE_BF16, 0, 0, 0)
+    assert lib.moe_ffn_backward_workspace_bytes(ctypes.byref(ok)) > 0
+    for field, value in (("w_dtype", moe.MOE_FP8_E4M3), ("B", 32), ("I", 384), ("weight_layout", 1),
+                         ("row_layout", 1), ("schedule", 1)):
+        p = moe._FfnParams(256, 2, 8, 512, 256, 64, moe.MOE_BF16, moe.MOE_BF16, 0, 0, 0)
+        setattr(p, field, value)
+        assert lib.moe_ffn_backward_workspace_bytes(ctypes.byref(p)) == -1, field
+    args = [P(8)] * 16                                       # 15 arrays and the workspace
+    args[9] = None                                           # expert_offsets is required here
+    assert lib.moe_ffn_backward(ctypes.byref(ok), *args, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    args[9] = P(8)
+    assert lib.moe_ffn_backward(ctypes.byref(ok), *args, 16, None) == moe.MOE_ERR_WORKSPACE
+    r = moe._RouteParams(4, 8, 2, 0, 1, 1, 1, 1.0, 0)
+    assert lib.moe_route_backward(ctypes.byref(r), P(8), P(8), P(8), None, None) == moe.MOE_ERR_INVALID_ARG
+    r.score = 7
+    assert lib.moe_route_backward(ctypes.byref(r), P(8), P(8), P(8), P(8), None) == moe.MOE_ERR_INVALID_ARG

@@ -1,0 +1,118 @@
+"""The backward (training) on the GPU against the oracle's derivative.
+
+dx, dW13 and dW2 within 2e-2 * max|oracle| (bf16 GEMM operands, fp32
+accumulation, as the forward's bf16 bar); the combine weights' gradient
+and d_logits within 1e-5 * max|oracle| (fp32 dot products).  The oracle gets
+the GPU forward's routing, weights and y_slots, so both differentiate the
+same forward."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+import routing_align_sort_amd as moe
+from gpu_helpers import device, host_bits, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run(cfg, L, B, seed=3):
+    dev = device()
+    layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"],
+                         n_group=cfg["n_group"], topk_group=cfg["topk_group"], renormalize=cfg["renormalize"],
+                         shared=bool(cfg.get("shared")), x_dtype=L["x"].dtype)
+    layer.forward(L["x"], L["logits"], L["bias"])
+    d_out = torch.tensor(np.random.default_rng(seed).standard_normal((cfg["T"], cfg["H"])).astype(np.float32),
+                         device=dev)
+    dx, dw13, dw2, d_logits, dwk = layer.backward(L["x"], L["logits"], d_out)
+    torch.cuda.synchronize()
+    return layer, d_out, dx, dw13, dw2, d_logits, dwk
+
+
+def check_all(cfg, L, B, label):
+    layer, d_out, dx, dw13, dw2, d_logits, dwk = run(cfg, L, B)
+    ids = layer.topk_ids.cpu().numpy()
+    w = layer.topk_weights.cpu().numpy()
+    y = layer.y_slots.cpu().numpy()
+    rdx, rdw13, rdw2, rdwk = oracle.ffn_backward(host_bits(L["x"]), host_bits(L["w13"]), host_bits(L["w2"]), ids, w,
+                                                 y, d_out.cpu().numpy(), w_dtype="bf16", x_dtype="bf16",
+                                                 inter="bf16")
+    rdl = oracle.route_backward(L["logits"].cpu().numpy(), ids, dwk.cpu().numpy(), cfg["K"], score=cfg["score"],
+                                renormalize=cfg["renormalize"], append_shared=bool(cfg.get("shared")))
+    errs = {"dx": rel_err(dx.cpu().numpy(), rdx), "dw13": rel_err(dw13.cpu().numpy(), rdw13),
+            "dw2": rel_err(dw2.cpu().numpy(), rdw2), "d_w": rel_err(dwk.cpu().numpy(), rdwk),
+            "d_logits": rel_err(d_logits.cpu().numpy(), rdl)}
+    say(f"{label}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k in ("dx", "dw13", "dw2"):
+        assert errs[k] <= 2e-2, (k, errs[k])
+    assert errs["d_w"] <= 1e-5 and errs["d_logits"] <= 1e-5, errs
+
+
+@pytest.mark.parametrize("B", [64, 128, 256])
+def test_backward_small_softmax(B):
+    dev = device()
+    cfg = ms.scaled("tiny_fp32", T=160, H=512, I=256, E=6, K=2, dtype="bf16", B=B)
+    L = ms.make_layer(cfg, device=dev)
+    check_all(cfg, L, B, f"backward softmax top-2 B={B}")
+
+
+def test_backward_small_sigmoid_groups_shared():
+    dev = device()
+    cfg = ms.scaled("decode_bf16", T=120, H=512, I=256, E=16, K=4, n_group=4, topk_group=2, shared=True)
+    L = ms.make_layer(cfg, device=dev)
+    check_all(cfg, L, 64, "backward sigmoid groups + shared B=64")
+
+
+def test_backward_skipped_slots_and_empty_experts():
+    dev = device()
+    rng = np.random.default_rng(9)
+    T, K, E, H, I, B = 70, 3, 9, 256, 256, 64
+    cfg = ms.scaled("tiny_fp32", T=T, H=H, I=I, E=E, K=K, dtype="bf16", B=B)
+    L = ms.make_layer(cfg, device=dev)
+    ids = rng.integers(0, 5, (T, K)).astype(np.int32)       # experts 5..8 get no rows
+    ids[rng.random((T, K)) < 0.1] = -1
+    w = rng.random((T, K)).astype(np.float32)
+    tid, tw = torch.tensor(ids, device=dev), torch.tensor(w, device=dev)
+    al = moe.moe_align_sort(tid, E, B)
+    y = moe.moe_grouped_ffn(L["x"], L["w13"], L["w2"], al["sorted_token_ids"], al["expert_ids"],
+                            al["num_tokens_post_padded"], K=K, B=B)
+    d_out = torch.tensor(rng.standard_normal((T, H)).astype(np.float32), device=dev)
+    dx, dw13, dw2, dwk = moe.moe_ffn_backward(L["x"], L["w13"], L["w2"], tid, tw, al["sorted_token_ids"],
+                                              al["expert_ids"], al["num_tokens_post_padded"],
+                                              al["expert_offsets"], y, d_out, B=B)
+    torch.cuda.synchronize()
+    rdx, rdw13, rdw2, rdwk = oracle.ffn_backward(host_bits(L["x"]), host_bits(L["w13"]), host_bits(L["w2"]), ids, w,
+                                                 y.cpu().numpy(), d_out.cpu().numpy(), w_dtype="bf16",
+                                                 x_dtype="bf16", inter="bf16")
+    assert rel_err(dx.cpu().numpy(), rdx) <= 2e-2
+    assert rel_err(dw13.cpu().numpy(), rdw13) <= 2e-2
+    assert rel_err(dw2.cpu().numpy(), rdw2) <= 2e-2
+    assert rel_err(dwk.cpu().numpy(), rdwk) <= 1e-5
+    assert not dw13[5:].any() and not dw2[5:].any()          # experts with no rows: zero
+    assert (dwk.cpu().numpy()[ids < 0] == 0).all()
+
+
+def test_backward_full_size_prefill_sampled():
+    dev = device()
+    cfg = ms.CONFIGS["prefill_bf16"]
+    L = ms.make_layer(cfg, device=dev)
+    layer, d_out, dx, dw13, dw2, d_logits, dwk = run(cfg, L, 64)
+    ids = layer.topk_ids.cpu().numpy()
+    w = layer.topk_weights.cpu().numpy()
+    y = layer.y_slots.cpu().numpy()
+    e = int(ids[0, 0])
+    toks = np.nonzero(ids[:, 0] == e)[0]                    # every token of one expert (64)
+    sub_ids = np.zeros((len(toks), 1), np.int32)
+    sel = torch.tensor([e], device=dev)
+    rdx, rdw13, rdw2, rdwk = oracle.ffn_backward(
+        host_bits(L["x"][torch.as_tensor(toks, device=dev)]), host_bits(L["w13"].index_select(0, sel)),
+        host_bits(L["w2"].index_select(0, sel)), sub_ids, w[toks], y[toks], d_out.cpu().numpy()[toks],
+        w_dtype="bf16", x_dtype="bf16", inter="bf16")
+    errs = (rel_err(dx.cpu().numpy()[toks], rdx), rel_err(dw13[e].cpu().numpy(), rdw13[0]),
+            rel_err(dw2[e].cpu().numpy(), rdw2[0]), rel_err(dwk.cpu().numpy()[toks], rdwk))
+    say(f"prefill bf16 full size, expert {e} ({len(toks)} tokens): dx {errs[0]:.2e} dw13 {errs[1]:.2e} "
+        f"dw2 {errs[2]:.2e} d_w {errs[3]:.2e}")
+    assert max(errs[:3]) <= 2e-2 and errs[3] <= 1e-5
+    del L
+    torch.cuda.empty_cache()
