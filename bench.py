@@ -309,6 +309,8 @@ def main():
     ap.add_argument("--align-only", action="store_true",
                     help="time Align & Sort alone (16k tokens warm / cold and the token-count sweep), "
                          "print its JSON and exit")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time the training backward of the prefill bf16 layer, print its JSON and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates rocprofv3 byte counters)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -337,6 +339,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.align_only:
         print(json.dumps(align_only(dev)), flush=True)
+        return
+    if args.backward_only:
+        print(json.dumps(backward_step(dev)), flush=True)
         return
     cfg = ms.CONFIGS[args.workload]
     B = args.B or cfg["B"]
@@ -416,6 +421,7 @@ def main():
         line["permute_path"] = permute_path(dev)
         line["ffn_input_state"] = ffn_input_state(dev)
         line["one_stage_schedule"] = one_stage(dev)
+        line["backward"] = backward_step(dev)
     if args.copy_probe:
         copy_probe(dev)
     if not args.no_cpu_baseline:
@@ -461,6 +467,48 @@ def permute_path(dev):
         }
         del r, base, layer
         torch.cuda.empty_cache()
+    return res
+
+
+def backward_step(dev, steps=10, warmup=3):
+    """The training backward of the headline layer (prefill bf16, 2048 tokens
+    x 32 experts, B 64, canonical weights): dx, dW13, dW2, the combine weights'
+    and the logits' gradients, after one forward.  Wall clock of back-to-back
+    backward calls, their useful FLOPs (gate/up recomputed 4SHI, data
+    gradients 2SHI + 4SHI, weight gradients 2SHI + 4SHI: 16SHI per step) and
+    the event-timed share of each GEMM."""
+    import torch
+
+    import moe_synth as ms
+    import routing_align_sort_amd as moe
+    cfg = ms.CONFIGS["prefill_bf16"]
+    L = ms.make_layer(cfg, device=dev)
+    layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=1, B=cfg["B"], score="softmax", renormalize=False)
+    x, logits = L["x"], L["logits"]
+    layer.forward(x, logits)
+    d_out = torch.randn((cfg["T"], cfg["H"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.moe_ffn_backward_workspace_bytes(cfg["T"], 1, cfg["E"], cfg["H"], cfg["I"], cfg["B"]),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        layer.backward(x, logits, d_out, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.backward(x, logits, d_out, workspace=ws)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    S = int((layer.topk_ids >= 0).sum().item())
+    flops = 16 * S * cfg["H"] * cfg["I"]
+    res = {"workload": describe("prefill_bf16", cfg, cfg["B"]) + ", backward", "us_per_step": round(us, 1),
+           "forward_us_per_step": None, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+           "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, logits)
+    torch.cuda.synchronize()
+    res["forward_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 1)
+    del layer, L, ws
+    torch.cuda.empty_cache()
     return res
 
 
