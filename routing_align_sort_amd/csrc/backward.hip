@@ -14,9 +14,10 @@
 //   routing: d_logits from d_w through softmax or sigmoid (+ renormalisation)
 //
 // The path: rows are moved into the sorted order (permute), the gate/up
-// values are recomputed, the data gradients are grouped NT GEMMs per M block
-// against transposed weight slabs, and the weight gradients are NT GEMMs per
-// expert over the expert's contiguous segment of the transposed activations.
+// values are recomputed (NT GEMM per M block), the data gradients are NN
+// GEMMs per M block against the weight slabs in their own layout, and the
+// weight gradients are NN GEMMs per expert over the expert's contiguous
+// segment: transposed dy / [d_g d_u] against the activation rows.
 // Every GEMM operand is bf16 (dy and [d_g d_u] rounded once), every
 // accumulation fp32.  Needs block_size_m a multiple of 64 (each expert's
 // segment is then a whole number of 64-element K-steps).
@@ -230,7 +231,7 @@ hipError_t launch_route_backward(const RouteArgs& a, const float* d_w, float* d_
 static inline int64_t al256(int64_t v) { return (v + 255) / 256 * 256; }
 
 struct BwdWs {
-    uint16_t *x_perm, *dy_slots, *dy_perm, *a_bf, *dgu, *w13t, *w2t, *dyt, *at, *dgut, *xt;
+    uint16_t *x_perm, *dy_slots, *dy_perm, *a_bf, *dgu, *dyt, *dgut;
     float *gu, *d_a, *dxs, *ones;
     int32_t *row_of_slot, *row_of_slot2;
 };
@@ -248,12 +249,8 @@ static BwdWs bwd_ws(void* ws, int64_t T, int64_t K, int64_t E, int64_t H, int64_
     w.a_bf = (uint16_t*)take(C * I * 2);
     w.dgu = (uint16_t*)take(C * 2 * I * 2);
     w.dxs = (float*)take(C * H * 4);
-    w.w13t = (uint16_t*)take(E * 2 * I * H * 2);
-    w.w2t = (uint16_t*)take(E * H * I * 2);
     w.dyt = (uint16_t*)take(H * C * 2);
-    w.at = (uint16_t*)take(I * C * 2);
     w.dgut = (uint16_t*)take(2 * I * C * 2);
-    w.xt = (uint16_t*)take(H * C * 2);
     w.ones = (float*)take(S * 4);
     w.row_of_slot = (int32_t*)take(S * 4);
     w.row_of_slot2 = (int32_t*)take(S * 4);
@@ -282,42 +279,39 @@ hipError_t launch_ffn_backward(const BwdArgs& a, void* ws, hipStream_t st) {
     MOE_TRY(hipGetLastError());
     MOE_TRY(launch_permute_rows(w.dy_slots, H * 2, 1, (int)E, S, C, a.sorted, a.post_padded, a.ids, nullptr,
                                 w.dy_perm, nullptr, w.row_of_slot2, st));
-    // 2. transposed weight slabs for the data gradients
-    MOE_TRY(transpose(a.w13, w.w13t, (int)(2 * I), (int)H, 2 * I, (int)E, 2 * I * H, 2 * I * H, nullptr, st));
-    MOE_TRY(transpose(a.w2, w.w2t, (int)H, (int)I, H, (int)E, H * I, H * I, nullptr, st));
-    // 3. gate/up recomputed, d_a, SwiGLU backward, dx through W13
+    // 2. gate/up recomputed (weights as stored: K-contiguous rows)
     NtGemmArgs g{};
     g.expert_ids = a.expert_ids; g.post_padded = a.post_padded; g.offsets = a.offsets; g.by_block = 1;
     g.a = w.x_perm; g.lda = H; g.b = a.w13; g.ldb = H; g.b_group = 2 * I * H; g.c = w.gu; g.ldc = 2 * I;
     g.M = a.B; g.N = (int)(2 * I); g.K = (int)H;
     MOE_TRY(launch_nt_gemm(g, a.B, nblk, st));
-    g.a = w.dy_perm; g.lda = H; g.b = w.w2t; g.ldb = H; g.b_group = I * H; g.c = w.d_a; g.ldc = I;
+    // 3. d_a = dy W2[e] (W2[e] is [H][I]: the NN form), SwiGLU backward, dx rows = [d_g d_u] W13[e]
+    g.a = w.dy_perm; g.lda = H; g.b = a.w2; g.ldb = I; g.b_group = H * I; g.c = w.d_a; g.ldc = I;
     g.N = (int)I; g.K = (int)H;
-    MOE_TRY(launch_nt_gemm(g, a.B, nblk, st));
+    MOE_TRY(launch_nn_gemm(g, a.B, nblk, st));
     if (C > 0)
         hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)C), dim3(kBwdThreads), 0, st, (int)I, a.post_padded,
                            (const float*)w.gu, (const float*)w.d_a, w.a_bf, w.dgu);
     MOE_TRY(hipGetLastError());
-    g.a = w.dgu; g.lda = 2 * I; g.b = w.w13t; g.ldb = 2 * I; g.b_group = H * 2 * I; g.c = w.dxs; g.ldc = H;
+    g.a = w.dgu; g.lda = 2 * I; g.b = a.w13; g.ldb = H; g.b_group = 2 * I * H; g.c = w.dxs; g.ldc = H;
     g.N = (int)H; g.K = (int)(2 * I);
-    MOE_TRY(launch_nt_gemm(g, a.B, nblk, st));
+    MOE_TRY(launch_nn_gemm(g, a.B, nblk, st));
     if (S > 0)
         hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((S + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads),
                            0, st, w.ones, S, 1.0f);
     MOE_TRY(hipGetLastError());
     MOE_TRY(launch_unpermute_combine(a.T, a.K, (int)H, w.dxs, w.ones, w.row_of_slot, 0, a.dx, st));
-    // 4. weight gradients: per expert over its segment of the transposed activations
+    // 4. weight gradients per expert: transposed dy / [d_g d_u] (K = the expert's rows,
+    //    contiguous) against the rows of a~ / x
     MOE_TRY(transpose(w.dy_perm, w.dyt, (int)C, (int)H, C, 1, 0, 0, a.post_padded, st));
-    MOE_TRY(transpose(w.a_bf, w.at, (int)C, (int)I, C, 1, 0, 0, a.post_padded, st));
     MOE_TRY(transpose(w.dgu, w.dgut, (int)C, (int)(2 * I), C, 1, 0, 0, a.post_padded, st));
-    MOE_TRY(transpose(w.x_perm, w.xt, (int)C, (int)H, C, 1, 0, 0, a.post_padded, st));
     g.by_block = 0;
-    g.a = w.dyt; g.lda = C; g.b = w.at; g.ldb = C; g.c = a.dw2; g.ldc = I; g.c_group = H * I;
+    g.a = w.dyt; g.lda = C; g.b = w.a_bf; g.ldb = I; g.c = a.dw2; g.ldc = I; g.c_group = H * I;
     g.M = (int)H; g.N = (int)I;
-    MOE_TRY(launch_nt_gemm(g, 128, E, st));
-    g.a = w.dgut; g.lda = C; g.b = w.xt; g.ldb = C; g.c = a.dw13; g.ldc = H; g.c_group = 2 * I * H;
+    MOE_TRY(launch_nn_gemm(g, 128, E, st));
+    g.a = w.dgut; g.lda = C; g.b = w.x_perm; g.ldb = H; g.c = a.dw13; g.ldc = H; g.c_group = 2 * I * H;
     g.M = (int)(2 * I); g.N = (int)H;
-    MOE_TRY(launch_nt_gemm(g, 128, E, st));
+    MOE_TRY(launch_nn_gemm(g, 128, E, st));
     return hipSuccess;
 }
 

@@ -1170,6 +1170,190 @@ nt_gemm_kernel(NtGemmArgs g) {
         }
 }
 
+// NN form: C[m][n] = sum_k A[m][k] * B[k][n], B in its own [K][N] layout (N
+// contiguous), so weight slabs and activation rows need no transpose.  A
+// (K contiguous rows) goes through LDS as in kloop; B goes through LDS in
+// its natural layout, 64 K-rows x 128 columns per K-step, and each lane reads
+// its MFMA operand with two transposing LDS reads (ds_read_b64_tr_b16): in a
+// group of 16 lanes, lanes 4q..4q+3 point at the 16 columns of K-row q and
+// lane i receives column i of the four rows.  A lane half h of MFMA slice kk
+// covers k = 32h + 8kk .. +7 on both operands (the A read of kloop).
+constexpr int kNnCols = 128;                         // N columns per workgroup: 4 waves x 32
+constexpr int kNnPitch = kNnCols + 8;                // B tile row pitch, elements (272 bytes)
+constexpr int kNnPF = 2;                             // K-steps of both operands in flight
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+template <int BM>
+struct NnSmem {
+    __attribute__((aligned(16))) uint8_t a[2 * Tile<BM>::ROWS * kLdsPitch];
+    __attribute__((aligned(16))) uint16_t b[2][64 * kNnPitch];
+};
+
+template <int BM>
+__global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_kernel(NtGemmArgs g) {
+    using TL = Tile<BM>;
+    constexpr int MT = TL::MT;
+    constexpr int CPR = TL::CPR;
+    constexpr int RPS = kFfnThreads / CPR;
+    constexpr int BCH = 64 * kNnCols / 8 / kFfnThreads;   // B chunks of 16 bytes per thread per K-step
+    __shared__ NnSmem<BM> sm;
+    const int nN = g.N / kNnCols;
+    const int mtiles = g.by_block ? 1 : g.M / BM;
+    int t = blockIdx.x;
+    const int nt = t % nN;
+    t /= nN;
+    const int mt0 = t % mtiles;
+    const int grp = t / mtiles;
+    int64_t a_off, b_off, c_off;
+    int K;
+    if (g.by_block) {
+        if (grp >= g.post_padded[0] / BM) return;
+        a_off = (int64_t)grp * BM * g.lda;
+        b_off = (int64_t)g.expert_ids[grp] * g.b_group;
+        c_off = (int64_t)grp * BM * g.ldc;
+        K = g.K;
+    } else {
+        const int lo = g.offsets[grp], hi = g.offsets[grp + 1];
+        a_off = (int64_t)mt0 * BM * g.lda + lo;              // A: transposed activations, columns lo..
+        b_off = (int64_t)lo * g.ldb;                          // B: activation rows lo..
+        c_off = (int64_t)grp * g.c_group + (int64_t)mt0 * BM * g.ldc;
+        K = hi - lo;
+    }
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id(), r32 = lane & 31, half = lane >> 5;
+    const int nk = K / 64;
+    f32x16_t acc[MT];
+#pragma unroll
+    for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m2][i] = 0.f;
+
+    if (nk > 0) {
+        const uint16_t* A = g.a + a_off;
+        const uint16_t* Bt = g.b + b_off + nt * kNnCols;
+        // A chunks: rows tid/CPR + r*RPS, bytes (tid%CPR)*16 of each 128-byte K-step
+        const int lds_a = (tid / CPR) * kLdsPitch + (tid % CPR) * 16;
+        int64_t aoff[TL::APT];
+#pragma unroll
+        for (int r = 0; r < TL::APT; ++r) {
+            const int m = tid / CPR + r * RPS;
+            aoff[r] = (int64_t)(m < BM ? m : 0) * g.lda * 2 + (tid % CPR) * 16;
+        }
+        // B chunks: K-row c/16 of the step, columns (c%16)*8 of the tile
+        int64_t boff[BCH];
+        int lds_b[BCH];
+#pragma unroll
+        for (int r = 0; r < BCH; ++r) {
+            const int c = tid + r * kFfnThreads;
+            boff[r] = (int64_t)(c / 16) * g.ldb + (c % 16) * 8;
+            lds_b[r] = (c / 16) * kNnPitch + (c % 16) * 8;
+        }
+        uint4 areg[kNnPF + 1][TL::APT];
+        uint4 breg[kNnPF + 1][BCH];
+        auto load = [&](uint4 (&ar)[TL::APT], uint4 (&br)[BCH], int k) {
+#pragma unroll
+            for (int r = 0; r < TL::APT; ++r)
+                ar[r] = __builtin_bit_cast(uint4, *(const u32x4_t*)((const uint8_t*)A + aoff[r] + (int64_t)k * 128));
+#pragma unroll
+            for (int r = 0; r < BCH; ++r)
+                br[r] = __builtin_bit_cast(uint4, *(const u32x4_t*)(Bt + boff[r] + (int64_t)k * 64 * g.ldb));
+        };
+        auto store = [&](const uint4 (&ar)[TL::APT], const uint4 (&br)[BCH], int buf) {
+#pragma unroll
+            for (int r = 0; r < TL::APT; ++r)
+                *(uint4*)(sm.a + buf * TL::ROWS * kLdsPitch + lds_a + r * RPS * kLdsPitch) = ar[r];
+#pragma unroll
+            for (int r = 0; r < BCH; ++r) *(uint4*)(&sm.b[buf][lds_b[r]]) = br[r];
+        };
+        // this lane's transposing-read address in the B tile, before the slice offset
+        const int grp16 = lane >> 4, q = (lane >> 2) & 3, sl = lane & 3;
+        const int b_row0 = (grp16 >> 1) * 32 + q;
+        const int b_col = w * 32 + (grp16 & 1) * 16 + 4 * sl;
+        auto compute = [&](int buf) {
+            const uint8_t* abase = sm.a + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * 64;
+            const uint16_t* bb = sm.b[buf];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16_t*)(bb + (b_row0 + kk * 8) * kNnPitch + b_col));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16_t*)(bb + (b_row0 + kk * 8 + 4) * kNnPitch + b_col));
+                uint4 bv;
+                bv.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+                bv.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+                bv.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+                bv.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+#pragma unroll
+                for (int m2 = 0; m2 < MT; ++m2) {
+                    const uint4 af = *(const uint4*)(abase + m2 * 32 * kLdsPitch + kk * 16);
+                    acc[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af), as_bf16x8(bv), acc[m2], 0, 0, 0);
+                }
+            }
+        };
+        // prologue: steps 0..PF-1 in flight, step 0 in LDS
+#pragma unroll
+        for (int s2 = 0; s2 < kNnPF; ++s2) load(areg[s2], breg[s2], min(s2, nk - 1));
+        store(areg[0], breg[0], 0);
+        __syncthreads();
+        // ring slots are compile-time: step k0+u loads into slot (u+PF)%(PF+1)
+        // and stores slot (u+1)%(PF+1)
+        static_assert(kNnPF == 2, "the K loop is unrolled by three");
+        auto step = [&](int k, auto uc) {
+            constexpr int u = decltype(uc)::value;
+            constexpr int sl_ld = (u + kNnPF) % (kNnPF + 1), sl_st = (u + 1) % (kNnPF + 1);
+            load(areg[sl_ld], breg[sl_ld], min(k + kNnPF, nk - 1));
+            if (MOE_FFN_PIN_LOADS) __builtin_amdgcn_sched_barrier(0);
+            compute(k & 1);
+            store(areg[sl_st], breg[sl_st], (k + 1) & 1);
+            __syncthreads();
+        };
+        for (int k0 = 0; k0 < nk; k0 += kNnPF + 1) {
+            step(k0, std::integral_constant<int, 0>{});
+            if (k0 + 1 < nk) step(k0 + 1, std::integral_constant<int, 1>{});
+            if (k0 + 2 < nk) step(k0 + 2, std::integral_constant<int, 2>{});
+        }
+    }
+    // The product is written once and not read again by this kernel: stores
+    // are non-temporal.  Where the tile buffers can hold it, each wave's BM x
+    // 32 block goes through LDS first so that a lane writes 16 bytes and a
+    // store instruction covers eight 128-byte row segments (the fp32 weight
+    // gradients make these launches bound by their writes).
+    if constexpr (sizeof(NnSmem<BM>) >= 4 * BM * 32 * sizeof(float)) {
+        __syncthreads();
+        float* st = reinterpret_cast<float*>(&sm) + w * BM * 32;
+#pragma unroll
+        for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st[(m2 * 32 + acc_row(i, lane)) * 32 + r32] = acc[m2][i];
+        __builtin_amdgcn_wave_barrier();
+        const int cq = (lane & 7) * 4;
+#pragma unroll
+        for (int j = 0; j < BM / 8; ++j) {
+            const int m = j * 8 + (lane >> 3);
+            const f32x4_t v = *(const f32x4_t*)(st + m * 32 + cq);
+            __builtin_nontemporal_store(v, (f32x4_t*)(g.c + c_off + (int64_t)m * g.ldc + nt * kNnCols + w * 32 + cq));
+        }
+    } else {
+        const int n0 = nt * kNnCols + w * 32 + r32;
+#pragma unroll
+        for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                __builtin_nontemporal_store(acc[m2][i], g.c + c_off + (int64_t)(m2 * 32 + acc_row(i, lane)) * g.ldc + n0);
+    }
+}
+
+hipError_t launch_nn_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream) {
+    const int64_t tiles = groups * (g.by_block ? 1 : g.M / BM) * (g.N / kNnCols);
+    if (tiles == 0) return hipSuccess;
+    switch (BM) {
+        case 64: hipLaunchKernelGGL(nn_gemm_kernel<64>, dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g); break;
+        case 128: hipLaunchKernelGGL(nn_gemm_kernel<128>, dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g); break;
+        case 256: hipLaunchKernelGGL(nn_gemm_kernel<256>, dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int BM>
 static hipError_t launch_nt_bm(const NtGemmArgs& g, int64_t groups, hipStream_t stream) {
     constexpr int PF = ffn_pf<kWBf16, BM>();

@@ -98,6 +98,9 @@ struct NtGemmArgs {
     int by_block;
 };
 hipError_t launch_nt_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream);
+// The NN form C[m][n] = sum_k A[m][k] B[k][n] (B in [K][N], N a multiple of 128),
+// same groupings; B_group / ldb address B's rows.
+hipError_t launch_nn_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream);
 
 struct BwdArgs {
     int T, K, E, H, I, B;
