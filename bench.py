@@ -389,6 +389,7 @@ def main():
         torch.cuda.empty_cache()
         line["hbm_probe"] = hbm_probe(dev)
         line["mfma_probe"] = mfma_probe(dev)
+        line["vendor_gemm"] = vendor_gemm(dev)
         line["align_sort_16k"] = align_only(dev)
         extra = {}
         # the HBM-bound secondary shapes at their own block size; the
@@ -679,6 +680,63 @@ def mfma_probe(dev, reps=5):
         res[name + "_tflops"] = round(tf, 1)
         res[name + "_frac_of_peak"] = round(tf / peak, 4)
     ev.close()
+    return res
+
+
+def vendor_gemm(dev, reps=10):
+    """Context for the compute-bound shapes: the vendor GEMM library
+    (hipBLASLt, called through torch) on the per-expert products of the
+    512-tokens-per-expert workload -- rows already grouped, no gather, no
+    SiLU, no scales in bf16 -- and on one dense product with all 16384 rows.
+    bf16: one batched call over the 32 experts; fp8 (E4M3, row-wise scales,
+    bf16 out): one call per expert, as the library has no grouped form here.
+    TFLOP/s from event timing, mean of `reps` after 3 warm-up calls."""
+    import torch
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    res = {}
+    E, M, H, I = 32, 512, 7168, 2048
+    for name, (m, k, n) in (("gate_up", (M, H, 2 * I)), ("down", (M, I, H))):
+        x = torch.randn(E, m, k, device=dev, dtype=torch.bfloat16, generator=g)
+        w = torch.randn(E, k, n, device=dev, dtype=torch.bfloat16, generator=g)    # contiguous [K, N]
+        t = timed(lambda: torch.bmm(x, w))
+        res[f"bf16_{name}_512_per_expert_tflops"] = round(2.0 * E * m * k * n / t / 1e12, 1)
+        del x, w
+        f8 = torch.float8_e4m3fn
+        x = (torch.randn(E, m, k, device=dev, generator=g) * 0.5).to(f8)
+        w = (torch.randn(E, n, k, device=dev, generator=g) * 0.5).to(f8)            # [N, K]: column-major operand
+        sx, sw = torch.ones(m, 1, device=dev), torch.ones(1, n, device=dev)
+        t = timed(lambda: [torch._scaled_mm(x[e], w[e].t(), scale_a=sx, scale_b=sw, out_dtype=torch.bfloat16)
+                           for e in range(E)])
+        res[f"fp8_{name}_512_per_expert_tflops"] = round(2.0 * E * m * k * n / t / 1e12, 1)
+        del x, w
+        torch.cuda.empty_cache()
+    m, k, n = E * M, H, 2 * I
+    x = torch.randn(m, k, device=dev, dtype=torch.bfloat16, generator=g)
+    w = torch.randn(k, n, device=dev, dtype=torch.bfloat16, generator=g)
+    t = timed(lambda: x @ w)
+    res["bf16_gate_up_dense_16384_rows_tflops"] = round(2.0 * m * k * n / t / 1e12, 1)
+    del x, w
+    x = (torch.randn(m, k, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)
+    w = (torch.randn(n, k, device=dev, generator=g) * 0.5).to(torch.float8_e4m3fn)
+    sx, sw = torch.ones(m, 1, device=dev), torch.ones(1, n, device=dev)
+    t = timed(lambda: torch._scaled_mm(x, w.t(), scale_a=sx, scale_b=sw, out_dtype=torch.bfloat16))
+    res["fp8_gate_up_dense_16384_rows_tflops"] = round(2.0 * m * k * n / t / 1e12, 1)
+    del x, w
+    torch.cuda.empty_cache()
     return res
 
 
