@@ -84,6 +84,8 @@ def _load():
     lib.oracle_row_of_slot.restype = i32
     lib.oracle_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, P]
     lib.oracle_unpermute_combine.restype = i32
+    lib.oracle_unpermute_combine_backward.argtypes = [i32, i32, i32, P, P, P, P, i64, i32, P, P]
+    lib.oracle_unpermute_combine_backward.restype = i32
     lib.oracle_ffn_backward.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P,
                                         P, P, P, P]
     lib.oracle_ffn_backward.restype = i32
@@ -334,6 +336,29 @@ def unpermute_combine(y_perm, topk_weights, row_of_slot_):
     if rc != 0:
         raise ValueError("oracle_unpermute_combine: invalid arguments")
     return out
+
+
+def unpermute_combine_backward(d_out, y_perm, topk_weights, sorted_ids, P=None, round_to="f64"):
+    """Gradient of unpermute_combine for an upstream d_out [T,H]: (d_y_perm
+    float64 [P,H], d_w float64 [T,K]).  d_y_perm[r] = w[s] d_out[s // K] for
+    the slot s in row r, zeros for padding rows; d_w[s] = <d_out[s // K],
+    y_perm[row of s]>, 0 for a slot that was not placed.  round_to: "f64"
+    (exact), "f32" or "bf16" (fp32 product rounded to bf16), as delivered."""
+    g = _c(d_out, np.float32)
+    y = _c(y_perm, np.float32)
+    w = _c(topk_weights, np.float32)
+    srt = _c(sorted_ids, np.int32)
+    T, K = w.shape
+    H = g.shape[1]
+    P = srt.shape[0] if P is None else int(P)
+    rnd = {"f64": 0, "f32": 1, "bf16": 2}[round_to]
+    dy = np.empty((P, H), np.float64)
+    dw = np.empty((T, K), np.float64)
+    rc = _load().oracle_unpermute_combine_backward(T, K, H, _ptr(g), _ptr(y), _ptr(w), _ptr(srt), P, rnd,
+                                                   _ptr(dy), _ptr(dw))
+    if rc != 0:
+        raise ValueError("oracle_unpermute_combine_backward: invalid arguments")
+    return dy, dw
 
 
 def ffn_backward(x, w13, w2, topk_ids, topk_weights, y_slots, d_out, *, w_dtype, x_dtype, inter):

@@ -563,6 +563,47 @@ int oracle_unpermute_combine(int T, int K, int H, const float *y_perm, const flo
     return 0;
 }
 
+/* Gradient of the unpermute-combine for an upstream d_out [T,H] ([DIG], the
+ * Megatron section: permute and unpermute are each other's gradients, so the
+ * gradient of the weighted unpermute is a weighted permute).  out is linear
+ * in both y_perm and w, so, in double:
+ *   d_y_perm[r] = w[s] * d_out[s / K]     for r < P, s = sorted[r] < S;
+ *                 zeros for a padding row r < P (no slot reads it)
+ *   d_w[s]      = sum_h d_out[s / K, h] * y_perm[row of s, h]; 0 for a slot
+ *                 that is not placed (its id was outside [0,E))
+ * round: how d_y_perm is delivered -- 0 exact (the product of two floats is
+ * exact in double), 1 rounded to fp32, 2 rounded to fp32 then to bf16 (the
+ * reading: the product is formed in fp32 and rounded once more to the output
+ * type).  Rows from P on are not written. */
+int oracle_unpermute_combine_backward(int T, int K, int H, const float *d_out, const float *y_perm,
+                                      const float *topk_weights, const int32_t *sorted, int64_t P,
+                                      int round, double *d_y_perm, double *d_w)
+{
+    if (T < 0 || K < 1 || H < 1 || P < 0 || round < 0 || round > 2) return 1;
+    int64_t S = (int64_t)T * K;
+    for (int64_t i = 0; i < S; i++) d_w[i] = 0.0;
+    for (int64_t r = 0; r < P; r++) {
+        double *dst = d_y_perm + r * H;
+        int32_t s = sorted[r];
+        if (s < 0 || s >= S) {
+            for (int h = 0; h < H; h++) dst[h] = 0.0;
+            continue;
+        }
+        const float *g = d_out + (int64_t)(s / K) * H;
+        const float *y = y_perm + r * H;
+        double dot = 0.0;
+        for (int h = 0; h < H; h++) {
+            double v = (double)topk_weights[s] * (double)g[h];
+            if (round >= 1) v = (double)(float)v;
+            if (round == 2) v = oracle_bf16_decode(oracle_bf16_encode((float)v));
+            dst[h] = v;
+            dot += (double)g[h] * (double)y[h];
+        }
+        d_w[s] = dot;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Backward (training)                                                        */
 /* ------------------------------------------------------------------------ */

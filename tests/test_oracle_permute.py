@@ -103,3 +103,74 @@ def test_rows_past_the_padded_count_are_left_alone():
     full = oracle.permute_rows(x, srt, 2)
     assert np.array_equal(xp[:P], full[:P])
     assert not full[P:].any()
+
+
+# ----------------------------------------------- gradient of the unpermute --
+def test_unpermute_backward_hand_worked():
+    # The layout of the hand-worked table: rows [1,4,0,2,5,6,3,6] hold slots
+    # (6 = padding).  Token t's slots are 2t, 2t+1.
+    ids = np.array([[1, 0], [1, 2], [0, 1]], np.int32)
+    srt = oracle.align_sort(ids, 3, 2)["sorted_token_ids"]
+    w = np.array([[0.5, 2.0], [1.0, -1.0], [0.25, 4.0]], np.float32)
+    g = np.array([[1, 2], [3, 4], [5, 6]], np.float32)              # d_out[t]
+    y = np.arange(16, dtype=np.float32).reshape(8, 2)               # y_perm rows
+    dy, dw = oracle.unpermute_combine_backward(g, y, w, srt)
+    # row r holds slot s: d_y = w[s] * d_out[s // 2]
+    want = [[2.0 * 1, 2.0 * 2], [0.25 * 5, 0.25 * 6], [0.5 * 1, 0.5 * 2], [1.0 * 3, 1.0 * 4],
+            [4.0 * 5, 4.0 * 6], [0, 0], [-1.0 * 3, -1.0 * 4], [0, 0]]
+    assert dy.tolist() == want
+    # slot s: <d_out[s // 2], y[row of s]>, rows of slots 0..5 = [2,0,3,6,1,4]
+    rows = [2, 0, 3, 6, 1, 4]
+    want_w = [float(g[s // 2] @ y[rows[s]]) for s in range(6)]
+    assert dw.ravel().tolist() == want_w
+
+
+@pytest.mark.parametrize("T,K,E,B", [(7, 3, 5, 4), (64, 8, 16, 16), (200, 2, 33, 32)])
+def test_unpermute_backward_is_the_adjoint(T, K, E, B):
+    # unpermute_combine is linear in y_perm and in w: for any directions,
+    # <d_out, UC(dY, w)> = <d_y_perm, dY> and <d_out, UC(y, dW)> = <d_w, dW>,
+    # with UC the separately pinned forward.
+    rng = np.random.default_rng(T + 7 * K)
+    ids, al = random_case(rng, T, K, E, B)
+    srt, P = al["sorted_token_ids"], al["num_tokens_post_padded"]
+    H = 12
+    C = srt.shape[0]
+    ros = oracle.row_of_slot(srt, T * K)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    g = rng.standard_normal((T, H)).astype(np.float32)
+    y = rng.standard_normal((C, H)).astype(np.float32)
+    dy, dw = oracle.unpermute_combine_backward(g, y, w, srt, P=P)
+    dY = rng.standard_normal((C, H)).astype(np.float32)
+    lhs = float(np.sum(g.astype(np.float64) * oracle.unpermute_combine(dY, w, ros)))
+    rhs = float(np.sum(dy * dY[:P].astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)) * H * K
+    dW = rng.standard_normal((T, K)).astype(np.float32)
+    lhs = float(np.sum(g.astype(np.float64) * oracle.unpermute_combine(y, dW, ros)))
+    rhs = float(np.sum(dw * dW.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)) * H * K
+    # padding rows get no gradient; skipped slots get a zero weight gradient
+    pad = srt[:P] >= T * K
+    assert (dy[pad] == 0).all()
+    assert (dw.ravel()[ros < 0] == 0).all()
+
+
+def _bf16_rne(v32):
+    # round-to-nearest-even on the bit pattern (add 0x7FFF plus the kept lsb)
+    u = v32.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint32) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def test_unpermute_backward_rounding_of_the_delivered_rows():
+    rng = np.random.default_rng(3)
+    ids, al = random_case(rng, 40, 4, 6, 8, p_invalid=0.0)
+    srt, P = al["sorted_token_ids"], al["num_tokens_post_padded"]
+    w = rng.standard_normal((40, 4)).astype(np.float32)
+    g = rng.standard_normal((40, 16)).astype(np.float32)
+    y = rng.standard_normal((srt.shape[0], 16)).astype(np.float32)
+    exact, _ = oracle.unpermute_combine_backward(g, y, w, srt, P=P)
+    f32, _ = oracle.unpermute_combine_backward(g, y, w, srt, P=P, round_to="f32")
+    b16, _ = oracle.unpermute_combine_backward(g, y, w, srt, P=P, round_to="bf16")
+    ref32 = exact.astype(np.float32)                # a product of two floats is exact in double
+    assert np.array_equal(f32, ref32.astype(np.float64))
+    assert np.array_equal(b16, _bf16_rne(ref32).astype(np.float64))
