@@ -437,7 +437,8 @@ def permute_path(dev):
     sets (no step finds its input in the last-level cache): step time of both, and the permute and unpermute-combine kernels
     with their HBM rates on algorithmic bytes (permute: each placed row read
     once, each row below num_tokens_post_padded written; unpermute-combine:
-    every placed row read, out written)."""
+    every placed row read, out written), and the unpermute-combine's gradient
+    (event-timed alone, 10 calls)."""
     import torch
 
     import moe_synth as ms
@@ -454,6 +455,27 @@ def permute_path(dev):
         perm_bytes = S_valid * H * xb + P * H * xb
         unperm_bytes = S_valid * H * 4 + cfg["T"] * H * 2
         base = run_layer_timed(cfg, B, 16, 8, dev, rotate=32, graph=False)
+        # the unpermute-combine's gradient on the same layout (training): each
+        # placed row reads d_out's row and y_perm's row, every row below P
+        # writes d_y_perm (bf16, the GEMMs' operand type)
+        import routing_align_sort_amd as moe
+        d_out = torch.randn((layer.T, H), dtype=torch.float32, device=dev)
+        d_y = torch.empty((C, H), dtype=torch.bfloat16, device=dev)
+        d_w = torch.empty((layer.T, layer.KO), dtype=torch.float32, device=dev)
+        ev = moe.HipEvents(2 * 10)
+        for i in range(13):
+            if i >= 3:
+                ev.record(2 * (i - 3))
+            moe.moe_unpermute_combine_backward(d_out, layer.y_slots, layer.topk_weights, layer.topk_ids, layer.sorted,
+                                               layer.ntpp, layer.E_slabs, B, d_y_perm_dtype=torch.bfloat16,
+                                               d_y_perm=d_y, d_topk_weights=d_w)
+            if i >= 3:
+                ev.record(2 * (i - 3) + 1)
+        torch.cuda.synchronize()
+        ub_us = _mean([ev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(10)])
+        ev.close()
+        ub_bytes = S_valid * H * 4 * 2 + P * H * 2
+        del d_out, d_y, d_w
         res[name] = {
             "block_size_m": B,
             "us_per_step_sorted_rows": round(r["wall_s"] / r["steps"] * 1e6, 1),
@@ -464,6 +486,8 @@ def permute_path(dev):
             "permute_gbs": round(perm_bytes / (r["us"]["permute"] * 1e-6) / 1e9, 1),
             "unpermute_combine_us": round(r["us"]["combine"], 2),
             "unpermute_combine_gbs": round(unperm_bytes / (r["us"]["combine"] * 1e-6) / 1e9, 1),
+            "unpermute_combine_backward_us": round(ub_us, 2),
+            "unpermute_combine_backward_gbs": round(ub_bytes / (ub_us * 1e-6) / 1e9, 1),
             "stage_us": {k: round(v, 2) for k, v in r["us"].items()},
         }
         del r, base, layer

@@ -17,6 +17,11 @@
  *   moe_grouped_ffn        (row_layout MOE_ROWS_SORTED) x_perm -> y_perm [C,H]
  *   moe_unpermute_combine  y_perm, row_of_slot, topk weights -> out [T,H]
  *
+ * Training adds the gradients: moe_ffn_backward (the layer: dx, dw13, dw2,
+ * d_topk_weights), moe_route_backward (d_logits), and for the permuted path
+ * moe_unpermute_combine_backward (d_y_perm, d_topk_weights) and
+ * moe_unpermute_combine with unit weights (the permute's gradient).
+ *
  * Conventions shared by every call
  * --------------------------------
  * - Pointers named as device pointers must point to device memory of the
@@ -50,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
     MOE_OK = 0,
@@ -321,8 +326,25 @@ moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float
  * skipping row_of_slot[t*K+k] < 0, of topk_weights[t,k] * y_perm[row, h] in
  * fp32 -- the same arithmetic as moe_combine, so on y_perm[r] =
  * y_slots[sorted_token_ids[r]] both give the same bits.  y_perm device fp32
- * [C,H]; out device [T,H] in out_dtype (MOE_F32 or MOE_BF16).  Limits: H a
- * multiple of 4.
+ * [C,H]; out device [T,H] in out_dtype (MOE_F32 or MOE_BF16).  topk_weights
+ * NULL means every weight is 1: the sum of a token's rows, which is the
+ * gradient of moe_permute_rows (d_x from d_x_perm).  Limits: H a multiple
+ * of 4.
+ *
+ * moe_unpermute_combine_backward: the gradient of moe_unpermute_combine for
+ * an upstream d_out [T,H] (the Megatron section of the same page: permute
+ * and unpermute are each other's gradients).  For r < P:
+ *   d_y_perm[r] = topk_weights[s] * d_out[s / K]   with s = sorted_token_ids[r]
+ *                 < T*K (the product in fp32, delivered in d_y_perm_dtype,
+ *                 MOE_F32 or MOE_BF16 rounded to nearest even); a zero row
+ *                 for a padding row;
+ *   d_topk_weights[s] = <d_out[s / K], y_perm[r]>  (fp32 sums);
+ * d_topk_weights[i] = 0 for a slot whose topk_ids[i] is outside [0,E); rows
+ * from P to C are not written.  d_out device fp32 [T,H]; y_perm device fp32
+ * [C,H] (the forward's); topk_weights device fp32 [T,K]; topk_ids,
+ * sorted_token_ids, num_tokens_post_padded as for moe_permute_rows with the
+ * same T,K,E,B; d_y_perm device [C,H]; d_topk_weights device fp32 [T,K].
+ * Limits: H a multiple of 4.
  */
 moe_status_t moe_permute_rows(const void *x, int32_t T, int32_t K, int32_t E, int32_t B,
                               int64_t row_bytes, const int32_t *topk_ids,
@@ -332,6 +354,13 @@ moe_status_t moe_permute_rows(const void *x, int32_t T, int32_t K, int32_t E, in
 moe_status_t moe_unpermute_combine(int32_t T, int32_t K, int32_t H, const float *y_perm,
                                    const float *topk_weights, const int32_t *row_of_slot,
                                    int32_t out_dtype, void *out, void *stream);
+moe_status_t moe_unpermute_combine_backward(int32_t T, int32_t K, int32_t E, int32_t B, int32_t H,
+                                            const float *d_out, const float *y_perm,
+                                            const float *topk_weights, const int32_t *topk_ids,
+                                            const int32_t *sorted_token_ids,
+                                            const int32_t *num_tokens_post_padded,
+                                            int32_t d_y_perm_dtype, void *d_y_perm,
+                                            float *d_topk_weights, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Backward (training)                                                       */

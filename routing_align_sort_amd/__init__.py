@@ -48,7 +48,7 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
             "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_prepack_weights",
             "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine",
-            "moe_ffn_backward_workspace_bytes", "moe_ffn_backward", "moe_route_backward")
+            "moe_unpermute_combine_backward", "moe_ffn_backward_workspace_bytes", "moe_ffn_backward", "moe_route_backward")
 
 
 def load_library(path: str = LIB_PATH):
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_permute_rows.restype = i32
     lib.moe_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_unpermute_combine.restype = i32
+    lib.moe_unpermute_combine_backward.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i32, P, P, P]
+    lib.moe_unpermute_combine_backward.restype = i32
     lib.moe_ffn_backward_workspace_bytes.argtypes = [ctypes.POINTER(_FfnParams)]
     lib.moe_ffn_backward_workspace_bytes.restype = i64
     lib.moe_ffn_backward.argtypes = [ctypes.POINTER(_FfnParams)] + [P] * 16 + [sz, P]
@@ -379,13 +381,18 @@ def moe_permute_rows(x, topk_ids, sorted_token_ids, num_tokens_post_padded, E, B
 
 
 def moe_unpermute_combine(y_perm, topk_weights, row_of_slot, *, out_dtype=torch.bfloat16, out=None,
-                          stream=None):
-    """out[t] = sum_k w[t,k] * y_perm[row_of_slot[t*K+k]] (ascending k, rows < 0 skipped)."""
+                          stream=None, T=None, K=None):
+    """out[t] = sum_k w[t,k] * y_perm[row_of_slot[t*K+k]] (ascending k, rows < 0 skipped).
+    topk_weights None: every weight is 1 (the gradient of moe_permute_rows);
+    then T and K must be given."""
     lib = load_library()
-    T, K = topk_weights.shape
+    if topk_weights is not None:
+        T, K = topk_weights.shape
+        _need(topk_weights, torch.float32, "topk_weights", T * K)
+    elif T is None or K is None:
+        raise ValueError("unit weights need T and K")
     H = y_perm.shape[1]
     _need(y_perm, torch.float32, "y_perm")
-    _need(topk_weights, torch.float32, "topk_weights", T * K)
     _need(row_of_slot, torch.int32, "row_of_slot", T * K)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=y_perm.device)
@@ -394,6 +401,36 @@ def moe_unpermute_combine(y_perm, topk_weights, row_of_slot, *, out_dtype=torch.
         T, K, H, _ptr(y_perm), _ptr(topk_weights), _ptr(row_of_slot), _DT[out_dtype], _ptr(out),
         _stream(stream)))
     return out
+
+
+def moe_unpermute_combine_backward(d_out, y_perm, topk_weights, topk_ids, sorted_token_ids,
+                                   num_tokens_post_padded, E, B, *, d_y_perm_dtype=torch.float32,
+                                   d_y_perm=None, d_topk_weights=None, stream=None):
+    """Gradient of moe_unpermute_combine for the upstream d_out [T,H]: returns
+    (d_y_perm [C,H], d_topk_weights fp32 [T,K]).  d_y_perm[r] = w[s] d_out[s//K]
+    for the slot s in row r < P, zeros for a padding row; rows from P on are
+    not written.  d_topk_weights[s] = <d_out[s//K], y_perm[r]>, 0 for a skipped slot."""
+    lib = load_library()
+    T, K = topk_ids.shape
+    H = d_out.shape[1]
+    C = moe_align_sort_capacity(T, K, E, B)
+    _need(d_out, torch.float32, "d_out", T * H)
+    _need(y_perm, torch.float32, "y_perm", C * H)
+    _need(topk_weights, torch.float32, "topk_weights", T * K)
+    _need(topk_ids, torch.int32, "topk_ids", T * K)
+    _need(sorted_token_ids, torch.int32, "sorted_token_ids", C)
+    _need(num_tokens_post_padded, torch.int32, "num_tokens_post_padded", 1)
+    if d_y_perm is None:
+        d_y_perm = torch.empty((C, H), dtype=d_y_perm_dtype, device=d_out.device)
+    _need(d_y_perm, d_y_perm_dtype, "d_y_perm", C * H)
+    if d_topk_weights is None:
+        d_topk_weights = torch.empty((T, K), dtype=torch.float32, device=d_out.device)
+    _need(d_topk_weights, torch.float32, "d_topk_weights", T * K)
+    _check("moe_unpermute_combine_backward", lib.moe_unpermute_combine_backward(
+        T, K, E, B, H, _ptr(d_out), _ptr(y_perm), _ptr(topk_weights), _ptr(topk_ids),
+        _ptr(sorted_token_ids), _ptr(num_tokens_post_padded), _DT[d_y_perm_dtype], _ptr(d_y_perm),
+        _ptr(d_topk_weights), _stream(stream)))
+    return d_y_perm, d_topk_weights
 
 
 # ---------------------------------------------------------------- backward --

@@ -132,11 +132,6 @@ swiglu_bwd_kernel(int I, const int32_t* __restrict__ post_padded, const float* _
     }
 }
 
-__global__ void __launch_bounds__(kBwdThreads) fill_f32_kernel(float* p, int64_t n, float v) {
-    const int64_t i = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
-    if (i < n) p[i] = v;
-}
-
 // --------------------------------------------------------- routing backward --
 // One wave per token, scores in double (as the forward computes them):
 // dL/ds_e = c (d_w_k / N - [renorm] sum_j d_w_j s_j / N^2) for the chosen
@@ -232,7 +227,7 @@ static inline int64_t al256(int64_t v) { return (v + 255) / 256 * 256; }
 
 struct BwdWs {
     uint16_t *x_perm, *dy_slots, *dy_perm, *a_bf, *dgu, *dyt, *dgut;
-    float *gu, *d_a, *dxs, *ones;
+    float *gu, *d_a, *dxs;
     int32_t *row_of_slot, *row_of_slot2;
 };
 
@@ -251,7 +246,6 @@ static BwdWs bwd_ws(void* ws, int64_t T, int64_t K, int64_t E, int64_t H, int64_
     w.dxs = (float*)take(C * H * 4);
     w.dyt = (uint16_t*)take(H * C * 2);
     w.dgut = (uint16_t*)take(2 * I * C * 2);
-    w.ones = (float*)take(S * 4);
     w.row_of_slot = (int32_t*)take(S * 4);
     w.row_of_slot2 = (int32_t*)take(S * 4);
     if (total) *total = p - static_cast<uint8_t*>(ws);
@@ -296,11 +290,7 @@ hipError_t launch_ffn_backward(const BwdArgs& a, void* ws, hipStream_t st) {
     g.a = w.dgu; g.lda = 2 * I; g.b = a.w13; g.ldb = H; g.b_group = 2 * I * H; g.c = w.dxs; g.ldc = H;
     g.N = (int)H; g.K = (int)(2 * I);
     MOE_TRY(launch_nn_gemm(g, a.B, nblk, st));
-    if (S > 0)
-        hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((S + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads),
-                           0, st, w.ones, S, 1.0f);
-    MOE_TRY(hipGetLastError());
-    MOE_TRY(launch_unpermute_combine(a.T, a.K, (int)H, w.dxs, w.ones, w.row_of_slot, 0, a.dx, st));
+    MOE_TRY(launch_unpermute_combine(a.T, a.K, (int)H, w.dxs, nullptr, w.row_of_slot, 0, a.dx, st));
     // 4. weight gradients per expert: transposed dy / [d_g d_u] (K = the expert's rows,
     //    contiguous) against the rows of a~ / x
     MOE_TRY(transpose(w.dy_perm, w.dyt, (int)C, (int)H, C, 1, 0, 0, a.post_padded, st));

@@ -294,9 +294,29 @@ moe_status_t moe_unpermute_combine(int32_t T, int32_t K, int32_t H, const float*
     if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (H % 4) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
-    if (!y_perm || !topk_weights || !row_of_slot || !out) return MOE_ERR_INVALID_ARG;
+    if (!y_perm || !row_of_slot || !out) return MOE_ERR_INVALID_ARG;   // topk_weights NULL: weight 1
     return from_hip(launch_unpermute_combine(T, K, H, y_perm, topk_weights, row_of_slot, out_dtype == MOE_BF16,
                                              out, as_stream(stream)));
+}
+
+moe_status_t moe_unpermute_combine_backward(int32_t T, int32_t K, int32_t E, int32_t B, int32_t H,
+                                            const float* d_out, const float* y_perm, const float* topk_weights,
+                                            const int32_t* topk_ids, const int32_t* sorted_token_ids,
+                                            const int32_t* num_tokens_post_padded, int32_t d_y_perm_dtype,
+                                            void* d_y_perm, float* d_topk_weights, void* stream) {
+    if (!align_args_ok(T, K, E, B) || H < 1) return MOE_ERR_INVALID_ARG;
+    if (d_y_perm_dtype != MOE_F32 && d_y_perm_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (H % 4) return MOE_ERR_UNSUPPORTED;
+    const int64_t S = (int64_t)T * K;
+    if (S == 0) return MOE_OK;
+    if (!d_out || !y_perm || !topk_weights || !topk_ids || !sorted_token_ids || !num_tokens_post_padded ||
+        !d_y_perm || !d_topk_weights)
+        return MOE_ERR_INVALID_ARG;
+    const int64_t C = capacity(S, E, B);
+    return from_hip(launch_unpermute_combine_backward(K, E, H, S, C, d_out, y_perm, topk_weights, topk_ids,
+                                                      sorted_token_ids, num_tokens_post_padded,
+                                                      d_y_perm_dtype == MOE_BF16, d_y_perm, d_topk_weights,
+                                                      as_stream(stream)));
 }
 
 moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float* y_slots,

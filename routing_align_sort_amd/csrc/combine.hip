@@ -23,6 +23,8 @@ constexpr int kCombineThreads = 256;
 // kMapped: the rows come from the permuted buffer through row_of_slot (a
 // row < 0 is a skipped slot); otherwise from y_slots by slot, skipping ids
 // outside [0,E).  The arithmetic is the same, so both give the same bits.
+// w == nullptr: every weight is 1 (the unweighted sum of a token's rows,
+// which is the gradient of the permute).
 template <bool kBf16, bool kMapped>
 __global__ void __launch_bounds__(kCombineThreads)
 combine_kernel(int T, int K, int E, int H, int nchunk, const float* __restrict__ y,
@@ -41,7 +43,7 @@ combine_kernel(int T, int K, int E, int H, int nchunk, const float* __restrict__
             const int e = ids[i];
             if (e < 0 || e >= E) continue;
         }
-        const float wk = w[i];
+        const float wk = w ? w[i] : 1.f;
         const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)(y + row * H + h));
         acc[0] += wk * v[0];
         acc[1] += wk * v[1];

@@ -130,6 +130,12 @@ hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, cons
                           const int32_t* ids, int out_bf16, void* out, hipStream_t stream);
 hipError_t launch_unpermute_combine(int T, int K, int H, const float* y_perm, const float* w,
                                     const int32_t* row_of_slot, int out_bf16, void* out, hipStream_t stream);
+// Gradient of the unpermute-combine in the permuted layout: d_y_perm rows
+// (fp32 or bf16) and the combine weights' gradient.
+hipError_t launch_unpermute_combine_backward(int K, int E, int H, int64_t S, int64_t C, const float* d_out,
+                                             const float* y_perm, const float* w, const int32_t* ids,
+                                             const int32_t* sorted, const int32_t* post_padded, int out_bf16,
+                                             void* d_y_perm, float* d_w, hipStream_t stream);
 
 // ----------------------------------------------------------------- permute --
 hipError_t launch_permute_rows(const void* x, int64_t row_bytes, int K, int E, int64_t S, int64_t C,

@@ -30,14 +30,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -174,6 +174,15 @@ def test_permute_and_row_layout_validation(lib):
                                 None) == moe.MOE_OK
     assert lib.moe_unpermute_combine(4, 2, 6, P(8), P(8), P(8), 1, P(8), None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(4, 2, 8, None, P(8), P(8), 1, P(8), None) == moe.MOE_ERR_INVALID_ARG
+    # the backward of the unpermute: H a multiple of 4, fp32 or bf16 rows, every pointer given
+    ub = lib.moe_unpermute_combine_backward
+    args = [P(8)] * 6
+    assert ub(4, 2, 8, 16, 6, *args, 0, P(8), P(8), None) == moe.MOE_ERR_UNSUPPORTED
+    assert ub(4, 2, 8, 16, 8, *args, 2, P(8), P(8), None) == moe.MOE_ERR_UNSUPPORTED
+    assert ub(4, 2, 8, 16, 8, *args, 0, P(8), None, None) == moe.MOE_ERR_INVALID_ARG
+    assert ub(4, 2, 8, 16, 8, None, *args[1:], 0, P(8), P(8), None) == moe.MOE_ERR_INVALID_ARG
+    assert ub(4, 0, 8, 16, 8, *args, 0, P(8), P(8), None) == moe.MOE_ERR_INVALID_ARG
+    assert ub(0, 2, 8, 16, 8, None, None, None, None, None, None, 0, None, None, None) == moe.MOE_OK
     # the sorted row layout: not for fp32, unknown layouts rejected, x has C rows
     p = moe._FfnParams(64, 2, 8, 256, 256, 16, 0, 0, 0, moe.MOE_ROWS_SORTED)
     assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) == -1

@@ -134,3 +134,73 @@ def test_layer_sorted_rows_full_size_prefill():
     say("prefill bf16 full size: sorted rows bit-identical to gathered rows")
     del L
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------- gradient of the unpermute --
+@pytest.mark.parametrize("T,K,E,B,H,dt", [
+    (1, 1, 1, 16, 4, torch.float32), (37, 3, 5, 16, 48, torch.float32), (300, 8, 64, 32, 512, torch.bfloat16),
+    (2048, 1, 32, 64, 7168, torch.float32), (16384, 8, 256, 64, 64, torch.bfloat16),
+    (999, 2, 33, 128, 7168, torch.bfloat16)])
+def test_unpermute_combine_backward_matches_oracle(T, K, E, B, H, dt):
+    dev = device()
+    say(f"unpermute backward T={T} K={K} E={E} B={B} H={H} {dt}")
+    rng = np.random.default_rng(T * 7 + H)
+    ids = ids_with_invalid(rng, T, K, E)
+    tid = torch.tensor(ids, device=dev)
+    al = moe.moe_align_sort(tid, E, B)
+    srt_d, ntpp = al["sorted_token_ids"], al["num_tokens_post_padded"]
+    C = srt_d.numel()
+    g = rng.standard_normal((T, H)).astype(np.float32)
+    y = rng.standard_normal((C, H)).astype(np.float32)
+    w = rng.standard_normal((T, K)).astype(np.float32)
+    # rows past the padded count keep what was there; every weight gradient is written
+    dy0 = torch.full((C, H), 7.0, dtype=dt, device=dev)
+    dw0 = torch.full((T, K), -999.0, dtype=torch.float32, device=dev)
+    dy, dw = moe.moe_unpermute_combine_backward(
+        torch.tensor(g, device=dev), torch.tensor(y, device=dev), torch.tensor(w, device=dev), tid, srt_d, ntpp,
+        E, B, d_y_perm_dtype=dt, d_y_perm=dy0.clone(), d_topk_weights=dw0.clone())
+    torch.cuda.synchronize()
+    srt = srt_d.cpu().numpy()
+    P = int(ntpp.item())
+    want_dy, want_dw = oracle.unpermute_combine_backward(g, y, w, srt, P=P,
+                                                         round_to="f32" if dt == torch.float32 else "bf16")
+    got_dy = dy.float().cpu().numpy()
+    assert np.array_equal(got_dy[:P], want_dy.astype(np.float32))                # one product, one rounding
+    assert (got_dy[P:] == 7.0).all()
+    got_dw = dw.cpu().numpy()
+    assert not (got_dw == -999.0).any()
+    ros = oracle.row_of_slot(srt, T * K)
+    skipped = (ros < 0).reshape(T, K)
+    assert (got_dw[skipped] == 0).all()
+    # fp32 sums in another order: within 1e-5 of each slot's sum of |terms|
+    scale = np.zeros((T, K))
+    placed = np.nonzero(ros >= 0)[0]
+    scale.ravel()[placed] = np.abs(g[placed // K].astype(np.float64) * y[ros[placed]]).sum(axis=1)
+    err = np.abs(got_dw - want_dw)
+    assert (err <= 1e-5 * scale + 1e-30).all(), float((err / np.maximum(scale, 1e-30)).max())
+    say(f"  P={P} of C={C}: d_y_perm bit-exact, d_w within {float((err / np.maximum(scale, 1e-30)).max()):.1e}")
+
+
+@pytest.mark.parametrize("T,K,E,B,H", [(37, 3, 5, 16, 48), (2048, 8, 32, 64, 512)])
+def test_unit_weight_unpermute_is_the_permute_gradient(T, K, E, B, H):
+    # d_x[t] = sum of the rows of t's slots: the unweighted unpermute, which
+    # must also give the same bits as the weighted call with weights of 1
+    dev = device()
+    rng = np.random.default_rng(T + 3)
+    ids = ids_with_invalid(rng, T, K, E)
+    tid = torch.tensor(ids, device=dev)
+    al = moe.moe_align_sort(tid, E, B)
+    C = al["sorted_token_ids"].numel()
+    _, ros, _ = moe.moe_permute_rows(torch.zeros((T, 16), dtype=torch.uint8, device=dev), tid,
+                                     al["sorted_token_ids"], al["num_tokens_post_padded"], E, B)
+    d_xp = rng.standard_normal((C, H)).astype(np.float32)
+    d_xp_d = torch.tensor(d_xp, device=dev)
+    dx = moe.moe_unpermute_combine(d_xp_d, None, ros, out_dtype=torch.float32, T=T, K=K)
+    ones = torch.ones((T, K), dtype=torch.float32, device=dev)
+    dx1 = moe.moe_unpermute_combine(d_xp_d, ones, ros, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx1)
+    want = oracle.unpermute_combine(d_xp, np.ones((T, K), np.float32), ros.cpu().numpy())
+    scale = oracle.unpermute_combine(np.abs(d_xp), np.ones((T, K), np.float32), ros.cpu().numpy())
+    assert (np.abs(dx.cpu().numpy() - want) <= 1e-6 * scale + 1e-30).all()
+    say(f"unit-weight unpermute T={T} K={K}: equals the weighted call, within 1e-6 of the oracle")
