@@ -220,6 +220,11 @@ CONFIGS = {
     "prefill_fp8": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e4m3", score="softmax",
                         bias=False, n_group=1, topk_group=1, renormalize=False,
                         routing="zipf", zipf_s=1.2, shared=True, B=64),
+    # The a8w8 shape of the pages' aiter kernel figure: 2048 token-slots as
+    # 32 experts x 64 tokens (uniform routing, no shared expert), fp8.
+    "prefill_fp8_uniform": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e4m3", score="softmax",
+                                bias=False, n_group=1, topk_group=1, renormalize=False,
+                                routing="uniform", B=64),
     # Compute-bound shapes of the same layer: 2048 tokens x top-8 over the 32
     # local experts, exactly 512 slots per expert (bf16; and fp8 + shared expert).
     "prefill_bf16_512": dict(T=2048, H=7168, I=2048, E=32, K=8, dtype="bf16", score="softmax",

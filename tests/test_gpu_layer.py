@@ -212,3 +212,27 @@ def test_layer_prefill_mxfp4_full_size():
         check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill mxfp4 B={B}")
     del L
     torch.cuda.empty_cache()
+
+
+def test_layer_prefill_fp8_uniform_full_size():
+    # the pages' aiter a8w8 shape: 32 experts x 64 tokens, fp8
+    dev = device()
+    cfg = ms.CONFIGS["prefill_fp8_uniform"]
+    say("generating prefill fp8 weights (32 experts, 1.41 GB), uniform routing")
+    L = ms.make_layer(cfg, device=dev)
+    for B in (32, 64):
+        check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill fp8 uniform B={B}")
+    del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16_512", "prefill_fp8_512", "prefill_fp4_512"])
+def test_layer_512_per_expert_full_size(name):
+    # the compute-bound shapes at the block size the bench times them with
+    dev = device()
+    cfg = ms.CONFIGS[name]
+    say(f"generating {name} weights; 2048 tokens x top-{cfg['K']} over {cfg['E']} experts")
+    L = ms.make_layer(cfg, device=dev)
+    check_layer(cfg, L, sample_tokens(cfg["T"], 16, 5), B=128, label=f"{name} B=128")
+    del L
+    torch.cuda.empty_cache()
