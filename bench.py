@@ -424,6 +424,19 @@ def main():
             sweep[str(b2)] = {"us_per_step": round(sm["us_per_step"], 1), "gate_up_us": sm["us"]["gate_up"],
                               "down_us": sm["us"]["down"], "grouped_gemm_tflops": round(sm["grouped_gemm_tflops"], 1)}
         line["block_size_sweep"] = sweep
+        # the fp8 workload (Zipf routing + shared expert) over the same block
+        # sizes: its heavy experts re-read their weights once per block
+        if args.workload != "prefill_fp8":
+            c2 = ms.CONFIGS["prefill_fp8"]
+            sw8 = {}
+            for b2 in (32, 64, 128):
+                r2 = run_layer_timed(c2, b2, 10, 3, dev, graph=False)
+                sm = summarize(c2, b2, r2)
+                del r2
+                torch.cuda.empty_cache()
+                sw8[str(b2)] = {"us_per_step": round(sm["us_per_step"], 1), "gate_up_us": sm["us"]["gate_up"],
+                                "down_us": sm["us"]["down"], "num_tokens_post_padded": sm["num_tokens_post_padded"]}
+            line["block_size_sweep_prefill_fp8"] = sw8
         line["permute_path"] = permute_path(dev)
         line["ffn_input_state"] = ffn_input_state(dev)
         line["one_stage_schedule"] = one_stage(dev)

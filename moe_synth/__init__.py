@@ -219,7 +219,7 @@ CONFIGS = {
     # The a8w8 variant: Zipf(1.2) over 32 experts plus one always-on shared expert.
     "prefill_fp8": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e4m3", score="softmax",
                         bias=False, n_group=1, topk_group=1, renormalize=False,
-                        routing="zipf", zipf_s=1.2, shared=True, B=64),
+                        routing="zipf", zipf_s=1.2, shared=True, B=128),
     # The a8w8 shape of the pages' aiter kernel figure: 2048 token-slots as
     # 32 experts x 64 tokens (uniform routing, no shared expert), fp8.
     "prefill_fp8_uniform": dict(T=2048, H=7168, I=2048, E=32, K=1, dtype="e4m3", score="softmax",
