@@ -116,6 +116,20 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=
         layer.forward(*inputs[s % rotate], bias)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # a top-1 layer runs its FFN and combine as one call; the same steps with
+    # the two calls apart, for comparison
+    wall_sep = float("nan")
+    if layer.top1:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            xs, ls = inputs[s % rotate]
+            layer.route(ls, bias)
+            layer.align()
+            layer.ffn(xs)
+            layer.combine()
+        torch.cuda.synchronize()
+        wall_sep = time.perf_counter() - t0
     # 2. the same four calls captured once in a HIP graph and replayed
     wall_graph = float("nan")
     if graph:
@@ -163,6 +177,7 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=
     ids_np = layer.topk_ids.cpu().numpy()
     res = {
         "wall_s": wall,
+        "wall_sep_s": wall_sep,
         "wall_graph_s": wall_graph,
         "us": {n: _mean(v) for n, v in per.items()},
         "us_step_events": _mean(total),
@@ -189,6 +204,8 @@ def summarize(cfg, B, r):
         "tokens_per_s": cfg["T"] * steps / r["wall_s"],
         "us_per_step": r["wall_s"] / steps * 1e6,
         "graph_us_per_step": r["wall_graph_s"] / steps * 1e6 if r["wall_graph_s"] == r["wall_graph_s"] else None,
+        "us_per_step_ffn_then_combine": (r["wall_sep_s"] / steps * 1e6 if r["wall_sep_s"] == r["wall_sep_s"]
+                                         else None),
         "event_timed_us_per_step": r["us_step_events"],
         "us": {k: round(v, 2) for k, v in us.items()},
         "experts_hit": ab["experts_hit"],
@@ -526,7 +543,9 @@ def backward_step(dev, steps=10, warmup=3):
     import routing_align_sort_amd as moe
     cfg = ms.CONFIGS["prefill_bf16"]
     L = ms.make_layer(cfg, device=dev)
-    layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=1, B=cfg["B"], score="softmax", renormalize=False)
+    # a training forward keeps the slot rows the backward reads (no top-1 fusion)
+    layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=1, B=cfg["B"], score="softmax", renormalize=False,
+                         top1=False)
     x, logits = L["x"], L["logits"]
     layer.forward(x, logits)
     d_out = torch.randn((cfg["T"], cfg["H"]), dtype=torch.float32, device=dev)

@@ -10,6 +10,8 @@
  *   moe_grouped_ffn  x, expert weights, the sorted layout -> y_slots [T*K, H]
  *   moe_combine      y_slots, topk weights   -> out [T,H]
  *
+ * (with top-1 routing, moe_grouped_ffn_top1 does the last two in one call),
+ *
  * or, with the rows moved into the sorted order first (the layout a
  * dispatch to expert-owning GPUs sends):
  *
@@ -55,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
     MOE_OK = 0,
@@ -239,6 +241,29 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t *p, const void *x, const voi
                              const int32_t *sorted_token_ids, const int32_t *expert_ids,
                              const int32_t *num_tokens_post_padded, float *y_slots,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_grouped_ffn followed by moe_combine for top-1 routing, in one call.  The
+ * combine is defined as for moe_combine (the dignews.cc page, opening
+ * paragraphs: a token's output is the gate-weighted result of its chosen
+ * experts).  With K == 1 every token has at most one slot, so the sum has one
+ * term, and the down GEMM writes it straight into out.
+ *   out[t,h] = 0 + topk_weights[t] * y[t,h]   (fp32; the bits of moe_combine)
+ *   out[t]   = 0 where topk_ids[t] is outside [0,E)
+ * p as for moe_grouped_ffn with p->K == 1 (no appended shared expert),
+ * MOE_ROWS_BY_TOKEN and MOE_SCHEDULE_TWO_LAUNCH; bf16, E4M3 or E2M1 weights
+ * (fp32: MOE_ERR_UNSUPPORTED).  K != 1 is MOE_ERR_INVALID_ARG.  topk_ids
+ * int32 [T] and topk_weights fp32 [T] as moe_route_topk wrote them; out
+ * device [T,H] in out_dtype (MOE_F32 or MOE_BF16, bf16 rounded to nearest
+ * even).  workspace: moe_grouped_ffn_workspace_bytes(p) bytes.  No y_slots
+ * buffer is written.
+ */
+moe_status_t moe_grouped_ffn_top1(const moe_ffn_params_t *p, const void *x, const void *w13,
+                                  const void *w13_scale, const void *w2, const void *w2_scale,
+                                  const int32_t *sorted_token_ids, const int32_t *expert_ids,
+                                  const int32_t *num_tokens_post_padded, const int32_t *topk_ids,
+                                  const float *topk_weights, int32_t out_dtype, void *out,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One-time weight preparation, off the per-token path: rewrites canonical

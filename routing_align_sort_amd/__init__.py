@@ -46,7 +46,7 @@ class _FfnParams(ctypes.Structure):
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
-            "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_prepack_weights",
+            "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_grouped_ffn_top1", "moe_prepack_weights",
             "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine",
             "moe_unpermute_combine_backward", "moe_ffn_backward_workspace_bytes", "moe_ffn_backward", "moe_route_backward")
 
@@ -77,6 +77,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_grouped_ffn.restype = i32
     lib.moe_grouped_ffn_profiled.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P, P, P, P, P, P,
                                              sz, P, P]
+    lib.moe_grouped_ffn_top1.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P, P, P, P, P, P, i32, P, P,
+                                         sz, P]
+    lib.moe_grouped_ffn_top1.restype = i32
     lib.moe_grouped_ffn_profiled.restype = i32
     lib.moe_prepack_weights.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P]
     lib.moe_prepack_weights.restype = i32
@@ -326,6 +329,47 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     return y_slots
 
 
+def moe_grouped_ffn_top1(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, topk_ids,
+                         topk_weights, *, B, w13_scale=None, w2_scale=None, out_dtype=torch.bfloat16,
+                         out=None, workspace=None, stream=None, packed=False):
+    """moe_grouped_ffn + moe_combine for top-1 routing in one call: out[t] =
+    w[t] * FFN(x[t]) (zero rows for ids outside [0,E)); same bits as the two calls."""
+    lib = load_library()
+    T, H = x.shape
+    E, I, H2 = weight_dims(w13)
+    fp4 = w13.dtype == FP4
+    if H2 != H or tuple(w2.shape) != (E, H, I // 2 if fp4 else I):
+        raise ValueError("weight shapes do not match x")
+    if tuple(topk_ids.shape) != (T, 1):
+        raise ValueError("moe_grouped_ffn_top1 needs topk_ids of shape [T, 1]")
+    _need(x, x.dtype, "x")
+    _need(w13, w13.dtype, "w13")
+    _need(w2, w13.dtype, "w2")
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (num_tokens_post_padded, "num_tokens_post_padded"), (topk_ids, "topk_ids")):
+        _need(t, torch.int32, n)
+    _need(topk_weights, torch.float32, "topk_weights", T)
+    if w13.dtype == torch.float8_e4m3fn:
+        _need(w13_scale, torch.float32, "w13_scale", E * 2 * I)
+        _need(w2_scale, torch.float32, "w2_scale", E * H)
+    if fp4:
+        _need(w13_scale, E8M0, "w13_scale", E * 2 * I * (H // 32))
+        _need(w2_scale, E8M0, "w2_scale", E * H * (I // 32))
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=x.device)
+    _need(out, out_dtype, "out", T * H)
+    p = _ffn_params(T, 1, E, H, I, B, w13.dtype, x.dtype, packed, False, False)
+    need = moe_grouped_ffn_workspace_bytes(T, 1, E, H, I, B, w13.dtype, x.dtype, False, False)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("moe_grouped_ffn_top1", lib.moe_grouped_ffn_top1(
+        ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(topk_ids),
+        _ptr(topk_weights), _DT[out_dtype], _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
 # ------------------------------------------------------------------ combine --
 def moe_combine(y_slots, topk_weights, topk_ids, E, *, out_dtype=torch.bfloat16, out=None,
                 stream=None):
@@ -505,12 +549,15 @@ class MoELayer:
     With rows="sorted" the token rows are first moved into the sorted order
     (permute), the FFN reads and writes that order, and the combine reads back
     through the inverse map (route -> align -> permute -> FFN -> unpermute).
+    top1: with one slot per token (K 1, no shared expert, rows by token, the
+    two-launch schedule, not fp32) "auto" runs the FFN and the combine as one
+    call (moe_grouped_ffn_top1; the same output bits); False keeps them apart.
     """
 
     def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
                  w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None,
-                 rows="by_token", schedule="two_launch"):
+                 rows="by_token", schedule="two_launch", top1="auto"):
         dev = w13.device
         if packed is None:
             packed = w13.dtype != torch.float32
@@ -559,6 +606,13 @@ class MoELayer:
             self.x_perm = torch.empty((C, self.H), dtype=x_dtype, device=dev)
             self.row_of_slot = torch.empty(T * self.KO, dtype=torch.int32, device=dev)
         self.out = torch.empty((T, self.H), dtype=out_dtype, device=dev)
+        eligible = (self.KO == 1 and not self.rows_sorted and not self.fused and w13.dtype != torch.float32)
+        if top1 not in ("auto", True, False):
+            raise ValueError("top1 must be 'auto', True or False")
+        if top1 is True and not eligible:
+            raise ValueError("top1 needs K 1 without a shared expert, rows by token, two launches, not fp32")
+        self.top1 = eligible and top1 is not False
+        self._y_current = False     # y_slots holds the last forward's rows (the backward reads them)
 
     def route(self, logits, bias=None):
         return moe_route_topk(logits, self.K, bias=bias, topk_ids=self.topk_ids,
@@ -574,6 +628,7 @@ class MoELayer:
                                 x_perm=self.x_perm, row_of_slot=self.row_of_slot)
 
     def ffn(self, x, stage_events=None):
+        self._y_current = True
         if self.rows_sorted:
             return moe_grouped_ffn(self.x_perm, self.w13, self.w2, self.sorted, self.expert_ids,
                                    self.ntpp, K=self.KO, B=self.B, w13_scale=self.w13_scale,
@@ -598,8 +653,20 @@ class MoELayer:
         return moe_combine(self.y_slots, self.topk_weights, self.topk_ids, self.E_slabs,
                            out_dtype=self.out_dtype, out=self.out)
 
+    def ffn_top1(self, x):
+        """The FFN and the combine of a top-1 layer in one call (into self.out)."""
+        self._y_current = False
+        return moe_grouped_ffn_top1(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
+                                    self.topk_ids, self.topk_weights, B=self.B, w13_scale=self.w13_scale,
+                                    w2_scale=self.w2_scale, out_dtype=self.out_dtype, out=self.out,
+                                    workspace=self.ws_ffn, packed=self.packed)
+
     def backward(self, x, logits, d_out, workspace=None):
-        """Gradients after forward(x, logits): (dx, dw13, dw2, d_logits), fp32."""
+        """Gradients after forward(x, logits): (dx, dw13, dw2, d_logits), fp32.
+        The backward reads the forward's slot rows; after a top-1 forward,
+        which does not write them, they are recomputed first."""
+        if not self._y_current:
+            self.ffn(x)
         dx, dw13, dw2, dwk = moe_ffn_backward(
             x, self.w13_canonical, self.w2_canonical, self.topk_ids, self.topk_weights, self.sorted,
             self.expert_ids, self.ntpp, self.offsets, self.y_slots, d_out, B=self.B, workspace=workspace)
@@ -614,6 +681,8 @@ class MoELayer:
         self.align()
         if self.rows_sorted:
             self.permute(x)
+        if self.top1:
+            return self.ffn_top1(x)
         self.ffn(x)
         return self.combine()
 

@@ -151,24 +151,34 @@ int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t* p) {
     return ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C, p->schedule == MOE_SCHEDULE_FUSED);
 }
 
+// The top-1 combine fused into the down GEMM (moe_grouped_ffn_top1); out
+// null for the plain FFN.
+struct Top1Out {
+    const int32_t* ids;
+    const float* w;
+    void* out;
+    int bf16;
+};
+
 static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
                                 const void* w13_scale, const void* w2, const void* w2_scale,
                                 const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                                const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
-                                size_t workspace_bytes, void* stream, hipEvent_t const* ev) {
+                                const int32_t* num_tokens_post_padded, float* y_slots, const Top1Out& top1,
+                                void* workspace, size_t workspace_bytes, void* stream, hipEvent_t const* ev) {
     const moe_status_t st = ffn_check(p);
     if (st != MOE_OK) return st;
     const int64_t S = (int64_t)p->T * p->K;
     const int64_t C = capacity(S, p->E, p->B);
     if (S == 0) return MOE_OK;
-    if (!x || !w13 || !w2 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded || !y_slots)
+    if (!x || !w13 || !w2 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded ||
+        (!y_slots && !top1.out))
         return MOE_ERR_INVALID_ARG;
     if ((p->w_dtype == MOE_FP8_E4M3 || p->w_dtype == MOE_FP4_E2M1) && (!w13_scale || !w2_scale))
         return MOE_ERR_INVALID_ARG;
     const int64_t need =
         ffn_workspace_bytes(p->w_dtype, ffn_x_rows(p), p->H, p->I, C, p->schedule == MOE_SCHEDULE_FUSED);
     if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
-    FfnArgs a;
+    FfnArgs a{};
     a.T = p->T; a.K = p->K; a.E = p->E; a.H = p->H; a.I = p->I; a.B = p->B;
     a.S = S; a.C = C;
     a.x = x; a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
@@ -177,6 +187,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     a.packed = p->weight_layout == MOE_LAYOUT_PACKED;
     a.rows_sorted = p->row_layout == MOE_ROWS_SORTED;
     a.fused = p->schedule == MOE_SCHEDULE_FUSED;
+    a.top1_w = top1.w; a.top1_ids = top1.ids; a.top1_out = top1.out; a.top1_bf16 = top1.bf16;
     hipError_t e;
     if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream), ev);
     else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream), ev);
@@ -191,7 +202,26 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const voi
                              const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
                              size_t workspace_bytes, void* stream) {
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
-                       num_tokens_post_padded, y_slots, workspace, workspace_bytes, stream, nullptr);
+                       num_tokens_post_padded, y_slots, Top1Out{}, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status_t moe_grouped_ffn_top1(const moe_ffn_params_t* p, const void* x, const void* w13,
+                                  const void* w13_scale, const void* w2, const void* w2_scale,
+                                  const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                  const int32_t* num_tokens_post_padded, const int32_t* topk_ids,
+                                  const float* topk_weights, int32_t out_dtype, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    const moe_status_t st = ffn_check(p);
+    if (st != MOE_OK) return st;
+    if (p->K != 1) return MOE_ERR_INVALID_ARG;
+    if (p->w_dtype == MOE_F32 || p->row_layout != MOE_ROWS_BY_TOKEN || p->schedule != MOE_SCHEDULE_TWO_LAUNCH)
+        return MOE_ERR_UNSUPPORTED;
+    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->T == 0) return MOE_OK;
+    if (!topk_ids || !topk_weights || !out) return MOE_ERR_INVALID_ARG;
+    return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                       num_tokens_post_padded, nullptr, Top1Out{topk_ids, topk_weights, out, out_dtype == MOE_BF16},
+                       workspace, workspace_bytes, stream, nullptr);
 }
 
 moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, const void* w13,
@@ -204,7 +234,7 @@ moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, 
     for (int i = 0; i < 5; ++i)
         if (!events[i]) return MOE_ERR_INVALID_ARG;
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
-                       num_tokens_post_padded, y_slots, workspace, workspace_bytes, stream,
+                       num_tokens_post_padded, y_slots, Top1Out{}, workspace, workspace_bytes, stream,
                        reinterpret_cast<hipEvent_t const*>(events));
 }
 

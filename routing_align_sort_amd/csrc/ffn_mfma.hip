@@ -652,19 +652,56 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
                         y0 = y0 * rs * s0;
                         y1 = y1 * rs * s1;
                     }
-                    const int64_t yrow = a.rows_sorted ? (int64_t)mb * BM + m : (int64_t)slot;
-                    float* dst = a.y_slots + yrow * H + n0 + r32;
-                    dst[0] = y0;
-                    dst[32] = y1;
+                    if (a.top1_out) {
+                        // the combine of a token's single slot: 0 + w * y in
+                        // fp32, as the separate combine sums it
+                        const float wt = a.top1_w[slot];
+                        float o0 = 0.f, o1 = 0.f;
+                        o0 += wt * y0;
+                        o1 += wt * y1;
+                        const int64_t off = (int64_t)slot * H + n0 + r32;
+                        if (a.top1_bf16) {
+                            uint16_t* dst = (uint16_t*)a.top1_out + off;
+                            dst[0] = f32_to_bf16_bits(o0);
+                            dst[32] = f32_to_bf16_bits(o1);
+                        } else {
+                            float* dst = (float*)a.top1_out + off;
+                            dst[0] = o0;
+                            dst[32] = o1;
+                        }
+                    } else {
+                        const int64_t yrow = a.rows_sorted ? (int64_t)mb * BM + m : (int64_t)slot;
+                        float* dst = a.y_slots + yrow * H + n0 + r32;
+                        dst[0] = y0;
+                        dst[32] = y1;
+                    }
                 }
             }
         }
+}
+
+// Top-1 combine: a token whose id is outside [0,E) has no slot in the layout,
+// so no tile writes its output row; the workgroups of the down launch (every
+// one, tile or not) zero those rows, token t by workgroup t mod gridDim.
+__device__ __forceinline__ void top1_zero_skipped(const FfnArgs& a) {
+    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) {
+        const int e = a.top1_ids[t];
+        if (e >= 0 && e < a.E) continue;
+        if (a.top1_bf16) {
+            uint16_t* row = (uint16_t*)a.top1_out + t * a.H;
+            for (int h = threadIdx.x * 8; h < a.H; h += kFfnThreads * 8) *(uint4*)(row + h) = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            float* row = (float*)a.top1_out + t * a.H;
+            for (int h = threadIdx.x * 4; h < a.H; h += kFfnThreads * 4) *(uint4*)(row + h) = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
 }
 
 template <int kW, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     __shared__ FfnSmem<BM> sm;
+    if (a.top1_out) top1_zero_skipped(a);
     int mb, nt;
     if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
     stage2_tile<kW, kPacked, BM, PF>(a, h_in, sa, mb, nt, sm);

@@ -53,6 +53,14 @@ struct FfnArgs {
     int packed;                // weights in the layout written by launch_prepack
     int rows_sorted;           // x is [C,H] in the sorted row order, y written in that order
     int fused;                 // both GEMMs in one persistent launch
+    // Top-1 combine in the down GEMM's epilogue (K == 1, rows by token): when
+    // top1_out is set, out[t] = top1_w[t] * y of t's slot is written there
+    // (bf16 when top1_bf16, else fp32) instead of y_slots, and tokens whose
+    // id is outside [0,E) get zero rows.
+    const float* top1_w;
+    const int32_t* top1_ids;
+    void* top1_out;
+    int top1_bf16;
 };
 // Largest activation operand (bytes of x, or of the intermediate, as one
 // GEMM reads it) of the matrix-core kernels: they address it with 32-bit

@@ -88,9 +88,9 @@ def route_oracle(cfg, L, K=None):
     return ids, w
 
 
-def make_gpu_layer(cfg, L, B=None, packed=None):
+def make_gpu_layer(cfg, L, B=None, packed=None, top1="auto"):
     w13, w2, s13, s2 = as_library_weights(L)
-    return moe.MoELayer(w13, w2, T=cfg["T"], K=cfg["K"], B=B or cfg["B"], packed=packed,
+    return moe.MoELayer(w13, w2, T=cfg["T"], K=cfg["K"], B=B or cfg["B"], packed=packed, top1=top1,
                         score=cfg["score"], n_group=cfg["n_group"], topk_group=cfg["topk_group"],
                         renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
                         w13_scale=s13, w2_scale=s2,

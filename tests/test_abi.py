@@ -30,14 +30,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -174,6 +174,19 @@ def test_permute_and_row_layout_validation(lib):
                                 None) == moe.MOE_OK
     assert lib.moe_unpermute_combine(4, 2, 6, P(8), P(8), P(8), 1, P(8), None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_unpermute_combine(4, 2, 8, None, P(8), P(8), 1, P(8), None) == moe.MOE_ERR_INVALID_ARG
+    # the top-1 FFN + combine: K must be 1; fp32, sorted rows and the one-stage schedule are not built
+    t1 = lib.moe_grouped_ffn_top1
+    q = moe._FfnParams(64, 1, 8, 256, 256, 16, 1, 1, 0, moe.MOE_ROWS_BY_TOKEN)
+    ptrs = [P(8)] * 10
+    assert t1(ctypes.byref(q), *ptrs, 1, P(8), P(8), 0, None) == moe.MOE_ERR_WORKSPACE
+    assert t1(ctypes.byref(q), *ptrs, 2, P(8), P(8), 0, None) == moe.MOE_ERR_UNSUPPORTED
+    assert t1(ctypes.byref(q), *ptrs, 1, None, P(8), 0, None) == moe.MOE_ERR_INVALID_ARG
+    q.K = 2
+    assert t1(ctypes.byref(q), *ptrs, 1, P(8), P(8), 0, None) == moe.MOE_ERR_INVALID_ARG
+    q.K = 1; q.w_dtype = q.x_dtype = 0
+    assert t1(ctypes.byref(q), *ptrs, 1, P(8), P(8), 0, None) == moe.MOE_ERR_UNSUPPORTED
+    q.w_dtype = q.x_dtype = 1; q.row_layout = moe.MOE_ROWS_SORTED
+    assert t1(ctypes.byref(q), *ptrs, 1, P(8), P(8), 0, None) == moe.MOE_ERR_UNSUPPORTED
     # the backward of the unpermute: H a multiple of 4, fp32 or bf16 rows, every pointer given
     ub = lib.moe_unpermute_combine_backward
     args = [P(8)] * 6

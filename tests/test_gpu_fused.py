@@ -23,7 +23,7 @@ def layer_for(cfg, L, B, **kw):
 
 
 def compare(cfg, L, B, rows="by_token", calls=2):
-    two = layer_for(cfg, L, B, rows=rows)
+    two = layer_for(cfg, L, B, rows=rows, top1=False)      # its slot rows are compared
     one = layer_for(cfg, L, B, rows=rows, schedule="fused")
     ref = two.forward(L["x"], L["logits"], L["bias"]).clone()
     for c in range(calls):

@@ -20,8 +20,9 @@ def eager(layer, x, logits, bias):
     return out, layer.y_slots.clone(), layer.sorted.clone()
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8"])
+@pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8", "prefill_bf16"])
 def test_layer_graph_replays_match_eager(name):
+    # prefill_bf16 is top-1: its FFN and combine run as one call, with no slot rows
     dev = device()
     if name == "decode_bf16":
         cfg = ms.scaled(name, T=96, H=512, I=256, E=16, K=4, n_group=4, topk_group=2)
@@ -58,7 +59,8 @@ def test_layer_graph_replays_match_eager(name):
         want = ref2 if use2 else ref1
         say(f"{name}: replay {rep} ({'second' if use2 else 'first'} inputs)")
         assert torch.equal(layer.sorted, want[2]), rep
-        assert torch.equal(layer.y_slots, want[1]), rep
+        if not layer.top1:
+            assert torch.equal(layer.y_slots, want[1]), rep
         assert torch.equal(layer.out, want[0]), rep
         # eager work of the program's own between replays
         junk = torch.randn(1 << 20, device=dev)

@@ -17,8 +17,17 @@ pytestmark = pytest.mark.gpu
 
 
 def run_layer(cfg, L, B=None):
+    """The layer's forward as a caller runs it.  A top-1 layer runs the FFN and
+    the combine as one call (no slot rows written); it is also run through the
+    separate FFN + combine, which must give the same output bits, so that its
+    slot rows are there to compare as well."""
     layer = make_gpu_layer(cfg, L, B)
-    out = layer.forward(L["x"], L["logits"], L["bias"])
+    out = layer.forward(L["x"], L["logits"], L["bias"]).clone()
+    if layer.top1:
+        layer.ffn(L["x"])
+        sep = layer.combine()
+        torch.cuda.synchronize()
+        assert torch.equal(sep, out), "top-1 FFN + combine differs from the separate calls"
     torch.cuda.synchronize()
     return layer, out
 
@@ -111,7 +120,7 @@ def test_packed_weights_give_identical_results():
         for B in (16, 64, 128, 256):
             ys = []
             for packed in (False, True):
-                layer = make_gpu_layer(cfg, L, B, packed=packed)
+                layer = make_gpu_layer(cfg, L, B, packed=packed, top1=False)     # compares slot rows
                 layer.forward(L["x"], L["logits"], L["bias"])
                 torch.cuda.synchronize()
                 ys.append(layer.y_slots.clone())
