@@ -340,9 +340,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); multi-GPU sharding is described in DESIGN.md, not built.",
-              file=sys.stderr)
+        print(f"bench.py: the layer runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); it is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch
