@@ -43,6 +43,10 @@ __device__ __forceinline__ Cand wave_best(Cand c) {
     return c;
 }
 
+// JT: experts per lane the loops are unrolled for (a power of two with
+// 64*JT >= E), so a token of E experts does E/64 lanes' worth of work, not
+// the 1024-expert maximum's.
+template <int JT>
 __global__ void __launch_bounds__(kRouteWaves* kWave)
 route_topk_kernel(RouteArgs a) {
     __shared__ float keys_lds[kRouteWaves][kRouteMaxExperts];
@@ -51,41 +55,44 @@ route_topk_kernel(RouteArgs a) {
     const int t = blockIdx.x * kRouteWaves + w;
     if (t >= a.T) return;                       // whole wave leaves; no block barriers below
     const int E = a.E;
-    const int J = (E + kWave - 1) / kWave;
+    static_assert(JT <= kRouteMaxPerLane && JT <= 32, "experts per lane");
     const float* lg = a.logits + (int64_t)t * E;
 
-    float key[kRouteMaxPerLane];
-    double sc[kRouteMaxPerLane];
+    float key[JT];
+    double sc[JT];
     // 1. scores in double
     float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPerLane; ++j) {
+    for (int j = 0; j < JT; ++j) {
         const int e = lane + j * kWave;
-        key[j] = (j < J && e < E) ? lg[e] : -INFINITY;
+        key[j] = (e < E) ? lg[e] : -INFINITY;
         m = fmaxf(m, key[j]);
     }
     if (a.score == 0) {
         m = wave_max_f32(m);
         double z = 0.0;
 #pragma unroll
-        for (int j = 0; j < kRouteMaxPerLane; ++j) {
+        for (int j = 0; j < JT; ++j) {
             const int e = lane + j * kWave;
-            sc[j] = (j < J && e < E) ? exp((double)key[j] - (double)m) : 0.0;
+            sc[j] = (e < E) ? exp((double)key[j] - (double)m) : 0.0;
             z += sc[j];
         }
         z = wave_sum_f64(z);
 #pragma unroll
-        for (int j = 0; j < kRouteMaxPerLane; ++j) sc[j] = sc[j] / z;
+        for (int j = 0; j < JT; ++j) sc[j] = sc[j] / z;
     } else {
 #pragma unroll
-        for (int j = 0; j < kRouteMaxPerLane; ++j) sc[j] = 1.0 / (1.0 + exp(-(double)key[j]));
+        for (int j = 0; j < JT; ++j) {
+            const int e = lane + j * kWave;
+            sc[j] = (e < E) ? 1.0 / (1.0 + exp(-(double)key[j])) : 0.0;
+        }
     }
     // 2. selection keys in fp32
     uint32_t allowed = 0;
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPerLane; ++j) {
+    for (int j = 0; j < JT; ++j) {
         const int e = lane + j * kWave;
-        if (j < J && e < E) {
+        if (e < E) {
             const float s32 = (float)sc[j];
             key[j] = a.bias ? s32 + a.bias[e] : s32;
             allowed |= 1u << j;
@@ -95,9 +102,9 @@ route_topk_kernel(RouteArgs a) {
     if (a.n_group > 1) {
         const int gsize = E / a.n_group;
 #pragma unroll
-        for (int j = 0; j < kRouteMaxPerLane; ++j) {
+        for (int j = 0; j < JT; ++j) {
             const int e = lane + j * kWave;
-            if (j < J && e < E) keys_lds[w][e] = key[j];
+            if (e < E) keys_lds[w][e] = key[j];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -126,9 +133,9 @@ route_topk_kernel(RouteArgs a) {
         const uint64_t kept = ballot(keep);
         uint32_t al = 0;
 #pragma unroll
-        for (int j = 0; j < kRouteMaxPerLane; ++j) {
+        for (int j = 0; j < JT; ++j) {
             const int e = lane + j * kWave;
-            if (j < J && e < E && ((kept >> (e / gsize)) & 1ull)) al |= 1u << j;
+            if (e < E && ((kept >> (e / gsize)) & 1ull)) al |= 1u << j;
         }
         allowed = al;
     }
@@ -138,7 +145,7 @@ route_topk_kernel(RouteArgs a) {
     for (int k = 0; k < a.K; ++k) {
         Cand c{-INFINITY, INT32_MAX, 0.0};
 #pragma unroll
-        for (int j = 0; j < kRouteMaxPerLane; ++j) {
+        for (int j = 0; j < JT; ++j) {
             if ((allowed >> j) & 1u) {
                 const Cand d{key[j], lane + j * kWave, sc[j]};
                 if (better(d, c)) c = d;
@@ -167,7 +174,14 @@ route_topk_kernel(RouteArgs a) {
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
     const int blocks = (a.T + kRouteWaves - 1) / kRouteWaves;
-    hipLaunchKernelGGL(route_topk_kernel, dim3(blocks), dim3(kRouteWaves * kWave), 0, stream, a);
+    const int J = (a.E + kWave - 1) / kWave;
+    const dim3 g(blocks), b(kRouteWaves * kWave);
+    if (J <= 1) hipLaunchKernelGGL(route_topk_kernel<1>, g, b, 0, stream, a);
+    else if (J <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, g, b, 0, stream, a);
+    else if (J <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, g, b, 0, stream, a);
+    else if (J <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, g, b, 0, stream, a);
+    else if (J <= kRouteMaxPerLane) hipLaunchKernelGGL(route_topk_kernel<kRouteMaxPerLane>, g, b, 0, stream, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
