@@ -243,3 +243,34 @@ def test_backward_validation(lib):
     assert lib.moe_route_backward(ctypes.byref(r), P(8), P(8), P(8), None, None) == moe.MOE_ERR_INVALID_ARG
     r.score = 7
     assert lib.moe_route_backward(ctypes.byref(r), P(8), P(8), P(8), P(8), None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_product_path_fails_loudly_without_the_library(tmp_path):
+    # no fallback: with the library missing the binding raises, and it never
+    # pulls in the CPU oracle
+    import subprocess
+    import sys
+    code = ("import sys\n"
+            "import routing_align_sort_amd as moe\n"
+            "try:\n"
+            "    moe.moe_align_sort_capacity(4, 2, 8, 16)\n"
+            "    print('no error')\n"
+            "except ImportError as e:\n"
+            "    print('raised:', e)\n"
+            "print('oracle imported' if 'oracle' in sys.modules else 'oracle not imported')\n")
+    env = dict(os.environ, MOE_LIB_PATH=str(tmp_path / "missing.so"))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, cwd=ROOT,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "missing.so" in r.stdout, r.stdout
+    assert "oracle not imported" in r.stdout
+
+
+def test_product_sources_do_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "routing_align_sort_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
+                assert "moe_oracle" not in src, f
