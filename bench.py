@@ -530,44 +530,46 @@ def permute_path(dev):
 
 
 def backward_step(dev, steps=10, warmup=3):
-    """The training backward of the headline layer (prefill bf16, 2048 tokens
-    x 32 experts, B 64, canonical weights): dx, dW13, dW2, the combine weights'
-    and the logits' gradients, after one forward.  Wall clock of back-to-back
-    backward calls, their useful FLOPs (gate/up recomputed 4SHI, data
-    gradients 2SHI + 4SHI, weight gradients 2SHI + 4SHI: 16SHI per step) and
-    the event-timed share of each GEMM."""
+    """The training step of the headline layer (prefill bf16, 2048 tokens x 32
+    experts, B 64, canonical weights).  The training forward keeps the slot
+    rows and the fp32 gate/up values; the backward reads them and computes dx,
+    dW13, dW2, the combine weights' and the logits' gradients.  Wall clock of
+    back-to-back calls of each; the backward's useful FLOPs are data
+    gradients 2SHI + 4SHI and weight gradients 2SHI + 4SHI (12SHI).  Also the
+    backward that recomputes gate/up itself (16SHI with the recompute)."""
     import torch
 
     import moe_synth as ms
     import routing_align_sort_amd as moe
     cfg = ms.CONFIGS["prefill_bf16"]
     L = ms.make_layer(cfg, device=dev)
-    # a training forward keeps the slot rows the backward reads (no top-1 fusion)
     layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=1, B=cfg["B"], score="softmax", renormalize=False,
-                         top1=False)
+                         train=True)
     x, logits = L["x"], L["logits"]
-    layer.forward(x, logits)
     d_out = torch.randn((cfg["T"], cfg["H"]), dtype=torch.float32, device=dev)
     ws = torch.empty(moe.moe_ffn_backward_workspace_bytes(cfg["T"], 1, cfg["E"], cfg["H"], cfg["I"], cfg["B"]),
                      dtype=torch.uint8, device=dev)
-    for _ in range(warmup):
-        layer.backward(x, logits, d_out, workspace=ws)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        layer.backward(x, logits, d_out, workspace=ws)
-    torch.cuda.synchronize()
-    us = (time.perf_counter() - t0) / steps * 1e6
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e6
+
+    fwd = timed(lambda: layer.forward(x, logits))
+    us = timed(lambda: layer.backward(x, logits, d_out, workspace=ws))
+    us_re = timed(lambda: layer.backward(x, logits, d_out, workspace=ws, recompute=True))
     S = int((layer.topk_ids >= 0).sum().item())
-    flops = 16 * S * cfg["H"] * cfg["I"]
-    res = {"workload": describe("prefill_bf16", cfg, cfg["B"]) + ", backward", "us_per_step": round(us, 1),
-           "forward_us_per_step": None, "tflops": round(flops / (us * 1e-6) / 1e12, 1),
-           "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        layer.forward(x, logits)
-    torch.cuda.synchronize()
-    res["forward_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 1)
+    shi = S * cfg["H"] * cfg["I"]
+    res = {"workload": describe("prefill_bf16", cfg, cfg["B"]) + ", training backward",
+           "us_per_step": round(us, 1), "forward_us_per_step": round(fwd, 1),
+           "tflops": round(12 * shi / (us * 1e-6) / 1e12, 1),
+           "mfma_frac": round(12 * shi / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+           "us_per_step_recomputing_gate_up": round(us_re, 1)}
     del layer, L, ws
     torch.cuda.empty_cache()
     return res

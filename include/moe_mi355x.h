@@ -20,7 +20,8 @@
  *   moe_unpermute_combine  y_perm, row_of_slot, topk weights -> out [T,H]
  *
  * Training adds the gradients: moe_ffn_backward (the layer: dx, dw13, dw2,
- * d_topk_weights), moe_route_backward (d_logits), and for the permuted path
+ * d_topk_weights; after moe_grouped_ffn_train, which keeps the gate and up
+ * values for it), moe_route_backward (d_logits), and for the permuted path
  * moe_unpermute_combine_backward (d_y_perm, d_topk_weights) and
  * moe_unpermute_combine with unit weights (the permute's gradient).
  *
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
     MOE_OK = 0,
@@ -411,10 +412,20 @@ moe_status_t moe_unpermute_combine_backward(int32_t T, int32_t K, int32_t E, int
  * topk_weights: the forward's inputs; sorted_token_ids, expert_ids,
  * num_tokens_post_padded and expert_offsets [E+1]: moe_align_sort's outputs
  * (expert_offsets required here); y_slots: the forward's moe_grouped_ffn
- * output; d_out device fp32 [T,H].  Outputs (device fp32, overwritten): dx
+ * output; gate_up: the training forward's gate and up values
+ * (moe_grouped_ffn_train), or NULL to recompute them from x and w13 (the
+ * same products, the backward's own GEMM); d_out device fp32 [T,H].  Outputs (device fp32, overwritten): dx
  * [T,H], dw13 [E,2I,H], dw2 [E,H,I], d_topk_weights [T,K].  GEMM operands are
  * bf16 (dy and [d_g d_u] rounded once), accumulation fp32.  workspace: at
  * least moe_ffn_backward_workspace_bytes(p) bytes, 256-byte aligned.
+ *
+ * moe_grouped_ffn_train: moe_grouped_ffn (bf16 weights and activations,
+ * MOE_ROWS_BY_TOKEN, MOE_SCHEDULE_TWO_LAUNCH; else MOE_ERR_UNSUPPORTED) that
+ * also writes what the backward reads of the forward: for every sorted row r
+ * below num_tokens_post_padded, gate_up[r, j] = g and gate_up[r, I + j] = u,
+ * the fp32 products x·w13[e] before the SwiGLU (gate_up device fp32 [C,2I],
+ * C = moe_align_sort_capacity; rows from P on are not written).  y_slots as
+ * for moe_grouped_ffn; workspace moe_grouped_ffn_workspace_bytes(p).
  *
  * moe_route_backward: d_logits [T,E] (device fp32) for d_topk_weights over
  * the routed columns (an appended shared column has no gradient):
@@ -429,9 +440,14 @@ moe_status_t moe_ffn_backward(const moe_ffn_params_t *p, const void *x, const vo
                               const int32_t *topk_ids, const float *topk_weights,
                               const int32_t *sorted_token_ids, const int32_t *expert_ids,
                               const int32_t *num_tokens_post_padded, const int32_t *expert_offsets,
-                              const float *y_slots, const float *d_out, float *dx, float *dw13,
-                              float *dw2, float *d_topk_weights, void *workspace,
-                              size_t workspace_bytes, void *stream);
+                              const float *y_slots, const float *gate_up, const float *d_out,
+                              float *dx, float *dw13, float *dw2, float *d_topk_weights,
+                              void *workspace, size_t workspace_bytes, void *stream);
+moe_status_t moe_grouped_ffn_train(const moe_ffn_params_t *p, const void *x, const void *w13,
+                                   const void *w2, const int32_t *sorted_token_ids,
+                                   const int32_t *expert_ids, const int32_t *num_tokens_post_padded,
+                                   float *y_slots, float *gate_up, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 moe_status_t moe_route_backward(const moe_route_params_t *p, const float *logits,
                                 const int32_t *topk_ids, const float *d_topk_weights, float *d_logits,
                                 void *stream);

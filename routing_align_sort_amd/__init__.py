@@ -48,7 +48,8 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
             "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_grouped_ffn_top1", "moe_prepack_weights",
             "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine",
-            "moe_unpermute_combine_backward", "moe_ffn_backward_workspace_bytes", "moe_ffn_backward", "moe_route_backward")
+            "moe_unpermute_combine_backward", "moe_ffn_backward_workspace_bytes", "moe_ffn_backward",
+            "moe_grouped_ffn_train", "moe_route_backward")
 
 
 def load_library(path: str = LIB_PATH):
@@ -95,7 +96,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_unpermute_combine_backward.restype = i32
     lib.moe_ffn_backward_workspace_bytes.argtypes = [ctypes.POINTER(_FfnParams)]
     lib.moe_ffn_backward_workspace_bytes.restype = i64
-    lib.moe_ffn_backward.argtypes = [ctypes.POINTER(_FfnParams)] + [P] * 16 + [sz, P]
+    lib.moe_ffn_backward.argtypes = [ctypes.POINTER(_FfnParams)] + [P] * 17 + [sz, P]
+    lib.moe_grouped_ffn_train.argtypes = [ctypes.POINTER(_FfnParams)] + [P] * 8 + [P, sz, P]
+    lib.moe_grouped_ffn_train.restype = i32
     lib.moe_ffn_backward.restype = i32
     lib.moe_route_backward.argtypes = [ctypes.POINTER(_RouteParams), P, P, P, P, P]
     lib.moe_route_backward.restype = i32
@@ -486,11 +489,45 @@ def moe_ffn_backward_workspace_bytes(T, K, E, H, I, B) -> int:
     return c
 
 
+def moe_grouped_ffn_train(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, *, K, B,
+                          y_slots=None, gate_up=None, workspace=None, stream=None, packed=False):
+    """moe_grouped_ffn (bf16 weights, canonical or packed) that also keeps the
+    fp32 gate and up values of every sorted row for the backward: returns
+    (y_slots [T*K,H], gate_up [C,2I])."""
+    lib = load_library()
+    T, H = x.shape
+    E, I, H2 = weight_dims(w13)
+    if H2 != H or tuple(w2.shape) != (E, H, I):
+        raise ValueError("weight shapes do not match x")
+    for t, n in ((x, "x"), (w13, "w13"), (w2, "w2")):
+        _need(t, torch.bfloat16, n)
+    for t, n in ((sorted_token_ids, "sorted_token_ids"), (expert_ids, "expert_ids"),
+                 (num_tokens_post_padded, "num_tokens_post_padded")):
+        _need(t, torch.int32, n)
+    C = moe_align_sort_capacity(T, K, E, B)
+    if y_slots is None:
+        y_slots = torch.empty((T * K, H), dtype=torch.float32, device=x.device)
+    _need(y_slots, torch.float32, "y_slots", T * K * H)
+    if gate_up is None:
+        gate_up = torch.empty((C, 2 * I), dtype=torch.float32, device=x.device)
+    _need(gate_up, torch.float32, "gate_up", C * 2 * I)
+    p = _ffn_params(T, K, E, H, I, B, torch.bfloat16, torch.bfloat16, packed)
+    need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, torch.bfloat16, torch.bfloat16)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("moe_grouped_ffn_train", lib.moe_grouped_ffn_train(
+        ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w2), _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(y_slots), _ptr(gate_up), _ptr(workspace), ws_bytes, _stream(stream)))
+    return y_slots, gate_up
+
+
 def moe_ffn_backward(x, w13, w2, topk_ids, topk_weights, sorted_token_ids, expert_ids,
-                     num_tokens_post_padded, expert_offsets, y_slots, d_out, *, B, workspace=None,
-                     stream=None):
+                     num_tokens_post_padded, expert_offsets, y_slots, d_out, *, B, gate_up=None,
+                     workspace=None, stream=None):
     """Gradients of moe_combine(moe_grouped_ffn(...)) for the upstream d_out [T,H]
-    (bf16 weights, canonical layout): returns (dx, dw13, dw2, d_topk_weights), fp32."""
+    (bf16 weights, canonical layout): returns (dx, dw13, dw2, d_topk_weights), fp32.
+    gate_up: the training forward's gate and up values (else recomputed)."""
     lib = load_library()
     T, H = x.shape
     E, I2, _ = w13.shape
@@ -503,6 +540,8 @@ def moe_ffn_backward(x, w13, w2, topk_ids, topk_weights, sorted_token_ids, exper
                      (expert_offsets, "expert_offsets", torch.int32), (y_slots, "y_slots", torch.float32),
                      (d_out, "d_out", torch.float32)):
         _need(t, dt, n)
+    if gate_up is not None:
+        _need(gate_up, torch.float32, "gate_up", sorted_token_ids.numel() * I2)
     dev = x.device
     dx = torch.empty((T, H), dtype=torch.float32, device=dev)
     dw13 = torch.empty((E, I2, H), dtype=torch.float32, device=dev)
@@ -516,8 +555,8 @@ def moe_ffn_backward(x, w13, w2, topk_ids, topk_weights, sorted_token_ids, exper
     _check("moe_ffn_backward", lib.moe_ffn_backward(
         ctypes.byref(p), _ptr(x), _ptr(w13), _ptr(w2), _ptr(topk_ids), _ptr(topk_weights),
         _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded), _ptr(expert_offsets),
-        _ptr(y_slots), _ptr(d_out), _ptr(dx), _ptr(dw13), _ptr(dw2), _ptr(dwk), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        _ptr(y_slots), _ptr(gate_up), _ptr(d_out), _ptr(dx), _ptr(dw13), _ptr(dw2), _ptr(dwk), _ptr(workspace),
+        ws_bytes, _stream(stream)))
     return dx, dw13, dw2, dwk
 
 
@@ -552,12 +591,14 @@ class MoELayer:
     top1: with one slot per token (K 1, no shared expert, rows by token, the
     two-launch schedule, not fp32) "auto" runs the FFN and the combine as one
     call (moe_grouped_ffn_top1; the same output bits); False keeps them apart.
+    train: the forward keeps the gate/up values (moe_grouped_ffn_train) and the
+    backward reads them instead of recomputing.
     """
 
     def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
                  w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None,
-                 rows="by_token", schedule="two_launch", top1="auto"):
+                 rows="by_token", schedule="two_launch", top1="auto", train=False):
         dev = w13.device
         if packed is None:
             packed = w13.dtype != torch.float32
@@ -611,8 +652,16 @@ class MoELayer:
             raise ValueError("top1 must be 'auto', True or False")
         if top1 is True and not eligible:
             raise ValueError("top1 needs K 1 without a shared expert, rows by token, two launches, not fp32")
-        self.top1 = eligible and top1 is not False
+        self.top1 = eligible and top1 is not False and not train
         self._y_current = False     # y_slots holds the last forward's rows (the backward reads them)
+        # train: the forward also keeps the gate/up values, and the backward reads them
+        self.train = bool(train)
+        self.gate_up = None
+        if self.train:
+            if w13.dtype != torch.bfloat16 or self.rows_sorted or self.fused:
+                raise ValueError("train needs bf16 weights, rows by token and two launches")
+            self.gate_up = torch.empty((C, 2 * I), dtype=torch.float32, device=dev)
+        self._gu_current = False
 
     def route(self, logits, bias=None):
         return moe_route_topk(logits, self.K, bias=bias, topk_ids=self.topk_ids,
@@ -629,6 +678,7 @@ class MoELayer:
 
     def ffn(self, x, stage_events=None):
         self._y_current = True
+        self._gu_current = False
         if self.rows_sorted:
             return moe_grouped_ffn(self.x_perm, self.w13, self.w2, self.sorted, self.expert_ids,
                                    self.ntpp, K=self.KO, B=self.B, w13_scale=self.w13_scale,
@@ -653,23 +703,34 @@ class MoELayer:
         return moe_combine(self.y_slots, self.topk_weights, self.topk_ids, self.E_slabs,
                            out_dtype=self.out_dtype, out=self.out)
 
+    def ffn_train(self, x):
+        """The training forward's FFN: slot rows plus the gate/up values the backward reads."""
+        self._y_current = True
+        self._gu_current = True
+        return moe_grouped_ffn_train(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp, K=self.KO,
+                                     B=self.B, y_slots=self.y_slots, gate_up=self.gate_up,
+                                     workspace=self.ws_ffn, packed=self.packed)
+
     def ffn_top1(self, x):
         """The FFN and the combine of a top-1 layer in one call (into self.out)."""
         self._y_current = False
+        self._gu_current = False
         return moe_grouped_ffn_top1(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
                                     self.topk_ids, self.topk_weights, B=self.B, w13_scale=self.w13_scale,
                                     w2_scale=self.w2_scale, out_dtype=self.out_dtype, out=self.out,
                                     workspace=self.ws_ffn, packed=self.packed)
 
-    def backward(self, x, logits, d_out, workspace=None):
+    def backward(self, x, logits, d_out, workspace=None, recompute=False):
         """Gradients after forward(x, logits): (dx, dw13, dw2, d_logits), fp32.
         The backward reads the forward's slot rows; after a top-1 forward,
-        which does not write them, they are recomputed first."""
+        which does not write them, they are recomputed first.  After a training
+        forward it reads the kept gate/up values unless recompute is set."""
         if not self._y_current:
             self.ffn(x)
         dx, dw13, dw2, dwk = moe_ffn_backward(
             x, self.w13_canonical, self.w2_canonical, self.topk_ids, self.topk_weights, self.sorted,
-            self.expert_ids, self.ntpp, self.offsets, self.y_slots, d_out, B=self.B, workspace=workspace)
+            self.expert_ids, self.ntpp, self.offsets, self.y_slots, d_out, B=self.B,
+            gate_up=self.gate_up if (self._gu_current and not recompute) else None, workspace=workspace)
         d_logits = moe_route_backward(logits, self.topk_ids, dwk, self.K, score=self.route_kw["score"],
                                       renormalize=self.route_kw["renormalize"],
                                       routed_scaling=self.route_kw["routed_scaling"],
@@ -683,7 +744,10 @@ class MoELayer:
             self.permute(x)
         if self.top1:
             return self.ffn_top1(x)
-        self.ffn(x)
+        if self.train:
+            self.ffn_train(x)
+        else:
+            self.ffn(x)
         return self.combine()
 
 

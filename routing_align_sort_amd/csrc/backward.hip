@@ -273,19 +273,24 @@ hipError_t launch_ffn_backward(const BwdArgs& a, void* ws, hipStream_t st) {
     MOE_TRY(hipGetLastError());
     MOE_TRY(launch_permute_rows(w.dy_slots, H * 2, 1, (int)E, S, C, a.sorted, a.post_padded, a.ids, nullptr,
                                 w.dy_perm, nullptr, w.row_of_slot2, st));
-    // 2. gate/up recomputed (weights as stored: K-contiguous rows)
+    // 2. the gate/up values: the training forward's, or recomputed (weights as
+    //    stored: K-contiguous rows)
     NtGemmArgs g{};
     g.expert_ids = a.expert_ids; g.post_padded = a.post_padded; g.offsets = a.offsets; g.by_block = 1;
-    g.a = w.x_perm; g.lda = H; g.b = a.w13; g.ldb = H; g.b_group = 2 * I * H; g.c = w.gu; g.ldc = 2 * I;
-    g.M = a.B; g.N = (int)(2 * I); g.K = (int)H;
-    MOE_TRY(launch_nt_gemm(g, a.B, nblk, st));
+    const float* gu = a.gate_up ? a.gate_up : w.gu;
+    if (!a.gate_up) {
+        g.a = w.x_perm; g.lda = H; g.b = a.w13; g.ldb = H; g.b_group = 2 * I * H; g.c = w.gu; g.ldc = 2 * I;
+        g.M = a.B; g.N = (int)(2 * I); g.K = (int)H;
+        MOE_TRY(launch_nt_gemm(g, a.B, nblk, st));
+    }
+    g.M = a.B;
     // 3. d_a = dy W2[e] (W2[e] is [H][I]: the NN form), SwiGLU backward, dx rows = [d_g d_u] W13[e]
     g.a = w.dy_perm; g.lda = H; g.b = a.w2; g.ldb = I; g.b_group = H * I; g.c = w.d_a; g.ldc = I;
     g.N = (int)I; g.K = (int)H;
     MOE_TRY(launch_nn_gemm(g, a.B, nblk, st));
     if (C > 0)
         hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)C), dim3(kBwdThreads), 0, st, (int)I, a.post_padded,
-                           (const float*)w.gu, (const float*)w.d_a, w.a_bf, w.dgu);
+                           gu, (const float*)w.d_a, w.a_bf, w.dgu);
     MOE_TRY(hipGetLastError());
     g.a = w.dgu; g.lda = 2 * I; g.b = a.w13; g.ldb = H; g.b_group = 2 * I * H; g.c = w.dxs; g.ldc = H;
     g.N = (int)H; g.K = (int)(2 * I);

@@ -164,7 +164,8 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
                                 const void* w13_scale, const void* w2, const void* w2_scale,
                                 const int32_t* sorted_token_ids, const int32_t* expert_ids,
                                 const int32_t* num_tokens_post_padded, float* y_slots, const Top1Out& top1,
-                                void* workspace, size_t workspace_bytes, void* stream, hipEvent_t const* ev) {
+                                float* save_gu, void* workspace, size_t workspace_bytes, void* stream,
+                                hipEvent_t const* ev) {
     const moe_status_t st = ffn_check(p);
     if (st != MOE_OK) return st;
     const int64_t S = (int64_t)p->T * p->K;
@@ -188,6 +189,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     a.rows_sorted = p->row_layout == MOE_ROWS_SORTED;
     a.fused = p->schedule == MOE_SCHEDULE_FUSED;
     a.top1_w = top1.w; a.top1_ids = top1.ids; a.top1_out = top1.out; a.top1_bf16 = top1.bf16;
+    a.save_gu = save_gu;
     hipError_t e;
     if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream), ev);
     else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream), ev);
@@ -202,7 +204,23 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const voi
                              const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
                              size_t workspace_bytes, void* stream) {
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
-                       num_tokens_post_padded, y_slots, Top1Out{}, workspace, workspace_bytes, stream, nullptr);
+                       num_tokens_post_padded, y_slots, Top1Out{}, nullptr, workspace, workspace_bytes, stream,
+                       nullptr);
+}
+
+moe_status_t moe_grouped_ffn_train(const moe_ffn_params_t* p, const void* x, const void* w13, const void* w2,
+                                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                   const int32_t* num_tokens_post_padded, float* y_slots, float* gate_up,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    const moe_status_t st = ffn_check(p);
+    if (st != MOE_OK) return st;
+    if (p->w_dtype != MOE_BF16 || p->x_dtype != MOE_BF16 || p->row_layout != MOE_ROWS_BY_TOKEN ||
+        p->schedule != MOE_SCHEDULE_TWO_LAUNCH)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)p->T * p->K == 0) return MOE_OK;
+    if (!gate_up) return MOE_ERR_INVALID_ARG;
+    return grouped_ffn(p, x, w13, nullptr, w2, nullptr, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                       y_slots, Top1Out{}, gate_up, workspace, workspace_bytes, stream, nullptr);
 }
 
 moe_status_t moe_grouped_ffn_top1(const moe_ffn_params_t* p, const void* x, const void* w13,
@@ -221,7 +239,7 @@ moe_status_t moe_grouped_ffn_top1(const moe_ffn_params_t* p, const void* x, cons
     if (!topk_ids || !topk_weights || !out) return MOE_ERR_INVALID_ARG;
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, nullptr, Top1Out{topk_ids, topk_weights, out, out_dtype == MOE_BF16},
-                       workspace, workspace_bytes, stream, nullptr);
+                       nullptr, workspace, workspace_bytes, stream, nullptr);
 }
 
 moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, const void* w13,
@@ -234,7 +252,7 @@ moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, 
     for (int i = 0; i < 5; ++i)
         if (!events[i]) return MOE_ERR_INVALID_ARG;
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
-                       num_tokens_post_padded, y_slots, Top1Out{}, workspace, workspace_bytes, stream,
+                       num_tokens_post_padded, y_slots, Top1Out{}, nullptr, workspace, workspace_bytes, stream,
                        reinterpret_cast<hipEvent_t const*>(events));
 }
 
@@ -263,7 +281,8 @@ int64_t moe_ffn_backward_workspace_bytes(const moe_ffn_params_t* p) {
 moe_status_t moe_ffn_backward(const moe_ffn_params_t* p, const void* x, const void* w13, const void* w2,
                               const int32_t* topk_ids, const float* topk_weights, const int32_t* sorted_token_ids,
                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
-                              const int32_t* expert_offsets, const float* y_slots, const float* d_out, float* dx,
+                              const int32_t* expert_offsets, const float* y_slots, const float* gate_up,
+                              const float* d_out, float* dx,
                               float* dw13, float* dw2, float* d_topk_weights, void* workspace,
                               size_t workspace_bytes, void* stream) {
     const moe_status_t st = bwd_check(p);
@@ -276,11 +295,12 @@ moe_status_t moe_ffn_backward(const moe_ffn_params_t* p, const void* x, const vo
     const int64_t C = capacity(S, p->E, p->B);
     const int64_t need = ffn_backward_workspace_bytes(p->T, p->K, p->E, p->H, p->I, C);
     if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
-    BwdArgs a;
+    BwdArgs a{};
     a.T = p->T; a.K = p->K; a.E = p->E; a.H = p->H; a.I = p->I; a.B = p->B; a.S = S; a.C = C;
     a.x = (const uint16_t*)x; a.w13 = (const uint16_t*)w13; a.w2 = (const uint16_t*)w2;
     a.ids = topk_ids; a.w = topk_weights; a.sorted = sorted_token_ids; a.expert_ids = expert_ids;
     a.post_padded = num_tokens_post_padded; a.offsets = expert_offsets; a.y_slots = y_slots; a.d_out = d_out;
+    a.gate_up = gate_up;
     a.dx = dx; a.dw13 = dw13; a.dw2 = dw2; a.d_w = d_topk_weights;
     return from_hip(launch_ffn_backward(a, workspace, as_stream(stream)));
 }

@@ -565,6 +565,11 @@ __device__ __forceinline__ void stage1_tile(const FfnArgs& a, uint16_t* __restri
                 g = g * s * sg;
                 u = u * s * su;
             }
+            if (a.save_gu && m < BM) {
+                float* gr = a.save_gu + ((int64_t)mb * BM + m) * 2 * I;
+                gr[col] = g;
+                gr[I + col] = u;
+            }
             const float hval = silu_f32(g) * u;
             if constexpr (F::kQuantA) {
                 // row max over this wave's 32 columns, then one atomic per row

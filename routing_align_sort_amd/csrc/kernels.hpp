@@ -61,6 +61,10 @@ struct FfnArgs {
     const int32_t* top1_ids;
     void* top1_out;
     int top1_bf16;
+    // Training forward: the gate and up values (fp32, after any scales) of
+    // sorted row r are written to save_gu[r*2I + j] and [r*2I + I + j] for
+    // rows below num_tokens_post_padded, for the backward; null otherwise.
+    float* save_gu;
 };
 // Largest activation operand (bytes of x, or of the intermediate, as one
 // GEMM reads it) of the matrix-core kernels: they address it with 32-bit
@@ -123,6 +127,7 @@ struct BwdArgs {
     const int32_t* post_padded;  // [1]
     const int32_t* offsets;      // [E+1]
     const float* y_slots;        // [S,H] the forward's
+    const float* gate_up;        // [C,2I] the training forward's gate and up values, or null (recomputed)
     const float* d_out;          // [T,H]
     float* dx;                   // [T,H]
     float* dw13;                 // [E,2I,H]

@@ -30,14 +30,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 5
+    assert moe.abi_version() == 6
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -234,11 +234,19 @@ def test_backward_validation(lib):
         p = moe._FfnParams(256, 2, 8, 512, 256, 64, moe.MOE_BF16, moe.MOE_BF16, 0, 0, 0)
         setattr(p, field, value)
         assert lib.moe_ffn_backward_workspace_bytes(ctypes.byref(p)) == -1, field
-    args = [P(8)] * 16                                       # 15 arrays and the workspace
-    args[9] = None                                           # expert_offsets is required here
+    args = [P(8)] * 17                                       # 16 arrays and the workspace
+    args[8] = None                                           # expert_offsets is required here
     assert lib.moe_ffn_backward(ctypes.byref(ok), *args, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
-    args[9] = P(8)
+    args[8] = P(8)
+    args[10] = None                                          # gate_up may be NULL (recomputed)
     assert lib.moe_ffn_backward(ctypes.byref(ok), *args, 16, None) == moe.MOE_ERR_WORKSPACE
+    # the training forward: bf16 only, by token, two launches; gate_up required
+    tr = lib.moe_grouped_ffn_train
+    targs = [P(8)] * 8
+    assert tr(ctypes.byref(ok), *targs, P(8), 0, None) == moe.MOE_ERR_WORKSPACE
+    assert tr(ctypes.byref(ok), *targs[:7], None, P(8), 0, None) == moe.MOE_ERR_INVALID_ARG
+    f8 = moe._FfnParams(256, 2, 8, 512, 256, 64, moe.MOE_FP8_E4M3, moe.MOE_BF16, 0, 0, 0)
+    assert tr(ctypes.byref(f8), *targs, P(8), 0, None) == moe.MOE_ERR_UNSUPPORTED
     r = moe._RouteParams(4, 8, 2, 0, 1, 1, 1, 1.0, 0)
     assert lib.moe_route_backward(ctypes.byref(r), P(8), P(8), P(8), None, None) == moe.MOE_ERR_INVALID_ARG
     r.score = 7

@@ -17,11 +17,11 @@ from gpu_helpers import device, host_bits, rel_err, say
 pytestmark = pytest.mark.gpu
 
 
-def run(cfg, L, B, seed=3):
+def run(cfg, L, B, seed=3, train=False):
     dev = device()
     layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"],
                          n_group=cfg["n_group"], topk_group=cfg["topk_group"], renormalize=cfg["renormalize"],
-                         shared=bool(cfg.get("shared")), x_dtype=L["x"].dtype)
+                         shared=bool(cfg.get("shared")), x_dtype=L["x"].dtype, train=train)
     layer.forward(L["x"], L["logits"], L["bias"])
     d_out = torch.tensor(np.random.default_rng(seed).standard_normal((cfg["T"], cfg["H"])).astype(np.float32),
                          device=dev)
@@ -30,8 +30,8 @@ def run(cfg, L, B, seed=3):
     return layer, d_out, dx, dw13, dw2, d_logits, dwk
 
 
-def check_all(cfg, L, B, label):
-    layer, d_out, dx, dw13, dw2, d_logits, dwk = run(cfg, L, B)
+def check_all(cfg, L, B, label, train=False):
+    layer, d_out, dx, dw13, dw2, d_logits, dwk = run(cfg, L, B, train=train)
     ids = layer.topk_ids.cpu().numpy()
     w = layer.topk_weights.cpu().numpy()
     y = layer.y_slots.cpu().numpy()
@@ -49,12 +49,55 @@ def check_all(cfg, L, B, label):
     assert errs["d_w"] <= 1e-5 and errs["d_logits"] <= 1e-5, errs
 
 
+@pytest.mark.parametrize("train", [False, True])
 @pytest.mark.parametrize("B", [64, 128, 256])
-def test_backward_small_softmax(B):
+def test_backward_small_softmax(B, train):
     dev = device()
     cfg = ms.scaled("tiny_fp32", T=160, H=512, I=256, E=6, K=2, dtype="bf16", B=B)
     L = ms.make_layer(cfg, device=dev)
-    check_all(cfg, L, B, f"backward softmax top-2 B={B}")
+    check_all(cfg, L, B, f"backward softmax top-2 B={B}" + (" (gate/up kept by the forward)" if train else ""),
+              train=train)
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_training_forward_keeps_gate_up(B):
+    # the training forward: same output and slot rows as the plain forward, the
+    # kept gate/up values equal x . w13[e] of every placed row, and the
+    # backward that reads them agrees with the one that recomputes them
+    dev = device()
+    cfg = ms.scaled("tiny_fp32", T=160, H=512, I=256, E=6, K=2, dtype="bf16", B=B)
+    L = ms.make_layer(cfg, device=dev)
+    mk = lambda train: moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"],
+                                    renormalize=cfg["renormalize"], x_dtype=L["x"].dtype, train=train,
+                                    top1=False)
+    a, b = mk(True), mk(False)
+    oa = a.forward(L["x"], L["logits"]).clone()
+    ob = b.forward(L["x"], L["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(a.y_slots, b.y_slots)
+    K, T, I = cfg["K"], cfg["T"], cfg["I"]
+    P = int(a.ntpp.item())
+    srt = a.sorted.cpu().numpy()[:P]
+    rows = np.nonzero(srt < T * K)[0]
+    toks = srt[rows] // K
+    exps = a.expert_ids.cpu().numpy()[rows // B]
+    xh = L["x"].double().cpu().numpy()
+    wh = L["w13"].double().cpu().numpy()
+    ref = np.einsum("rh,rjh->rj", xh[toks], wh[exps])              # [rows, 2I] in float64
+    got = a.gate_up.cpu().numpy()[rows]
+    err = rel_err(got, ref)
+    assert err <= 1e-5, err
+    d_out = torch.tensor(np.random.default_rng(5).standard_normal((T, cfg["H"])).astype(np.float32), device=dev)
+    ga = a.backward(L["x"], L["logits"], d_out)
+    gb = b.backward(L["x"], L["logits"], d_out)
+    torch.cuda.synchronize()
+    names = ("dx", "dw13", "dw2", "d_logits", "d_w")
+    diffs = {n: rel_err(u.cpu().numpy(), v.cpu().numpy()) for n, u, v in zip(names, ga, gb)}
+    say(f"B={B}: kept gate/up within {err:.1e} of x.w13; kept vs recomputed: "
+        + "  ".join(f"{k} {v:.1e}" for k, v in diffs.items()))
+    assert torch.equal(ga[3], gb[3]) and torch.equal(ga[4], gb[4])      # from y_slots only
+    for n in ("dx", "dw13", "dw2"):
+        assert diffs[n] <= 5e-3, (n, diffs[n])
 
 
 def test_backward_small_sigmoid_groups_shared():
