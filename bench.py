@@ -536,7 +536,8 @@ def backward_step(dev, steps=10, warmup=3):
     dW13, dW2, the combine weights' and the logits' gradients.  Wall clock of
     back-to-back calls of each; the backward's useful FLOPs are data
     gradients 2SHI + 4SHI and weight gradients 2SHI + 4SHI (12SHI).  Also the
-    backward that recomputes gate/up itself (16SHI with the recompute)."""
+    backward that recomputes gate/up itself (16SHI with the recompute), and the
+    one that writes the weight gradients in bf16."""
     import torch
 
     import moe_synth as ms
@@ -563,13 +564,16 @@ def backward_step(dev, steps=10, warmup=3):
     fwd = timed(lambda: layer.forward(x, logits))
     us = timed(lambda: layer.backward(x, logits, d_out, workspace=ws))
     us_re = timed(lambda: layer.backward(x, logits, d_out, workspace=ws, recompute=True))
+    layer.grad_dtype = torch.bfloat16
+    us_bf16 = timed(lambda: layer.backward(x, logits, d_out, workspace=ws))
     S = int((layer.topk_ids >= 0).sum().item())
     shi = S * cfg["H"] * cfg["I"]
     res = {"workload": describe("prefill_bf16", cfg, cfg["B"]) + ", training backward",
            "us_per_step": round(us, 1), "forward_us_per_step": round(fwd, 1),
            "tflops": round(12 * shi / (us * 1e-6) / 1e12, 1),
            "mfma_frac": round(12 * shi / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
-           "us_per_step_recomputing_gate_up": round(us_re, 1)}
+           "us_per_step_recomputing_gate_up": round(us_re, 1),
+           "us_per_step_bf16_weight_grads": round(us_bf16, 1)}
     del layer, L, ws
     torch.cuda.empty_cache()
     return res

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
     MOE_OK = 0,
@@ -234,6 +234,7 @@ typedef struct {
     int32_t weight_layout;     /* moe_weight_layout_t of w13 and w2 */
     int32_t row_layout;        /* moe_row_layout_t of x and y_slots */
     int32_t schedule;          /* moe_schedule_t */
+    int32_t grad_dtype;        /* moe_dtype_t of moe_ffn_backward's dw13 and dw2: MOE_F32 (0) or MOE_BF16 */
 } moe_ffn_params_t;
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);
@@ -414,9 +415,12 @@ moe_status_t moe_unpermute_combine_backward(int32_t T, int32_t K, int32_t E, int
  * (expert_offsets required here); y_slots: the forward's moe_grouped_ffn
  * output; gate_up: the training forward's gate and up values
  * (moe_grouped_ffn_train), or NULL to recompute them from x and w13 (the
- * same products, the backward's own GEMM); d_out device fp32 [T,H].  Outputs (device fp32, overwritten): dx
- * [T,H], dw13 [E,2I,H], dw2 [E,H,I], d_topk_weights [T,K].  GEMM operands are
- * bf16 (dy and [d_g d_u] rounded once), accumulation fp32.  workspace: at
+ * same products, the backward's own GEMM); d_out device fp32 [T,H].
+ * Outputs (device, overwritten): dx fp32 [T,H]; dw13 [E,2I,H] and dw2
+ * [E,H,I] in p->grad_dtype (MOE_F32, or MOE_BF16: the fp32 sums rounded once
+ * to nearest even, half the bytes to write; other types MOE_ERR_UNSUPPORTED);
+ * d_topk_weights fp32 [T,K].  GEMM operands are bf16 (dy and [d_g d_u]
+ * rounded once), accumulation fp32.  workspace: at
  * least moe_ffn_backward_workspace_bytes(p) bytes, 256-byte aligned.
  *
  * moe_grouped_ffn_train: moe_grouped_ffn (bf16 weights and activations,
@@ -441,7 +445,7 @@ moe_status_t moe_ffn_backward(const moe_ffn_params_t *p, const void *x, const vo
                               const int32_t *sorted_token_ids, const int32_t *expert_ids,
                               const int32_t *num_tokens_post_padded, const int32_t *expert_offsets,
                               const float *y_slots, const float *gate_up, const float *d_out,
-                              float *dx, float *dw13, float *dw2, float *d_topk_weights,
+                              float *dx, void *dw13, void *dw2, float *d_topk_weights,
                               void *workspace, size_t workspace_bytes, void *stream);
 moe_status_t moe_grouped_ffn_train(const moe_ffn_params_t *p, const void *x, const void *w13,
                                    const void *w2, const int32_t *sorted_token_ids,

@@ -41,7 +41,7 @@ class _FfnParams(ctypes.Structure):
                 ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("B", ctypes.c_int32),
                 ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
                 ("weight_layout", ctypes.c_int32), ("row_layout", ctypes.c_int32),
-                ("schedule", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
@@ -230,11 +230,12 @@ MOE_ROWS_BY_TOKEN, MOE_ROWS_SORTED = 0, 1
 MOE_SCHEDULE_TWO_LAUNCH, MOE_SCHEDULE_FUSED = 0, 1
 
 
-def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False, rows_sorted=False, fused=False):
+def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False, rows_sorted=False, fused=False,
+                grad_dtype=torch.float32):
     return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype],
                       MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_CANONICAL,
                       MOE_ROWS_SORTED if rows_sorted else MOE_ROWS_BY_TOKEN,
-                      MOE_SCHEDULE_FUSED if fused else MOE_SCHEDULE_TWO_LAUNCH)
+                      MOE_SCHEDULE_FUSED if fused else MOE_SCHEDULE_TWO_LAUNCH, _DT[grad_dtype])
 
 
 def moe_prepack_weights(w13, w2, *, stream=None):
@@ -524,9 +525,10 @@ def moe_grouped_ffn_train(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_p
 
 def moe_ffn_backward(x, w13, w2, topk_ids, topk_weights, sorted_token_ids, expert_ids,
                      num_tokens_post_padded, expert_offsets, y_slots, d_out, *, B, gate_up=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, grad_dtype=torch.float32):
     """Gradients of moe_combine(moe_grouped_ffn(...)) for the upstream d_out [T,H]
-    (bf16 weights, canonical layout): returns (dx, dw13, dw2, d_topk_weights), fp32.
+    (bf16 weights, canonical layout): returns (dx, dw13, dw2, d_topk_weights),
+    fp32 except dw13 and dw2 in grad_dtype (fp32 or bf16).
     gate_up: the training forward's gate and up values (else recomputed)."""
     lib = load_library()
     T, H = x.shape
@@ -544,10 +546,12 @@ def moe_ffn_backward(x, w13, w2, topk_ids, topk_weights, sorted_token_ids, exper
         _need(gate_up, torch.float32, "gate_up", sorted_token_ids.numel() * I2)
     dev = x.device
     dx = torch.empty((T, H), dtype=torch.float32, device=dev)
-    dw13 = torch.empty((E, I2, H), dtype=torch.float32, device=dev)
-    dw2 = torch.empty((E, H, I), dtype=torch.float32, device=dev)
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("grad_dtype must be float32 or bfloat16")
+    dw13 = torch.empty((E, I2, H), dtype=grad_dtype, device=dev)
+    dw2 = torch.empty((E, H, I), dtype=grad_dtype, device=dev)
     dwk = torch.empty((T, K), dtype=torch.float32, device=dev)
-    p = _ffn_params(T, K, E, H, I, B, torch.bfloat16, torch.bfloat16)
+    p = _ffn_params(T, K, E, H, I, B, torch.bfloat16, torch.bfloat16, grad_dtype=grad_dtype)
     need = moe_ffn_backward_workspace_bytes(T, K, E, H, I, B)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -592,13 +596,15 @@ class MoELayer:
     two-launch schedule, not fp32) "auto" runs the FFN and the combine as one
     call (moe_grouped_ffn_top1; the same output bits); False keeps them apart.
     train: the forward keeps the gate/up values (moe_grouped_ffn_train) and the
-    backward reads them instead of recomputing.
+    backward reads them instead of recomputing.  grad_dtype: the weight
+    gradients' type (float32, or bfloat16: rounded once, half the bytes).
     """
 
     def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
                  w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None,
-                 rows="by_token", schedule="two_launch", top1="auto", train=False):
+                 rows="by_token", schedule="two_launch", top1="auto", train=False,
+                 grad_dtype=torch.float32):
         dev = w13.device
         if packed is None:
             packed = w13.dtype != torch.float32
@@ -656,6 +662,7 @@ class MoELayer:
         self._y_current = False     # y_slots holds the last forward's rows (the backward reads them)
         # train: the forward also keeps the gate/up values, and the backward reads them
         self.train = bool(train)
+        self.grad_dtype = grad_dtype
         self.gate_up = None
         if self.train:
             if w13.dtype != torch.bfloat16 or self.rows_sorted or self.fused:
@@ -730,7 +737,8 @@ class MoELayer:
         dx, dw13, dw2, dwk = moe_ffn_backward(
             x, self.w13_canonical, self.w2_canonical, self.topk_ids, self.topk_weights, self.sorted,
             self.expert_ids, self.ntpp, self.offsets, self.y_slots, d_out, B=self.B,
-            gate_up=self.gate_up if (self._gu_current and not recompute) else None, workspace=workspace)
+            gate_up=self.gate_up if (self._gu_current and not recompute) else None, workspace=workspace,
+            grad_dtype=self.grad_dtype)
         d_logits = moe_route_backward(logits, self.topk_ids, dwk, self.K, score=self.route_kw["score"],
                                       renormalize=self.route_kw["renormalize"],
                                       routed_scaling=self.route_kw["routed_scaling"],

@@ -301,10 +301,11 @@ hipError_t launch_ffn_backward(const BwdArgs& a, void* ws, hipStream_t st) {
     MOE_TRY(transpose(w.dy_perm, w.dyt, (int)C, (int)H, C, 1, 0, 0, a.post_padded, st));
     MOE_TRY(transpose(w.dgu, w.dgut, (int)C, (int)(2 * I), C, 1, 0, 0, a.post_padded, st));
     g.by_block = 0;
-    g.a = w.dyt; g.lda = C; g.b = w.a_bf; g.ldb = I; g.c = a.dw2; g.ldc = I; g.c_group = H * I;
+    g.c_bf16 = a.dw_bf16;
+    g.a = w.dyt; g.lda = C; g.b = w.a_bf; g.ldb = I; g.c = (float*)a.dw2; g.ldc = I; g.c_group = H * I;
     g.M = (int)H; g.N = (int)I;
     MOE_TRY(launch_nn_gemm(g, 128, E, st));
-    g.a = w.dgut; g.lda = C; g.b = w.x_perm; g.ldb = H; g.c = a.dw13; g.ldc = H; g.c_group = 2 * I * H;
+    g.a = w.dgut; g.lda = C; g.b = w.x_perm; g.ldb = H; g.c = (float*)a.dw13; g.ldc = H; g.c_group = 2 * I * H;
     g.M = (int)(2 * I); g.N = (int)H;
     MOE_TRY(launch_nn_gemm(g, 128, E, st));
     return hipSuccess;

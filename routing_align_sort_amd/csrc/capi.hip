@@ -261,6 +261,7 @@ static moe_status_t bwd_check(const moe_ffn_params_t* p) {
     if (p->T < 0 || p->K < 1 || p->E < 1 || p->H < 1 || p->I < 1 || !align_args_ok(p->T, p->K, p->E, p->B))
         return MOE_ERR_INVALID_ARG;
     if (p->w_dtype != MOE_BF16 || p->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->grad_dtype != MOE_F32 && p->grad_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->weight_layout != MOE_LAYOUT_CANONICAL || p->row_layout != MOE_ROWS_BY_TOKEN ||
         p->schedule != MOE_SCHEDULE_TWO_LAUNCH)
         return MOE_ERR_UNSUPPORTED;
@@ -283,7 +284,7 @@ moe_status_t moe_ffn_backward(const moe_ffn_params_t* p, const void* x, const vo
                               const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                               const int32_t* expert_offsets, const float* y_slots, const float* gate_up,
                               const float* d_out, float* dx,
-                              float* dw13, float* dw2, float* d_topk_weights, void* workspace,
+                              void* dw13, void* dw2, float* d_topk_weights, void* workspace,
                               size_t workspace_bytes, void* stream) {
     const moe_status_t st = bwd_check(p);
     if (st != MOE_OK) return st;
@@ -301,6 +302,7 @@ moe_status_t moe_ffn_backward(const moe_ffn_params_t* p, const void* x, const vo
     a.ids = topk_ids; a.w = topk_weights; a.sorted = sorted_token_ids; a.expert_ids = expert_ids;
     a.post_padded = num_tokens_post_padded; a.offsets = expert_offsets; a.y_slots = y_slots; a.d_out = d_out;
     a.gate_up = gate_up;
+    a.dw_bf16 = p->grad_dtype == MOE_BF16;
     a.dx = dx; a.dw13 = dw13; a.dw2 = dw2; a.d_w = d_topk_weights;
     return from_hip(launch_ffn_backward(a, workspace, as_stream(stream)));
 }

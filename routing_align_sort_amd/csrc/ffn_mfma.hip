@@ -1365,6 +1365,31 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_kernel(NtGemmArgs g) {
     // gradients make these launches bound by their writes).
     if constexpr (sizeof(NnSmem<BM>) >= 4 * BM * 32 * sizeof(float)) {
         __syncthreads();
+        if (g.c_bf16) {
+            // bf16: the workgroup's whole BM x 128 block goes through LDS, so
+            // that a row's 256 bytes leave as 16-byte lanes (whole 128-byte
+            // lines; a wave's 64-byte half rows had written slower than fp32)
+            float* st = reinterpret_cast<float*>(&sm);
+#pragma unroll
+            for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st[(m2 * 32 + acc_row(i, lane)) * kNnCols + w * 32 + r32] = acc[m2][i];
+            __syncthreads();
+            const int c8 = (tid & 15) * 8, r0 = tid >> 4;
+#pragma unroll
+            for (int j = 0; j < BM / 16; ++j) {
+                const int m = j * 16 + r0;
+                const f32x4_t lo = *(const f32x4_t*)(st + m * kNnCols + c8);
+                const f32x4_t hi = *(const f32x4_t*)(st + m * kNnCols + c8 + 4);
+                const u32x4_t u = {(uint32_t)f32_to_bf16_bits(lo[0]) | ((uint32_t)f32_to_bf16_bits(lo[1]) << 16),
+                                   (uint32_t)f32_to_bf16_bits(lo[2]) | ((uint32_t)f32_to_bf16_bits(lo[3]) << 16),
+                                   (uint32_t)f32_to_bf16_bits(hi[0]) | ((uint32_t)f32_to_bf16_bits(hi[1]) << 16),
+                                   (uint32_t)f32_to_bf16_bits(hi[2]) | ((uint32_t)f32_to_bf16_bits(hi[3]) << 16)};
+                __builtin_nontemporal_store(
+                    u, (u32x4_t*)((uint16_t*)g.c + c_off + (int64_t)m * g.ldc + nt * kNnCols + c8));
+            }
+            return;
+        }
         float* st = reinterpret_cast<float*>(&sm) + w * BM * 32;
 #pragma unroll
         for (int m2 = 0; m2 < MT; ++m2)
@@ -1383,8 +1408,11 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_kernel(NtGemmArgs g) {
 #pragma unroll
         for (int m2 = 0; m2 < MT; ++m2)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                __builtin_nontemporal_store(acc[m2][i], g.c + c_off + (int64_t)(m2 * 32 + acc_row(i, lane)) * g.ldc + n0);
+            for (int i = 0; i < 16; ++i) {
+                const int64_t off = c_off + (int64_t)(m2 * 32 + acc_row(i, lane)) * g.ldc + n0;
+                if (g.c_bf16) __builtin_nontemporal_store(f32_to_bf16_bits(acc[m2][i]), (uint16_t*)g.c + off);
+                else __builtin_nontemporal_store(acc[m2][i], g.c + off);
+            }
     }
 }
 

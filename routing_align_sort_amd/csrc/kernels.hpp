@@ -101,13 +101,14 @@ struct NtGemmArgs {
     int64_t lda;
     const uint16_t* b;
     int64_t ldb, b_group;
-    float* c;
+    float* c;                  // fp32 C, or bf16 C at (uint16_t*)c when c_bf16
     int64_t ldc, c_group;
     int M, N, K;
     const int32_t* expert_ids;
     const int32_t* post_padded;
     const int32_t* offsets;
     int by_block;
+    int c_bf16;                // NN form only: C rounded to bf16
 };
 hipError_t launch_nt_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream);
 // The NN form C[m][n] = sum_k A[m][k] B[k][n] (B in [K][N], N a multiple of 128),
@@ -130,8 +131,9 @@ struct BwdArgs {
     const float* gate_up;        // [C,2I] the training forward's gate and up values, or null (recomputed)
     const float* d_out;          // [T,H]
     float* dx;                   // [T,H]
-    float* dw13;                 // [E,2I,H]
-    float* dw2;                  // [E,H,I]
+    void* dw13;                  // [E,2I,H] fp32, or bf16 when dw_bf16
+    void* dw2;                   // [E,H,I]
+    int dw_bf16;
     float* d_w;                  // [T,K]
 };
 int64_t ffn_backward_workspace_bytes(int64_t T, int64_t K, int64_t E, int64_t H, int64_t I, int64_t C);

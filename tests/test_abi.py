@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 6
+    assert moe.abi_version() == 7
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -230,7 +230,7 @@ def test_backward_validation(lib):
     ok = moe._FfnParams(256, 2, 8, 512, 256, 64, moe.MOE_BF16, moe.MOE_BF16, 0, 0, 0)
     assert lib.moe_ffn_backward_workspace_bytes(ctypes.byref(ok)) > 0
     for field, value in (("w_dtype", moe.MOE_FP8_E4M3), ("B", 32), ("I", 384), ("weight_layout", 1),
-                         ("row_layout", 1), ("schedule", 1)):
+                         ("row_layout", 1), ("schedule", 1), ("grad_dtype", moe.MOE_FP8_E4M3)):
         p = moe._FfnParams(256, 2, 8, 512, 256, 64, moe.MOE_BF16, moe.MOE_BF16, 0, 0, 0)
         setattr(p, field, value)
         assert lib.moe_ffn_backward_workspace_bytes(ctypes.byref(p)) == -1, field

@@ -159,3 +159,26 @@ def test_backward_full_size_prefill_sampled():
     assert max(errs[:3]) <= 2e-2 and errs[3] <= 1e-5
     del L
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_bf16_weight_gradients(B):
+    # bf16 weight gradients are the fp32 sums rounded once (torch's RNE cast of
+    # the fp32 gradients, bit for bit); every other output is unchanged
+    dev = device()
+    cfg = ms.scaled("tiny_fp32", T=160, H=512, I=256, E=6, K=2, dtype="bf16", B=B)
+    L = ms.make_layer(cfg, device=dev)
+    d_out = torch.tensor(np.random.default_rng(7).standard_normal((cfg["T"], cfg["H"])).astype(np.float32),
+                         device=dev)
+    res = []
+    for gd in (torch.float32, torch.bfloat16):
+        layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=cfg["K"], B=B, score=cfg["score"],
+                             renormalize=cfg["renormalize"], x_dtype=L["x"].dtype, train=True, grad_dtype=gd)
+        layer.forward(L["x"], L["logits"])
+        res.append([t.clone() for t in layer.backward(L["x"], L["logits"], d_out)])
+        torch.cuda.synchronize()
+    (dx, dw13, dw2, dl, dwk), (dx_b, dw13_b, dw2_b, dl_b, dwk_b) = res
+    assert dw13_b.dtype == torch.bfloat16 and dw2_b.dtype == torch.bfloat16
+    assert torch.equal(dw13_b, dw13.to(torch.bfloat16)) and torch.equal(dw2_b, dw2.to(torch.bfloat16))
+    assert torch.equal(dx, dx_b) and torch.equal(dl, dl_b) and torch.equal(dwk, dwk_b)
+    say(f"B={B}: bf16 weight gradients equal the rounded fp32 ones; dx, d_w, d_logits unchanged")
