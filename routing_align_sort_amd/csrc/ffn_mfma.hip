@@ -1224,6 +1224,12 @@ nt_gemm_kernel(NtGemmArgs g) {
 // group of 16 lanes, lanes 4q..4q+3 point at the 16 columns of K-row q and
 // lane i receives column i of the four rows.  A lane half h of MFMA slice kk
 // covers k = 32h + 8kk .. +7 on both operands (the A read of kloop).
+#ifndef MOE_NN_EXPERT_PERSISTENT
+#define MOE_NN_EXPERT_PERSISTENT 1
+#endif
+#ifndef MOE_NN_EXPERT_GRID_MULT
+#define MOE_NN_EXPERT_GRID_MULT 1
+#endif
 constexpr int kNnCols = 128;                         // N columns per workgroup: 4 waves x 32
 constexpr int kNnPitch = kNnCols + 8;                // B tile row pitch, elements (272 bytes)
 constexpr int kNnPF = 2;                             // K-steps of both operands in flight
@@ -1416,9 +1422,245 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_kernel(NtGemmArgs g) {
     }
 }
 
+// The per-expert (weight-gradient) form of the NN GEMM as a persistent
+// kernel.  An expert's K is only its own rows (a K-step or two at prefill),
+// so one tile is a short chain: load, one or two K-steps, epilogue.  Here a
+// workgroup walks tiles blockIdx.x, +gridDim.x, ...; when a tile's K loop
+// ends, the next tile's first K-step is loaded into registers before this
+// tile's epilogue runs, so those loads are in flight while its results go
+// out.  Vector-memory waits count loads and stores in issue order, so the
+// loads are issued before the stores, and both the K-step's move into LDS
+// and the expert offsets (kept in LDS, read with no vector-memory wait) sit
+// where a wait for the loads does not also wait for this tile's stores.
+// Same tiles, same K order and same results as nn_gemm_kernel per expert.
+constexpr int kNnExpertMaxGroups = 1024;
+
+template <int BM, bool kBf16>
+__global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_expert_kernel(NtGemmArgs g, int tiles, int groups) {
+    using TL = Tile<BM>;
+    constexpr int MT = TL::MT;
+    constexpr int CPR = TL::CPR;
+    constexpr int RPS = kFfnThreads / CPR;
+    constexpr int BCH = 64 * kNnCols / 8 / kFfnThreads;
+    static_assert(TL::ROWS == BM, "every A row of the tile is a row of C");
+    static_assert(sizeof(NnSmem<BM>) >= 4 * BM * 32 * sizeof(float), "the epilogue stages through the tile buffers");
+    __shared__ NnSmem<BM> sm;
+    __shared__ int s_off[kNnExpertMaxGroups + 1];
+    const int nN = g.N / kNnCols;
+    const int mtiles = g.M / BM;
+    const int tid = threadIdx.x, w = tid / kWave, lane = lane_id(), r32 = lane & 31, half = lane >> 5;
+    if (blockIdx.x >= tiles) return;                              // uniform per workgroup
+    for (int e = tid; e <= groups; e += kFfnThreads) s_off[e] = g.offsets[e];
+    // per-thread chunk offsets in bytes within one K-step, the same for every
+    // tile (the host checks that BM rows of A and 64 rows of B span under 2^31
+    // bytes)
+    const int lds_a = (tid / CPR) * kLdsPitch + (tid % CPR) * 16;
+    uint32_t aoff[TL::APT];
+#pragma unroll
+    for (int r = 0; r < TL::APT; ++r) aoff[r] = (uint32_t)((tid / CPR + r * RPS) * g.lda * 2 + (tid % CPR) * 16);
+    uint32_t boff[BCH];
+    int lds_b[BCH];
+#pragma unroll
+    for (int r = 0; r < BCH; ++r) {
+        const int c = tid + r * kFfnThreads;
+        boff[r] = (uint32_t)(((c / 16) * g.ldb + (c % 16) * 8) * 2);
+        lds_b[r] = (c / 16) * kNnPitch + (c % 16) * 8;
+    }
+    const int64_t bstep = (int64_t)g.ldb * 128;                  // bytes per 64 B rows
+    const int grp16 = lane >> 4, q = (lane >> 2) & 3, sl = lane & 3;
+    const int b_row0 = (grp16 >> 1) * 32 + q;
+    const int b_col = w * 32 + (grp16 & 1) * 16 + 4 * sl;
+    __syncthreads();                                              // s_off
+
+    struct TileRef {
+        const uint8_t* A;
+        const uint8_t* Bt;
+        int64_t c_off;
+        int nt, nk;
+    };
+    auto tile_ref = [&](int tile) {
+        TileRef r;
+        int t = tile;
+        r.nt = t % nN;
+        t /= nN;
+        const int mt0 = t % mtiles, grp = t / mtiles;
+        const int lo = __builtin_amdgcn_readfirstlane(s_off[grp]);
+        const int hi = __builtin_amdgcn_readfirstlane(s_off[grp + 1]);
+        r.A = (const uint8_t*)(g.a + (int64_t)mt0 * BM * g.lda + lo);          // transposed activations
+        r.Bt = (const uint8_t*)(g.b + (int64_t)lo * g.ldb + r.nt * kNnCols);   // activation rows lo..
+        r.c_off = (int64_t)grp * g.c_group + (int64_t)mt0 * BM * g.ldc;
+        r.nk = (hi - lo) / 64;
+        return r;
+    };
+    // two register slots: an expert has a K-step or two, so loads are guarded
+    // rather than clamped (a clamped ring would fetch a lone step three times)
+    uint4 areg[2][TL::APT];
+    uint4 breg[2][BCH];
+    auto load = [&](const TileRef& tr, uint4 (&ar)[TL::APT], uint4 (&br)[BCH], int k) {
+        const uint8_t* a0 = tr.A + (int64_t)k * 128;             // uniform 64-bit bases, 32-bit lane offsets
+        const uint8_t* b0 = tr.Bt + (int64_t)k * bstep;
+#pragma unroll
+        for (int r = 0; r < TL::APT; ++r) ar[r] = __builtin_bit_cast(uint4, *(const u32x4_t*)(a0 + aoff[r]));
+#pragma unroll
+        for (int r = 0; r < BCH; ++r) br[r] = __builtin_bit_cast(uint4, *(const u32x4_t*)(b0 + boff[r]));
+    };
+    auto store = [&](const uint4 (&ar)[TL::APT], const uint4 (&br)[BCH], int buf) {
+#pragma unroll
+        for (int r = 0; r < TL::APT; ++r)
+            *(uint4*)(sm.a + buf * TL::ROWS * kLdsPitch + lds_a + r * RPS * kLdsPitch) = ar[r];
+#pragma unroll
+        for (int r = 0; r < BCH; ++r) *(uint4*)(&sm.b[buf][lds_b[r]]) = br[r];
+    };
+    f32x16_t acc[MT];
+    auto compute = [&](int buf) {
+        const uint8_t* abase = sm.a + buf * TL::ROWS * kLdsPitch + r32 * kLdsPitch + half * 64;
+        const uint16_t* bb = sm.b[buf];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_t*)(bb + (b_row0 + kk * 8) * kNnPitch + b_col));
+            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16_t*)(bb + (b_row0 + kk * 8 + 4) * kNnPitch + b_col));
+            uint4 bv;
+            bv.x = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+            bv.y = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+            bv.z = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+            bv.w = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+#pragma unroll
+            for (int m2 = 0; m2 < MT; ++m2) {
+                const uint4 af = *(const uint4*)(abase + m2 * 32 * kLdsPitch + kk * 16);
+                acc[m2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af), as_bf16x8(bv), acc[m2], 0, 0, 0);
+            }
+        }
+    };
+
+    // an expert without rows has nothing to load: its slot is zeroed instead,
+    // so that the move into LDS (and the wait for the loads) is unconditional
+    auto load_first = [&](const TileRef& tr) {
+        if (tr.nk > 0) {
+            load(tr, areg[0], breg[0], 0);
+        } else {
+#pragma unroll
+            for (int r = 0; r < TL::APT; ++r) areg[0][r] = uint4{0, 0, 0, 0};
+#pragma unroll
+            for (int r = 0; r < BCH; ++r) breg[0][r] = uint4{0, 0, 0, 0};
+        }
+    };
+    // the epilogue, as nn_gemm_kernel's: staged through LDS, non-temporal stores
+    auto epilogue = [&](const TileRef& tr) {
+        __syncthreads();                                          // last K-step's reads done
+        if constexpr (kBf16) {
+            float* st = reinterpret_cast<float*>(&sm);
+#pragma unroll
+            for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st[(m2 * 32 + acc_row(i, lane)) * kNnCols + w * 32 + r32] = acc[m2][i];
+            __syncthreads();
+            const int c8 = (tid & 15) * 8, r0 = tid >> 4;
+            uint16_t* cb = (uint16_t*)g.c + tr.c_off + (int64_t)r0 * g.ldc + tr.nt * kNnCols + c8;
+#pragma unroll
+            for (int j = 0; j < BM / 16; ++j) {
+                const int m = j * 16 + r0;
+                const f32x4_t lo = *(const f32x4_t*)(st + m * kNnCols + c8);
+                const f32x4_t hi = *(const f32x4_t*)(st + m * kNnCols + c8 + 4);
+                const u32x4_t u = {(uint32_t)f32_to_bf16_bits(lo[0]) | ((uint32_t)f32_to_bf16_bits(lo[1]) << 16),
+                                   (uint32_t)f32_to_bf16_bits(lo[2]) | ((uint32_t)f32_to_bf16_bits(lo[3]) << 16),
+                                   (uint32_t)f32_to_bf16_bits(hi[0]) | ((uint32_t)f32_to_bf16_bits(hi[1]) << 16),
+                                   (uint32_t)f32_to_bf16_bits(hi[2]) | ((uint32_t)f32_to_bf16_bits(hi[3]) << 16)};
+                __builtin_nontemporal_store(u, (u32x4_t*)cb);
+                cb += (int64_t)16 * g.ldc;
+            }
+        } else {
+            float* st = reinterpret_cast<float*>(&sm) + w * BM * 32;
+#pragma unroll
+            for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) st[(m2 * 32 + acc_row(i, lane)) * 32 + r32] = acc[m2][i];
+            __builtin_amdgcn_wave_barrier();
+            const int cq = (lane & 7) * 4, r0 = lane >> 3;
+            float* cf = g.c + tr.c_off + (int64_t)r0 * g.ldc + tr.nt * kNnCols + w * 32 + cq;
+#pragma unroll
+            for (int j = 0; j < BM / 8; ++j) {
+                const f32x4_t v = *(const f32x4_t*)(st + (j * 8 + r0) * 32 + cq);
+                __builtin_nontemporal_store(v, (f32x4_t*)cf);
+                cf += (int64_t)8 * g.ldc;
+            }
+        }
+    };
+
+    int tile = blockIdx.x;
+    TileRef cur = tile_ref(tile);
+    load_first(cur);
+    store(areg[0], breg[0], 0);
+    while (true) {
+#pragma unroll
+        for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[m2][i] = 0.f;
+        __syncthreads();                                          // K-step 0 in LDS buffer 0
+        // step k computes from buffer k & 1 while step k + 1 moves from slot
+        // (k + 1) & 1 into the other buffer, last read two steps back
+        const int nk = cur.nk;
+        for (int k0 = 0; k0 < nk; k0 += 2) {
+            const bool one = k0 + 1 < nk, two = k0 + 2 < nk;
+            if (one) load(cur, areg[1], breg[1], k0 + 1);
+            compute(0);
+            if (one) {
+                store(areg[1], breg[1], 1);
+                __syncthreads();
+                if (two) load(cur, areg[0], breg[0], k0 + 2);
+                compute(1);
+                if (two) {
+                    store(areg[0], breg[0], 0);
+                    __syncthreads();
+                }
+            }
+        }
+        const int next = tile + (int)gridDim.x;
+        if (next >= tiles) {                                      // the last tile: nothing to prefetch
+            epilogue(cur);
+            return;
+        }
+        // the next tile's first K-step is in flight during this epilogue;
+        // every path from these loads reaches the move into LDS below, the
+        // one place they are waited for
+        const TileRef nxt = tile_ref(next);
+        load_first(nxt);
+        epilogue(cur);
+        __syncthreads();                                          // staging reads done
+        store(areg[0], breg[0], 0);
+        tile = next;
+        cur = nxt;
+    }
+}
+
+template <int BM, bool kBf16>
+static hipError_t launch_nn_expert_bm(const NtGemmArgs& g, int64_t tiles, int64_t groups, hipStream_t stream) {
+    static int resident = 0;                                      // per process: one device shape
+    if (resident == 0) resident = resident_workgroups(nn_gemm_expert_kernel<BM, kBf16>);
+    if (resident <= 0) return hipErrorInvalidValue;
+    const int64_t grid = std::min<int64_t>(tiles, (int64_t)resident * MOE_NN_EXPERT_GRID_MULT);
+    hipLaunchKernelGGL((nn_gemm_expert_kernel<BM, kBf16>), dim3((unsigned)grid), dim3(kFfnThreads), 0, stream, g,
+                       (int)tiles, (int)groups);
+    return hipGetLastError();
+}
+
+// Whether nn_gemm_expert_kernel's 32-bit chunk offsets and its offset table
+// cover this launch.
+static bool nn_expert_fits(const NtGemmArgs& g, int BM, int64_t tiles, int64_t groups) {
+    return tiles < INT32_MAX && groups <= kNnExpertMaxGroups && (int64_t)BM * g.lda * 2 < ((int64_t)1 << 31) &&
+           (int64_t)64 * g.ldb * 2 < ((int64_t)1 << 31);
+}
+
 hipError_t launch_nn_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream) {
     const int64_t tiles = groups * (g.by_block ? 1 : g.M / BM) * (g.N / kNnCols);
     if (tiles == 0) return hipSuccess;
+    if (!g.by_block && MOE_NN_EXPERT_PERSISTENT && (BM == 64 || BM == 128) && nn_expert_fits(g, BM, tiles, groups)) {
+        if (BM == 64) return g.c_bf16 ? launch_nn_expert_bm<64, true>(g, tiles, groups, stream)
+                                      : launch_nn_expert_bm<64, false>(g, tiles, groups, stream);
+        return g.c_bf16 ? launch_nn_expert_bm<128, true>(g, tiles, groups, stream)
+                        : launch_nn_expert_bm<128, false>(g, tiles, groups, stream);
+    }
     switch (BM) {
         case 64: hipLaunchKernelGGL(nn_gemm_kernel<64>, dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g); break;
         case 128: hipLaunchKernelGGL(nn_gemm_kernel<128>, dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g); break;
