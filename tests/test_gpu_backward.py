@@ -182,3 +182,40 @@ def test_bf16_weight_gradients(B):
     assert torch.equal(dw13_b, dw13.to(torch.bfloat16)) and torch.equal(dw2_b, dw2.to(torch.bfloat16))
     assert torch.equal(dx, dx_b) and torch.equal(dl, dl_b) and torch.equal(dwk, dwk_b)
     say(f"B={B}: bf16 weight gradients equal the rounded fp32 ones; dx, d_w, d_logits unchanged")
+
+
+def test_weight_gradients_many_tiles_per_workgroup():
+    # dW13 has 16 x 8 x 12 = 1536 tiles and dW2 768: more than the persistent
+    # weight-gradient kernel's grid at two workgroups per CU, so each workgroup
+    # walks several tiles, across experts with no rows (zero K-steps) and one
+    # with 256 rows (four K-steps); fp32 against the oracle, bf16 the same sums
+    dev = device()
+    rng = np.random.default_rng(21)
+    T, K, E, H, I, B = 384, 2, 16, 1536, 512, 64
+    cfg = ms.scaled("tiny_fp32", T=T, H=H, I=I, E=E, K=K, dtype="bf16", B=B)
+    L = ms.make_layer(cfg, device=dev)
+    ids = rng.integers(1, 12, (T, K)).astype(np.int32)      # experts 12..15 get no rows
+    ids[:256, 0] = 0                                        # expert 0: 256 rows
+    ids[:256, 1] = rng.integers(1, 12, 256)
+    w = rng.random((T, K)).astype(np.float32)
+    tid, tw = torch.tensor(ids, device=dev), torch.tensor(w, device=dev)
+    al = moe.moe_align_sort(tid, E, B)
+    y = moe.moe_grouped_ffn(L["x"], L["w13"], L["w2"], al["sorted_token_ids"], al["expert_ids"],
+                            al["num_tokens_post_padded"], K=K, B=B)
+    d_out = torch.tensor(rng.standard_normal((T, H)).astype(np.float32), device=dev)
+    res = []
+    for gd in (torch.float32, torch.bfloat16):
+        res.append(moe.moe_ffn_backward(L["x"], L["w13"], L["w2"], tid, tw, al["sorted_token_ids"],
+                                        al["expert_ids"], al["num_tokens_post_padded"], al["expert_offsets"], y,
+                                        d_out, B=B, grad_dtype=gd))
+        torch.cuda.synchronize()
+    (dx, dw13, dw2, dwk), (dx_b, dw13_b, dw2_b, dwk_b) = res
+    rdx, rdw13, rdw2, rdwk = oracle.ffn_backward(host_bits(L["x"]), host_bits(L["w13"]), host_bits(L["w2"]), ids, w,
+                                                 y.cpu().numpy(), d_out.cpu().numpy(), w_dtype="bf16",
+                                                 x_dtype="bf16", inter="bf16")
+    errs = (rel_err(dw13.cpu().numpy(), rdw13), rel_err(dw2.cpu().numpy(), rdw2), rel_err(dx.cpu().numpy(), rdx))
+    say(f"{E} experts, H {H}, I {I}: dw13 {errs[0]:.2e} dw2 {errs[1]:.2e} dx {errs[2]:.2e}")
+    assert max(errs) <= 2e-2 and rel_err(dwk.cpu().numpy(), rdwk) <= 1e-5
+    assert not dw13[12:].any() and not dw2[12:].any()
+    assert torch.equal(dw13_b, dw13.to(torch.bfloat16)) and torch.equal(dw2_b, dw2.to(torch.bfloat16))
+    assert torch.equal(dx, dx_b) and torch.equal(dwk, dwk_b)
