@@ -1422,8 +1422,8 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_kernel(NtGemmArgs g) {
     }
 }
 
-// The per-expert (weight-gradient) form of the NN GEMM as a persistent
-// kernel.  An expert's K is only its own rows (a K-step or two at prefill),
+// The per-expert (weight-gradient) form of the NN GEMM with a bf16 product,
+// as a persistent kernel.  An expert's K is only its own rows (a K-step or two at prefill),
 // so one tile is a short chain: load, one or two K-steps, epilogue.  Here a
 // workgroup walks tiles blockIdx.x, +gridDim.x, ...; when a tile's K loop
 // ends, the next tile's first K-step is loaded into registers before this
@@ -1433,9 +1433,12 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_kernel(NtGemmArgs g) {
 // and the expert offsets (kept in LDS, read with no vector-memory wait) sit
 // where a wait for the loads does not also wait for this tile's stores.
 // Same tiles, same K order and same results as nn_gemm_kernel per expert.
+// With fp32 products the launches are bound by their writes and the
+// one-tile-per-workgroup kernel is as fast (slightly faster), so it keeps
+// that case.
 constexpr int kNnExpertMaxGroups = 1024;
 
-template <int BM, bool kBf16>
+template <int BM>
 __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_expert_kernel(NtGemmArgs g, int tiles, int groups) {
     using TL = Tile<BM>;
     constexpr int MT = TL::MT;
@@ -1546,45 +1549,29 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_expert_kernel(NtGemmAr
             for (int r = 0; r < BCH; ++r) breg[0][r] = uint4{0, 0, 0, 0};
         }
     };
-    // the epilogue, as nn_gemm_kernel's: staged through LDS, non-temporal stores
+    // the epilogue, as nn_gemm_kernel's bf16 one: the whole BM x 128 block
+    // staged through LDS, 16-byte non-temporal stores of whole rows
     auto epilogue = [&](const TileRef& tr) {
         __syncthreads();                                          // last K-step's reads done
-        if constexpr (kBf16) {
-            float* st = reinterpret_cast<float*>(&sm);
+        float* st = reinterpret_cast<float*>(&sm);
 #pragma unroll
-            for (int m2 = 0; m2 < MT; ++m2)
+        for (int m2 = 0; m2 < MT; ++m2)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) st[(m2 * 32 + acc_row(i, lane)) * kNnCols + w * 32 + r32] = acc[m2][i];
-            __syncthreads();
-            const int c8 = (tid & 15) * 8, r0 = tid >> 4;
-            uint16_t* cb = (uint16_t*)g.c + tr.c_off + (int64_t)r0 * g.ldc + tr.nt * kNnCols + c8;
+            for (int i = 0; i < 16; ++i) st[(m2 * 32 + acc_row(i, lane)) * kNnCols + w * 32 + r32] = acc[m2][i];
+        __syncthreads();
+        const int c8 = (tid & 15) * 8, r0 = tid >> 4;
+        uint16_t* cb = (uint16_t*)g.c + tr.c_off + (int64_t)r0 * g.ldc + tr.nt * kNnCols + c8;
 #pragma unroll
-            for (int j = 0; j < BM / 16; ++j) {
-                const int m = j * 16 + r0;
-                const f32x4_t lo = *(const f32x4_t*)(st + m * kNnCols + c8);
-                const f32x4_t hi = *(const f32x4_t*)(st + m * kNnCols + c8 + 4);
-                const u32x4_t u = {(uint32_t)f32_to_bf16_bits(lo[0]) | ((uint32_t)f32_to_bf16_bits(lo[1]) << 16),
-                                   (uint32_t)f32_to_bf16_bits(lo[2]) | ((uint32_t)f32_to_bf16_bits(lo[3]) << 16),
-                                   (uint32_t)f32_to_bf16_bits(hi[0]) | ((uint32_t)f32_to_bf16_bits(hi[1]) << 16),
-                                   (uint32_t)f32_to_bf16_bits(hi[2]) | ((uint32_t)f32_to_bf16_bits(hi[3]) << 16)};
-                __builtin_nontemporal_store(u, (u32x4_t*)cb);
-                cb += (int64_t)16 * g.ldc;
-            }
-        } else {
-            float* st = reinterpret_cast<float*>(&sm) + w * BM * 32;
-#pragma unroll
-            for (int m2 = 0; m2 < MT; ++m2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) st[(m2 * 32 + acc_row(i, lane)) * 32 + r32] = acc[m2][i];
-            __builtin_amdgcn_wave_barrier();
-            const int cq = (lane & 7) * 4, r0 = lane >> 3;
-            float* cf = g.c + tr.c_off + (int64_t)r0 * g.ldc + tr.nt * kNnCols + w * 32 + cq;
-#pragma unroll
-            for (int j = 0; j < BM / 8; ++j) {
-                const f32x4_t v = *(const f32x4_t*)(st + (j * 8 + r0) * 32 + cq);
-                __builtin_nontemporal_store(v, (f32x4_t*)cf);
-                cf += (int64_t)8 * g.ldc;
-            }
+        for (int j = 0; j < BM / 16; ++j) {
+            const int m = j * 16 + r0;
+            const f32x4_t lo = *(const f32x4_t*)(st + m * kNnCols + c8);
+            const f32x4_t hi = *(const f32x4_t*)(st + m * kNnCols + c8 + 4);
+            const u32x4_t u = {(uint32_t)f32_to_bf16_bits(lo[0]) | ((uint32_t)f32_to_bf16_bits(lo[1]) << 16),
+                               (uint32_t)f32_to_bf16_bits(lo[2]) | ((uint32_t)f32_to_bf16_bits(lo[3]) << 16),
+                               (uint32_t)f32_to_bf16_bits(hi[0]) | ((uint32_t)f32_to_bf16_bits(hi[1]) << 16),
+                               (uint32_t)f32_to_bf16_bits(hi[2]) | ((uint32_t)f32_to_bf16_bits(hi[3]) << 16)};
+            __builtin_nontemporal_store(u, (u32x4_t*)cb);
+            cb += (int64_t)16 * g.ldc;
         }
     };
 
@@ -1634,13 +1621,13 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_expert_kernel(NtGemmAr
     }
 }
 
-template <int BM, bool kBf16>
+template <int BM>
 static hipError_t launch_nn_expert_bm(const NtGemmArgs& g, int64_t tiles, int64_t groups, hipStream_t stream) {
     static int resident = 0;                                      // per process: one device shape
-    if (resident == 0) resident = resident_workgroups(nn_gemm_expert_kernel<BM, kBf16>);
+    if (resident == 0) resident = resident_workgroups(nn_gemm_expert_kernel<BM>);
     if (resident <= 0) return hipErrorInvalidValue;
     const int64_t grid = std::min<int64_t>(tiles, (int64_t)resident * MOE_NN_EXPERT_GRID_MULT);
-    hipLaunchKernelGGL((nn_gemm_expert_kernel<BM, kBf16>), dim3((unsigned)grid), dim3(kFfnThreads), 0, stream, g,
+    hipLaunchKernelGGL(nn_gemm_expert_kernel<BM>, dim3((unsigned)grid), dim3(kFfnThreads), 0, stream, g,
                        (int)tiles, (int)groups);
     return hipGetLastError();
 }
@@ -1655,12 +1642,10 @@ static bool nn_expert_fits(const NtGemmArgs& g, int BM, int64_t tiles, int64_t g
 hipError_t launch_nn_gemm(const NtGemmArgs& g, int BM, int64_t groups, hipStream_t stream) {
     const int64_t tiles = groups * (g.by_block ? 1 : g.M / BM) * (g.N / kNnCols);
     if (tiles == 0) return hipSuccess;
-    if (!g.by_block && MOE_NN_EXPERT_PERSISTENT && (BM == 64 || BM == 128) && nn_expert_fits(g, BM, tiles, groups)) {
-        if (BM == 64) return g.c_bf16 ? launch_nn_expert_bm<64, true>(g, tiles, groups, stream)
-                                      : launch_nn_expert_bm<64, false>(g, tiles, groups, stream);
-        return g.c_bf16 ? launch_nn_expert_bm<128, true>(g, tiles, groups, stream)
-                        : launch_nn_expert_bm<128, false>(g, tiles, groups, stream);
-    }
+    if (!g.by_block && g.c_bf16 && MOE_NN_EXPERT_PERSISTENT && (BM == 64 || BM == 128) &&
+        nn_expert_fits(g, BM, tiles, groups))
+        return BM == 64 ? launch_nn_expert_bm<64>(g, tiles, groups, stream)
+                        : launch_nn_expert_bm<128>(g, tiles, groups, stream);
     switch (BM) {
         case 64: hipLaunchKernelGGL(nn_gemm_kernel<64>, dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g); break;
         case 128: hipLaunchKernelGGL(nn_gemm_kernel<128>, dim3((unsigned)tiles), dim3(kFfnThreads), 0, stream, g); break;
