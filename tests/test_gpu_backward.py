@@ -219,3 +219,29 @@ def test_weight_gradients_many_tiles_per_workgroup():
     assert not dw13[12:].any() and not dw2[12:].any()
     assert torch.equal(dw13_b, dw13.to(torch.bfloat16)) and torch.equal(dw2_b, dw2.to(torch.bfloat16))
     assert torch.equal(dx, dx_b) and torch.equal(dwk, dwk_b)
+
+
+def test_bf16_weight_gradients_full_size():
+    # at the full prefill bf16 shape the bf16 weight gradients come from the
+    # persistent kernel (57344 dW13 tiles, over a hundred per workgroup) and
+    # the fp32 ones from the one-tile-per-workgroup kernel: the first must be
+    # the second rounded to bf16, bit for bit
+    dev = device()
+    cfg = ms.CONFIGS["prefill_bf16"]
+    L = ms.make_layer(cfg, device=dev)
+    d_out = torch.tensor(np.random.default_rng(5).standard_normal((cfg["T"], cfg["H"])).astype(np.float32),
+                         device=dev)
+    res = []
+    for gd in (torch.float32, torch.bfloat16):
+        layer = moe.MoELayer(L["w13"], L["w2"], T=cfg["T"], K=1, B=cfg["B"], score="softmax", renormalize=False,
+                             train=True, grad_dtype=gd)
+        layer.forward(L["x"], L["logits"])
+        _, dw13, dw2, _, _ = layer.backward(L["x"], L["logits"], d_out)
+        torch.cuda.synchronize()
+        res.append((dw13, dw2, layer))
+    (dw13, dw2, _), (dw13_b, dw2_b, _) = res
+    assert torch.equal(dw13_b, dw13.to(torch.bfloat16)) and torch.equal(dw2_b, dw2.to(torch.bfloat16))
+    assert dw13.abs().amax().item() > 0
+    say("prefill bf16 full size: bf16 weight gradients (persistent kernel) equal the rounded fp32 ones")
+    del res, L
+    torch.cuda.empty_cache()
