@@ -1629,8 +1629,7 @@ __global__ void __launch_bounds__(kFfnThreads, 2) nn_gemm_expert_kernel(NtGemmAr
 
 template <int BM>
 static hipError_t launch_nn_expert_bm(const NtGemmArgs& g, int64_t tiles, int64_t groups, hipStream_t stream) {
-    static int resident = 0;                                      // per process: one device shape
-    if (resident == 0) resident = resident_workgroups(nn_gemm_expert_kernel<BM>);
+    static const int resident = resident_workgroups(nn_gemm_expert_kernel<BM>);   // once per process
     if (resident <= 0) return hipErrorInvalidValue;
     const int64_t grid = std::min<int64_t>(tiles, (int64_t)resident * MOE_NN_EXPERT_GRID_MULT);
     hipLaunchKernelGGL(nn_gemm_expert_kernel<BM>, dim3((unsigned)grid), dim3(kFfnThreads), 0, stream, g,
