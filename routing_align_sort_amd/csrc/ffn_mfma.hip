@@ -692,19 +692,26 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
 }
 
 // Top-1 combine: a token whose id is outside [0,E) has no slot in the layout,
-// so no tile writes its output row; the workgroups of the down launch (every
-// one, tile or not) zero those rows, token t by workgroup t mod gridDim.
-__device__ __forceinline__ void top1_zero_skipped(const FfnArgs& a) {
-    for (int64_t t = blockIdx.x; t < a.T; t += gridDim.x) {
-        const int e = a.top1_ids[t];
-        if (e >= 0 && e < a.E) continue;
-        if (a.top1_bf16) {
-            uint16_t* row = (uint16_t*)a.top1_out + t * a.H;
-            for (int h = threadIdx.x * 8; h < a.H; h += kFfnThreads * 8) *(uint4*)(row + h) = make_uint4(0u, 0u, 0u, 0u);
-        } else {
-            float* row = (float*)a.top1_out + t * a.H;
-            for (int h = threadIdx.x * 4; h < a.H; h += kFfnThreads * 4) *(uint4*)(row + h) = make_uint4(0u, 0u, 0u, 0u);
-        }
+// so no tile writes its output row; the threads of the down launch (every
+// workgroup, tile or not) zero those rows: token t by thread t / gridDim of
+// workgroup t mod gridDim.  A thread's first id is loaded before the tile and
+// tested after it, so the check adds no memory round trip to the tile's start.
+__device__ __forceinline__ void top1_zero_row(const FfnArgs& a, int64_t t) {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    if (a.top1_bf16) {
+        uint4* row = (uint4*)((uint16_t*)a.top1_out + t * a.H);
+        for (int h = 0; h < a.H / 8; ++h) row[h] = z;
+    } else {
+        uint4* row = (uint4*)((float*)a.top1_out + t * a.H);
+        for (int h = 0; h < a.H / 4; ++h) row[h] = z;
+    }
+}
+
+__device__ __forceinline__ void top1_zero_skipped(const FfnArgs& a, int64_t t0, int e0) {
+    const int64_t stride = (int64_t)gridDim.x * kFfnThreads;
+    for (int64_t t = t0; t < a.T; t += stride) {
+        const int e = t == t0 ? e0 : a.top1_ids[t];
+        if (e < 0 || e >= a.E) top1_zero_row(a, t);
     }
 }
 
@@ -712,10 +719,12 @@ template <int kW, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     __shared__ FfnSmem<BM> sm;
-    if (a.top1_out) top1_zero_skipped(a);
+    const int64_t t0 = blockIdx.x + (int64_t)threadIdx.x * gridDim.x;   // top-1: first token to check
+    int e0 = 0;
+    if (a.top1_out && t0 < a.T) e0 = a.top1_ids[t0];
     int mb, nt;
-    if (!ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) return;
-    stage2_tile<kW, kPacked, BM, PF>(a, h_in, sa, mb, nt, sm);
+    if (ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) stage2_tile<kW, kPacked, BM, PF>(a, h_in, sa, mb, nt, sm);
+    if (a.top1_out) top1_zero_skipped(a, t0, e0);
 }
 
 // --------------------------------------------------------- fp8 quantisation --
