@@ -53,8 +53,8 @@ combine_kernel(int T, int K, int E, int H, int nchunk, const float* __restrict__
     if (kBf16) {
         const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
-        uint2* o = (uint2*)((uint16_t*)out + (int64_t)t * H + h);
-        *o = make_uint2(lo, hi);
+        // the layer's output is not read again here: non-temporal
+        __builtin_nontemporal_store(u32x2_t{lo, hi}, (u32x2_t*)((uint16_t*)out + (int64_t)t * H + h));
     } else {
         *(f32x4_t*)((float*)out + (int64_t)t * H + h) = acc;
     }
