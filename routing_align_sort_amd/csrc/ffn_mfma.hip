@@ -696,26 +696,46 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
 }
 
 // Top-1 combine: a token whose id is outside [0,E) has no slot in the layout,
-// so no tile writes its output row; the threads of the down launch (every
-// workgroup, tile or not) zero those rows: token t by thread t / gridDim of
-// workgroup t mod gridDim.  A thread's first id is loaded before the tile and
-// tested after it, so the check adds no memory round trip to the tile's start.
+// so no tile writes its output row; the workgroups of the down launch (every
+// one, tile or not) zero those rows.  Thread i of workgroup b checks token
+// b + i * gridDim (its id is loaded before the tile and tested after it, so
+// the check adds no memory round trip to the tile's start); the flagged
+// tokens are shared through LDS and each row is zeroed by the whole
+// workgroup with coalesced 16-byte stores.
 __device__ __forceinline__ void top1_zero_row(const FfnArgs& a, int64_t t) {
     const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    uint4* row;
+    int n;
     if (a.top1_bf16) {
-        uint4* row = (uint4*)((uint16_t*)a.top1_out + t * a.H);
-        for (int h = 0; h < a.H / 8; ++h) row[h] = z;
+        row = (uint4*)((uint16_t*)a.top1_out + t * a.H);
+        n = a.H / 8;
     } else {
-        uint4* row = (uint4*)((float*)a.top1_out + t * a.H);
-        for (int h = 0; h < a.H / 4; ++h) row[h] = z;
+        row = (uint4*)((float*)a.top1_out + t * a.H);
+        n = a.H / 4;
     }
+    for (int h = threadIdx.x; h < n; h += kFfnThreads) row[h] = z;
 }
 
-__device__ __forceinline__ void top1_zero_skipped(const FfnArgs& a, int64_t t0, int e0) {
+__device__ __forceinline__ void top1_zero_skipped(const FfnArgs& a, int64_t t0, int e0, uint64_t* flag_lds) {
     const int64_t stride = (int64_t)gridDim.x * kFfnThreads;
-    for (int64_t t = t0; t < a.T; t += stride) {
-        const int e = t == t0 ? e0 : a.top1_ids[t];
-        if (e < 0 || e >= a.E) top1_zero_row(a, t);
+    const int w = threadIdx.x / kWave;
+    // uniform over the workgroup: every pass sees the same base
+    for (int64_t base = blockIdx.x; base < a.T; base += stride) {
+        const int64_t t = base + (int64_t)threadIdx.x * gridDim.x;
+        const int e = t == t0 ? e0 : (t < a.T ? a.top1_ids[t] : 0);
+        const uint64_t m = ballot(t < a.T && (e < 0 || e >= a.E));
+        if (lane_id() == 0) flag_lds[w] = m;
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < kFfnThreads / kWave; ++v) {
+            uint64_t f = flag_lds[v];
+            while (f) {
+                const int l = __builtin_ctzll(f);
+                f &= f - 1;
+                top1_zero_row(a, base + (int64_t)(v * kWave + l) * gridDim.x);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -723,12 +743,13 @@ template <int kW, bool kPacked, int BM, int PF>
 __global__ void __launch_bounds__(kFfnThreads, (ffn_min_blocks<kW, BM>()))
 ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict__ sa, int nN) {
     __shared__ FfnSmem<BM> sm;
+    __shared__ uint64_t skip_flags[kFfnThreads / kWave];
     const int64_t t0 = blockIdx.x + (int64_t)threadIdx.x * gridDim.x;   // top-1: first token to check
     int e0 = 0;
     if (a.top1_out && t0 < a.T) e0 = a.top1_ids[t0];
     int mb, nt;
     if (ffn_tile(a.post_padded[0] / BM, nN, &mb, &nt)) stage2_tile<kW, kPacked, BM, PF>(a, h_in, sa, mb, nt, sm);
-    if (a.top1_out) top1_zero_skipped(a, t0, e0);
+    if (a.top1_out) top1_zero_skipped(a, t0, e0, skip_flags);
 }
 
 // --------------------------------------------------------- fp8 quantisation --

@@ -79,6 +79,56 @@ def oracle_tokens(x, w13, w2, ids, w, toks, w13_scale=None, w2_scale=None):
     return out, y
 
 
+# Oracle results of the full-size workloads, computed once per test session
+# and shared by the test files that compare those workloads (keyed by the
+# workload's name and the compared tokens; the generators are seeded, so the
+# same name always means the same inputs).
+_ORACLE_CACHE = {}
+
+
+def oracle_layer_cached(name, cfg, L, toks=None):
+    """(ids, w, toks, out_ref [n,H] f64, y_ref [n*K,H] f32) of workload ``name``.
+
+    ``toks`` None compares every token; otherwise the given token indices."""
+    ids, w = route_oracle(cfg, L)
+    toks = np.arange(cfg["T"]) if toks is None else np.asarray(toks)
+    key = (name, toks.tobytes())
+    if key not in _ORACLE_CACHE:
+        say(f"oracle: {name}, {len(toks)} tokens x {ids.shape[1]} slots (cached for this session)")
+        ref, yref = oracle_tokens(L["x"], L["w13"], L["w2"], ids, w, toks, L.get("w13_scale"),
+                                  L.get("w2_scale"))
+        _ORACLE_CACHE[key] = (ref, yref)
+    ref, yref = _ORACLE_CACHE[key]
+    return ids, w, toks, ref, yref
+
+
+def seeded_subset(T, n, seed=0):
+    """A sorted seeded sample of n of T tokens (the compute-bound shapes' 256-token subsets)."""
+    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+
+
+def compare_out(out, toks, ref, dtype, label):
+    """max|gpu - oracle| / max|oracle| over the compared tokens' output rows, asserted."""
+    got = out[torch.as_tensor(toks, device=out.device)].float().cpu().numpy()
+    err = rel_err(got, ref)
+    say(f"{label}: out rel err {err:.3e} over {len(toks)} tokens (tol {TOL[dtype]})")
+    assert err <= TOL[dtype], (label, err)
+    return err
+
+
+def compare_slots(y_rows, toks, ids, yref, dtype, label):
+    """The same bar on the slot rows y_slots[t*K+k] of the compared tokens
+    (rows of skipped slots are not written, so they are left out)."""
+    K = ids.shape[1]
+    slots = (np.asarray(toks)[:, None] * K + np.arange(K)[None]).ravel()
+    valid = ids[toks].ravel() >= 0
+    got = y_rows[torch.as_tensor(slots[valid], device=y_rows.device)].cpu().numpy()
+    err = rel_err(got, yref[valid])
+    say(f"{label}: y_slots rel err {err:.3e} over {int(valid.sum())} slots (tol {TOL[dtype]})")
+    assert err <= TOL[dtype], (label, err)
+    return err
+
+
 def route_oracle(cfg, L, K=None):
     """The oracle's routing of a generated layer's logits."""
     ids, w = oracle.route_topk(L["logits"].cpu().numpy(), K or cfg["K"], score=cfg["score"],

@@ -9,7 +9,8 @@ import torch
 
 import moe_synth as ms
 import routing_align_sort_amd as moe
-from gpu_helpers import TOL, as_library_weights, device, oracle_tokens, rel_err, route_oracle, say
+from gpu_helpers import (TOL, as_library_weights, compare_out, compare_slots, device, oracle_layer_cached,
+                         oracle_tokens, rel_err, route_oracle, say, seeded_subset)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,8 +81,14 @@ def test_fused_equals_two_launch_full_size(name, B):
     dev = device()
     cfg = ms.CONFIGS[name]
     L = ms.make_layer(cfg, device=dev)
-    compare(cfg, L, B)
+    one, out = compare(cfg, L, B)
     say(f"fused {name} B={B} full size: bit-identical to two launches")
+    # and against the oracle directly: every token, or the compute-bound
+    # shape's seeded 256-token subset (the layer tests' subset)
+    toks = seeded_subset(cfg["T"], 256, 5) if name.endswith("_512") else None
+    ids, w, toks, ref, yref = oracle_layer_cached(name, cfg, L, toks)
+    compare_out(out, toks, ref, cfg["dtype"], f"fused {name} B={B}")
+    compare_slots(one.y_slots, toks, ids, yref, cfg["dtype"], f"fused {name} B={B}")
     del L
     torch.cuda.empty_cache()
 

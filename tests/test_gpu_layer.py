@@ -1,8 +1,10 @@
 """The grouped FFN and the whole layer (route -> align -> FFN -> combine) on the
 GPU against the oracle: max|gpu - oracle| <= tol * max|oracle| with tol 1e-4
-(fp32), 2e-2 (bf16), 6e-2 (fp8 and MXFP4 weights, both with fp8 activations);
-full-size workloads are compared on a seeded sample of tokens, small ones on
-every token."""
+(fp32), 2e-2 (bf16), 6e-2 (fp8 and MXFP4 weights, both with fp8 activations),
+over the layer output and, with the same bar, over the slot rows y_slots.
+Every token is compared, at the small shapes and at the full decode and
+prefill shapes; the compute-bound shapes with 512 tokens per expert (top-8 of
+32 experts) are compared on a seeded subset of 256 tokens."""
 import numpy as np
 import pytest
 import torch
@@ -10,8 +12,8 @@ import torch
 import moe_synth as ms
 import oracle
 import routing_align_sort_amd as moe
-from gpu_helpers import (TOL, device, make_gpu_layer, oracle_tokens, rel_err, route_oracle, say,
-                         host_bits)
+from gpu_helpers import (TOL, compare_out, compare_slots, device, make_gpu_layer, oracle_layer_cached,
+                         oracle_tokens, rel_err, route_oracle, say, seeded_subset, host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,26 +34,32 @@ def run_layer(cfg, L, B=None):
     return layer, out
 
 
-def check_layer(cfg, L, toks, B=None, label=""):
-    dev = device()
-    layer, out = run_layer(cfg, L, B)
-    ids, w = route_oracle(cfg, L)
+def check_routing_and_align(cfg, L, layer, ids, w, label):
     gid = layer.topk_ids.cpu().numpy()
     assert np.array_equal(gid, ids), f"{label}: routing differs"
     assert np.allclose(layer.topk_weights.cpu().numpy(), w, rtol=1e-6, atol=0)
     al = oracle.align_sort(ids, layer.E_slabs, layer.B)
     assert np.array_equal(layer.sorted.cpu().numpy(), al["sorted_token_ids"]), f"{label}: align"
+    assert np.array_equal(layer.expert_ids.cpu().numpy(), al["expert_ids"]), f"{label}: expert_ids"
     assert int(layer.ntpp.item()) == al["num_tokens_post_padded"]
-    ref, yref = oracle_tokens(L["x"], L["w13"], L["w2"], ids, w, toks, L.get("w13_scale"),
-                              L.get("w2_scale"))
-    got = out[torch.as_tensor(toks, device=dev)].float().cpu().numpy()
-    err = rel_err(got, ref)
-    K = ids.shape[1]
-    slots = (np.asarray(toks)[:, None] * K + np.arange(K)[None]).ravel()
-    valid = (ids[toks].ravel() >= 0)
-    yerr = rel_err(layer.y_slots[torch.as_tensor(slots, device=dev)].cpu().numpy()[valid], yref[valid])
-    say(f"{label}: out rel err {err:.3e}  y_slots rel err {yerr:.3e}  (tol {TOL[cfg['dtype']]})")
-    assert err <= TOL[cfg["dtype"]], err
+
+
+def check_layer(cfg, L, toks=None, B=None, label="", name=None):
+    """Routing and Align & Sort bit-exact, then the output rows of ``toks``
+    (every token when None) and their slot rows within the dtype's tolerance.
+    ``name`` caches the oracle's result under that workload name, so several
+    block sizes (and other test files) share one oracle run."""
+    layer, out = run_layer(cfg, L, B)
+    if name is not None:
+        ids, w, toks, ref, yref = oracle_layer_cached(name, cfg, L, toks)
+    else:
+        ids, w = route_oracle(cfg, L)
+        toks = np.arange(cfg["T"]) if toks is None else np.asarray(toks)
+        ref, yref = oracle_tokens(L["x"], L["w13"], L["w2"], ids, w, toks, L.get("w13_scale"),
+                                  L.get("w2_scale"))
+    check_routing_and_align(cfg, L, layer, ids, w, label)
+    compare_out(out, toks, ref, cfg["dtype"], label)
+    compare_slots(layer.y_slots, toks, ids, yref, cfg["dtype"], label)
     return layer, out
 
 
@@ -164,9 +172,9 @@ def test_generator_device_matches_host():
 
 
 # ----------------------------------------------------------- full-size shapes --
-def sample_tokens(T, n, seed=0):
-    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
-
+# Every token of the decode and prefill workloads against the oracle, at each
+# block size the bench and the pages' tuning range use; the oracle runs once
+# per workload and is shared by the block sizes.
 
 def test_layer_decode_bf16_full_size():
     dev = device()
@@ -174,7 +182,7 @@ def test_layer_decode_bf16_full_size():
     say("generating DeepSeek-V3-shaped decode weights (256 experts, 22.5 GB bf16)")
     L = ms.make_layer(cfg, device=dev)
     for B in (16, 32):
-        check_layer(cfg, L, sample_tokens(cfg["T"], 8, B), B=B, label=f"decode bf16 B={B}")
+        check_layer(cfg, L, B=B, label=f"decode bf16 B={B}", name="decode_bf16")
     del L
     torch.cuda.empty_cache()
 
@@ -185,7 +193,7 @@ def test_layer_prefill_bf16_full_size():
     say("generating prefill bf16 weights (32 experts, 2.8 GB)")
     L = ms.make_layer(cfg, device=dev)
     for B in (32, 64, 128):
-        check_layer(cfg, L, sample_tokens(cfg["T"], 48, B), B=B, label=f"prefill bf16 B={B}")
+        check_layer(cfg, L, B=B, label=f"prefill bf16 B={B}", name="prefill_bf16")
     del L
     torch.cuda.empty_cache()
 
@@ -196,7 +204,7 @@ def test_layer_prefill_fp8_full_size():
     say("generating prefill fp8 weights (32 + 1 shared experts, 1.45 GB)")
     L = ms.make_layer(cfg, device=dev)
     for B in (32, 64, 128):
-        check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill fp8 B={B}")
+        check_layer(cfg, L, B=B, label=f"prefill fp8 B={B}", name="prefill_fp8")
     del L
     torch.cuda.empty_cache()
 
@@ -207,7 +215,7 @@ def test_layer_decode_mxfp4_full_size():
     say("generating DeepSeek-V3-shaped MXFP4 decode weights (256 experts, 5.6 GB)")
     L = ms.make_layer(cfg, device=dev)
     for B in (16, 32):
-        check_layer(cfg, L, sample_tokens(cfg["T"], 8, B), B=B, label=f"decode mxfp4 B={B}")
+        check_layer(cfg, L, B=B, label=f"decode mxfp4 B={B}", name="decode_fp4")
     del L
     torch.cuda.empty_cache()
 
@@ -218,7 +226,7 @@ def test_layer_prefill_mxfp4_full_size():
     say("generating prefill MXFP4 weights (32 experts, 0.7 GB)")
     L = ms.make_layer(cfg, device=dev)
     for B in (32, 64, 128):
-        check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill mxfp4 B={B}")
+        check_layer(cfg, L, B=B, label=f"prefill mxfp4 B={B}", name="prefill_fp4")
     del L
     torch.cuda.empty_cache()
 
@@ -230,18 +238,22 @@ def test_layer_prefill_fp8_uniform_full_size():
     say("generating prefill fp8 weights (32 experts, 1.41 GB), uniform routing")
     L = ms.make_layer(cfg, device=dev)
     for B in (32, 64):
-        check_layer(cfg, L, sample_tokens(cfg["T"], 32, B), B=B, label=f"prefill fp8 uniform B={B}")
+        check_layer(cfg, L, B=B, label=f"prefill fp8 uniform B={B}", name="prefill_fp8_uniform")
     del L
     torch.cuda.empty_cache()
 
 
+SUBSET_512 = 256        # tokens of the compute-bound shapes compared with the oracle
+
+
 @pytest.mark.parametrize("name", ["prefill_bf16_512", "prefill_fp8_512", "prefill_fp4_512"])
 def test_layer_512_per_expert_full_size(name):
-    # the compute-bound shapes at the block size the bench times them with
+    # the compute-bound shapes at the block size the bench times them with;
+    # the whole layer runs, a seeded 256-token subset is compared
     dev = device()
     cfg = ms.CONFIGS[name]
     say(f"generating {name} weights; 2048 tokens x top-{cfg['K']} over {cfg['E']} experts")
     L = ms.make_layer(cfg, device=dev)
-    check_layer(cfg, L, sample_tokens(cfg["T"], 16, 5), B=128, label=f"{name} B=128")
+    check_layer(cfg, L, seeded_subset(cfg["T"], SUBSET_512, 5), B=128, label=f"{name} B=128", name=name)
     del L
     torch.cuda.empty_cache()

@@ -13,7 +13,8 @@ import torch
 import moe_synth as ms
 import oracle
 import routing_align_sort_amd as moe
-from gpu_helpers import TOL, device, make_gpu_layer, oracle_tokens, rel_err, route_oracle, say
+from gpu_helpers import (TOL, compare_out, compare_slots, device, make_gpu_layer, oracle_layer_cached,
+                         oracle_tokens, rel_err, route_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,8 +131,15 @@ def test_layer_sorted_rows_full_size_prefill():
     dev = device()
     cfg = ms.CONFIGS["prefill_bf16"]
     L = ms.make_layer(cfg, device=dev)
-    sorted_vs_gather(cfg, L, 64)
+    s, out = sorted_vs_gather(cfg, L, 64)
     say("prefill bf16 full size: sorted rows bit-identical to gathered rows")
+    # every token against the oracle; the sorted rows read back by slot
+    ids, w, toks, ref, yref = oracle_layer_cached("prefill_bf16", cfg, L)
+    compare_out(out, toks, ref, cfg["dtype"], "prefill bf16 sorted rows, B 64")
+    ros = s.row_of_slot.long()
+    y_by_slot = torch.zeros((s.T * s.KO, s.H), dtype=torch.float32, device=dev)
+    y_by_slot[ros >= 0] = s.y_slots[ros[ros >= 0]]
+    compare_slots(y_by_slot, toks, ids, yref, cfg["dtype"], "prefill bf16 sorted rows, B 64")
     del L
     torch.cuda.empty_cache()
 

@@ -8,7 +8,8 @@ import torch
 
 import moe_synth as ms
 import routing_align_sort_amd as moe
-from gpu_helpers import as_library_weights, device, make_gpu_layer, say
+from gpu_helpers import (as_library_weights, compare_out, device, make_gpu_layer, oracle_layer_cached,
+                         say)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,19 +21,16 @@ def small_cfg(name):
     return ms.scaled(name, **over)
 
 
-@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_fp8", "prefill_fp4"])
-@pytest.mark.parametrize("B", [16, 64, 128])
-@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
-def test_top1_equals_ffn_then_combine(name, B, out_dtype):
+def top1_vs_separate(cfg, B, out_dtype, p_skip, seed):
+    """moe_grouped_ffn_top1 against moe_grouped_ffn + moe_combine on ids with a
+    share p_skip of out-of-range tokens (canonical and packed weights)."""
     dev = device()
-    cfg = small_cfg(name)
-    say(f"top-1 {name} B={B} out {out_dtype}")
     L = ms.make_layer(cfg, device=dev)
     w13, w2, s13, s2 = as_library_weights(L)
     T, E = cfg["T"], cfg["E"]
-    rng = np.random.default_rng(B)
+    rng = np.random.default_rng(seed)
     ids = rng.integers(0, E, (T, 1)).astype(np.int32)
-    bad = rng.random(T) < 0.1
+    bad = rng.random(T) < p_skip
     ids[bad, 0] = rng.choice([-1, E, E + 5], size=int(bad.sum()))
     tid = torch.tensor(ids, device=dev)
     w = torch.tensor(rng.random((T, 1)).astype(np.float32) + 0.25, device=dev)
@@ -53,7 +51,26 @@ def test_top1_equals_ffn_then_combine(name, B, out_dtype):
         torch.cuda.synchronize()
         assert torch.equal(got, ref), f"packed={packed}"
         assert (got[torch.tensor(bad, device=dev)] == 0).all()
-    say(f"  {int(bad.sum())} skipped tokens zeroed; bit-identical to FFN + combine (canonical and packed)")
+    say(f"  {int(bad.sum())} of {T} skipped tokens zeroed; bit-identical to FFN + combine (canonical and packed)")
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_fp8", "prefill_fp4"])
+@pytest.mark.parametrize("B", [16, 64, 128])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_top1_equals_ffn_then_combine(name, B, out_dtype):
+    say(f"top-1 {name} B={B} out {out_dtype}")
+    top1_vs_separate(small_cfg(name), B, out_dtype, 0.1, B)
+
+
+@pytest.mark.parametrize("p_skip", [0.5, 0.9])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_top1_mostly_skipped_tokens_full_width(p_skip, out_dtype):
+    # an expert-parallel share: most tokens are handled by other experts'
+    # owners, so their ids are out of range and their rows are zeroed here,
+    # at the full hidden width
+    say(f"top-1 with {p_skip:.0%} skipped tokens, H 7168, out {out_dtype}")
+    cfg = ms.scaled("prefill_bf16", T=1500, H=7168, I=256, E=8)
+    top1_vs_separate(cfg, 64, out_dtype, p_skip, int(p_skip * 100))
 
 
 def test_top1_layer_full_size_prefill_bf16():
@@ -69,6 +86,8 @@ def test_top1_layer_full_size_prefill_bf16():
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     say("prefill bf16, B 64: the top-1 layer equals FFN + combine bit for bit")
+    ids, w, toks, ref, _ = oracle_layer_cached("prefill_bf16", cfg, L)
+    compare_out(a, toks, ref, cfg["dtype"], "prefill bf16 top-1, B 64")
 
 
 def test_backward_after_a_top1_forward():
