@@ -29,6 +29,8 @@
 //   beyond that a scan launch turns the matrix into per-workgroup bases and
 //   totals first.  Padding, the tail and expert_ids are written by all
 //   workgroups in a grid-strided pattern.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -370,19 +372,38 @@ AlignPlan align_plan(int64_t S, int E) {
     return p;
 }
 
+// One-time per-device set-up, race-free: hipFuncSetAttribute applies to the
+// current device, so each device gets its own once-flag.
+constexpr int kMaxDevices = 64;
+
+static hipError_t current_device(int* dev) {
+    hipError_t err = hipGetDevice(dev);
+    if (err != hipSuccess) return err;
+    return (*dev < 0 || *dev >= kMaxDevices) ? hipErrorInvalidDevice : hipSuccess;
+}
+
+template <int R>
+static hipError_t align_lds_opt_in() {
+    static std::once_flag once[kMaxDevices];
+    static hipError_t result[kMaxDevices];
+    int dev = 0;
+    hipError_t err = current_device(&dev);
+    if (err != hipSuccess) return err;
+    std::call_once(once[dev], [dev] {
+        result[dev] = hipFuncSetAttribute((const void*)align_place_kernel<R>,
+                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)(kAlignLdsInts * sizeof(int)));
+    });
+    return result[dev];
+}
+
 template <int R>
 static hipError_t launch_align_r(const AlignPlan& plan, const int32_t* ids, int64_t S, int E, int B, int64_t C,
                                  const AlignOut& o, void* workspace, hipStream_t stream) {
     const int nbits = align_nbits(E);
     const size_t lds = (size_t)align_place_lds_ints(E, R) * sizeof(int);
-    static bool lds_opt_in = false;                // idempotent, so a race here is harmless
-    if (!lds_opt_in) {
-        hipError_t err = hipFuncSetAttribute((const void*)align_place_kernel<R>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)(kAlignLdsInts * sizeof(int)));
-        if (err != hipSuccess) return err;
-        lds_opt_in = true;
-    }
+    hipError_t err0 = align_lds_opt_in<R>();
+    if (err0 != hipSuccess) return err0;
     int32_t* counts = plan.single ? nullptr : static_cast<int32_t*>(workspace);
     int32_t* totals = plan.scan ? counts + (int64_t)plan.G * E : nullptr;
     if (!plan.single) {
