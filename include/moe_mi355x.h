@@ -58,14 +58,15 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size  */
     MOE_ERR_UNSUPPORTED = 2,   /* valid but not built: block size, dtype, E>1024 */
     MOE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required   */
-    MOE_ERR_HIP = 4            /* a HIP launch failed (no device, bad pointer)  */
+    MOE_ERR_HIP = 4,           /* a HIP launch failed (no device, bad pointer)  */
+    MOE_ERR_SCRATCH_LIMIT = 5  /* input beyond the no-allocation call's scratch */
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_FP4_E2M1 = 3 } moe_dtype_t;
@@ -149,6 +150,27 @@ moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32
                             int32_t *sorted_token_ids, int32_t *expert_ids,
                             int32_t *num_tokens_post_padded, int32_t *expert_offsets,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_align_sort_noalloc: moe_align_sort without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * (minus the workspace), same result bits, same errors, plus
+ * MOE_ERR_SCRATCH_LIMIT when moe_align_sort_workspace_bytes(T,K,E,B) exceeds
+ * moe_align_sort_noalloc_scratch_bytes() (1088 KiB: for example up to 35M
+ * slots over 256 experts, or 4.4M over 1024).
+ * Its scratch is a fixed device array inside the library; each device the
+ * library runs on holds one copy until the process ends, and the call
+ * allocates nothing.  Every call on a device uses that device's copy: calls
+ * that overlap in time on one device (on different streams, or from
+ * different host threads onto one device without ordering) race on it and
+ * give wrong results; calls ordered on one stream are safe.
+ */
+int64_t moe_align_sort_noalloc_scratch_bytes(void);
+moe_status_t moe_align_sort_noalloc(const int32_t *topk_ids, int32_t T, int32_t K, int32_t E, int32_t B,
+                                    int32_t *sorted_token_ids, int32_t *expert_ids,
+                                    int32_t *num_tokens_post_padded, int32_t *expert_offsets,
+                                    void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Grouped expert FFN                                                        */

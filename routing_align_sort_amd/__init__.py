@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # MOE_LIB_PATH selects another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_HERE, "libmoe_mi355x.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_SCRATCH_LIMIT = range(6)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1 = 0, 1, 2, 3
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 
@@ -49,7 +49,8 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align
             "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_grouped_ffn_top1", "moe_prepack_weights",
             "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine",
             "moe_unpermute_combine_backward", "moe_ffn_backward_workspace_bytes", "moe_ffn_backward",
-            "moe_grouped_ffn_train", "moe_route_backward")
+            "moe_grouped_ffn_train", "moe_route_backward", "moe_align_sort_noalloc",
+            "moe_align_sort_noalloc_scratch_bytes")
 
 
 def load_library(path: str = LIB_PATH):
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_align_sort_workspace_bytes.restype = i64
     lib.moe_align_sort.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     lib.moe_align_sort.restype = i32
+    lib.moe_align_sort_noalloc_scratch_bytes.argtypes = []
+    lib.moe_align_sort_noalloc_scratch_bytes.restype = i64
+    lib.moe_align_sort_noalloc.argtypes = [P, i32, i32, i32, i32, P, P, P, P, P]
+    lib.moe_align_sort_noalloc.restype = i32
     lib.moe_grouped_ffn_workspace_bytes.argtypes = [ctypes.POINTER(_FfnParams)]
     lib.moe_grouped_ffn_workspace_bytes.restype = i64
     lib.moe_grouped_ffn.argtypes = [ctypes.POINTER(_FfnParams), P, P, P, P, P, P, P, P, P, P, sz, P]
@@ -205,6 +210,32 @@ def moe_align_sort(topk_ids, E, B, *, sorted_token_ids=None, expert_ids=None,
         _ptr(ids), T, K, E, B, _ptr(sorted_token_ids), _ptr(expert_ids),
         _ptr(num_tokens_post_padded), _ptr(expert_offsets), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return {"sorted_token_ids": sorted_token_ids, "expert_ids": expert_ids,
+            "num_tokens_post_padded": num_tokens_post_padded, "expert_offsets": expert_offsets}
+
+
+def moe_align_sort_noalloc_scratch_bytes() -> int:
+    return int(load_library().moe_align_sort_noalloc_scratch_bytes())
+
+
+def moe_align_sort_noalloc(topk_ids, E, B, *, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                           expert_offsets=None, stream=None):
+    """moe_align_sort into caller-given outputs with no workspace: the library's
+    fixed scratch stands in for it and nothing is allocated (outputs are
+    required for that reason).  Calls that overlap on one device race."""
+    lib = load_library()
+    ids = topk_ids if topk_ids.dim() == 2 else topk_ids.view(-1, 1)
+    T, K = ids.shape
+    _need(ids, torch.int32, "topk_ids")
+    C = moe_align_sort_capacity(T, K, E, B)
+    _need(sorted_token_ids, torch.int32, "sorted_token_ids", C)
+    _need(expert_ids, torch.int32, "expert_ids", C // B)
+    _need(num_tokens_post_padded, torch.int32, "num_tokens_post_padded", 1)
+    if expert_offsets is not None:
+        _need(expert_offsets, torch.int32, "expert_offsets", E + 1)
+    _check("moe_align_sort_noalloc", lib.moe_align_sort_noalloc(
+        _ptr(ids), T, K, E, B, _ptr(sorted_token_ids), _ptr(expert_ids),
+        _ptr(num_tokens_post_padded), _ptr(expert_offsets), _stream(stream)))
     return {"sorted_token_ids": sorted_token_ids, "expert_ids": expert_ids,
             "num_tokens_post_padded": num_tokens_post_padded, "expert_offsets": expert_offsets}
 

@@ -427,6 +427,25 @@ static hipError_t launch_align_r(const AlignPlan& plan, const int32_t* ids, int6
     return hipGetLastError();
 }
 
+// The no-allocation entry point's scratch: a fixed device array in place of
+// the caller's workspace.  Every device holds its own copy at its own
+// address; host code uses the address returned by hipGetSymbolAddress, never
+// the array's name (which is a host-side stand-in).
+static __device__ __align__(256) int32_t scratch[kAlignScratchBytes / sizeof(int32_t)];
+
+hipError_t align_scratch_address(void** ptr) {
+    static std::once_flag once[kMaxDevices];
+    static void* addr[kMaxDevices];
+    static hipError_t result[kMaxDevices];
+    int dev = 0;
+    hipError_t err = current_device(&dev);
+    if (err != hipSuccess) return err;
+    std::call_once(once[dev], [dev] { result[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)); });
+    if (result[dev] != hipSuccess) return result[dev];
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 hipError_t launch_align_sort(const int32_t* ids, int64_t S, int E, int B, int64_t C,
                              int32_t* sorted, int32_t* expert_ids, int32_t* post_padded,
                              int32_t* offsets, void* workspace, hipStream_t stream) {

@@ -37,6 +37,7 @@ const char* moe_status_string(int32_t s) {
         case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_HIP: return "HIP launch failed";
+        case MOE_ERR_SCRATCH_LIMIT: return "input too large for the fixed scratch of the no-allocation call";
         default: return "unknown status";
     }
 }
@@ -84,6 +85,25 @@ moe_status_t moe_align_sort(const int32_t* topk_ids, int32_t T, int32_t K, int32
     if (need > 0 && (!workspace || (int64_t)workspace_bytes < need)) return MOE_ERR_WORKSPACE;
     return from_hip(launch_align_sort(topk_ids, S, E, B, C, sorted_token_ids, expert_ids,
                                       num_tokens_post_padded, expert_offsets, workspace, as_stream(stream)));
+}
+
+int64_t moe_align_sort_noalloc_scratch_bytes(void) { return kAlignScratchBytes; }
+
+moe_status_t moe_align_sort_noalloc(const int32_t* topk_ids, int32_t T, int32_t K, int32_t E, int32_t B,
+                                    int32_t* sorted_token_ids, int32_t* expert_ids,
+                                    int32_t* num_tokens_post_padded, int32_t* expert_offsets, void* stream) {
+    if (!align_args_ok(T, K, E, B)) return MOE_ERR_INVALID_ARG;
+    if (E > kAlignMaxExperts || B > 1024) return MOE_ERR_UNSUPPORTED;
+    const int64_t S = (int64_t)T * K;
+    const int64_t C = capacity(S, E, B);
+    if (!num_tokens_post_padded || (S > 0 && !topk_ids) || (C > 0 && (!sorted_token_ids || !expert_ids)))
+        return MOE_ERR_INVALID_ARG;
+    if (align_plan(S, E).workspace_bytes > kAlignScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+    void* scratch = nullptr;                       // this device's copy of the fixed array
+    const hipError_t err = align_scratch_address(&scratch);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    return from_hip(launch_align_sort(topk_ids, S, E, B, C, sorted_token_ids, expert_ids,
+                                      num_tokens_post_padded, expert_offsets, scratch, as_stream(stream)));
 }
 
 static moe_status_t ffn_check(const moe_ffn_params_t* p) {

@@ -36,6 +36,11 @@ AlignPlan align_plan(int64_t S, int E);
 hipError_t launch_align_sort(const int32_t* ids, int64_t S, int E, int B, int64_t C, int32_t* sorted,
                              int32_t* expert_ids, int32_t* post_padded, int32_t* offsets,
                              void* workspace, hipStream_t stream);
+// The no-allocation Align & Sort's fixed scratch (a static device array of
+// this many bytes on every device the library runs on): its device address
+// on the current device, looked up once per device.
+constexpr int64_t kAlignScratchBytes = (int64_t)1088 << 10;
+hipError_t align_scratch_address(void** ptr);
 
 // -------------------------------------------------------------- grouped FFN --
 struct FfnArgs {

@@ -30,14 +30,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 7
+    assert moe.abi_version() == 8
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -66,6 +66,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     st = lib.moe_align_sort(P(8), 16384, 8, 256, 64, P(8), P(8), P(8), None, None, need - 1, None)
     assert st == moe.MOE_ERR_WORKSPACE
     assert lib.moe_align_sort_workspace_bytes(64, 8, 256, 16) == 0     # one workgroup, no workspace
+
+
+def test_no_alloc_align_sort_limit_is_checked_on_the_host(lib):
+    # beyond the fixed scratch: rejected before the device is touched
+    P = ctypes.c_void_p
+    limit = lib.moe_align_sort_noalloc_scratch_bytes()
+    assert limit == 1088 * 1024
+    assert lib.moe_align_sort_workspace_bytes(1 << 20, 8, 1024, 16) > limit
+    st = lib.moe_align_sort_noalloc(P(8), 1 << 20, 8, 1024, 16, P(8), P(8), P(8), None, None)
+    assert st == moe.MOE_ERR_SCRATCH_LIMIT
+    assert "scratch" in moe.status_string(st)
+    # the same argument checks as the workspace call
+    assert lib.moe_align_sort_noalloc(P(8), 4, 2, 8, 16, None, P(8), P(8), None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_align_sort_noalloc(None, 1, 1, 2000, 1, None, None, P(8), None, None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_route_validation(lib):
