@@ -255,7 +255,7 @@ def align_timed(dev, T, iters=200, cold=False, K=8, E=256, B=64, zipf_s=1.1):
     ids_np = ms.zipf_topk_ids(0, ms.TAG_IDS, T, K, E, zipf_s)
     ids = torch.from_numpy(ids_np).to(dev)
     ws_b = moe.moe_align_sort_workspace_bytes(T, K, E, B)
-    ws = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_b, 1), dtype=torch.uint8, device=dev)   # zero before first use
     out = moe.moe_align_sort(ids, E, B, workspace=ws)            # allocates the outputs once
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold else None
     ev = moe.HipEvents(2 * iters)

@@ -36,8 +36,12 @@
  *   frees or synchronises, and never reads device memory from the host, so a
  *   sequence of calls can be captured into a HIP graph.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
- *   work is enqueued asynchronously on it.  The library keeps no mutable
- *   global state; calls are thread-safe.
+ *   work is enqueued asynchronously on it.  Calls are thread-safe: the
+ *   library's only host-side state is one-time per-device set-up (kernel
+ *   attributes, device properties, the address of moe_align_sort_noalloc's
+ *   scratch), guarded by std::call_once; its only device-side state is that
+ *   scratch (see there).  Buffers passed to calls that overlap in time must
+ *   not overlap.
  * - Errors: arguments are validated on the host before anything is enqueued;
  *   an invalid call returns a status != MOE_OK and enqueues nothing.  A launch
  *   that fails returns MOE_ERR_HIP.  Data are never an error: expert ids
@@ -140,8 +144,17 @@ moe_status_t moe_route_topk(const moe_route_params_t *p, const float *logits, co
  * topk_ids device int32 [T*K]; sorted_token_ids device int32 [C] (out);
  * expert_ids device int32 [C/B] (out); num_tokens_post_padded device int32 [1]
  * (out); expert_offsets device int32 [E+1] (out) or NULL; workspace device,
- * at least moe_align_sort_workspace_bytes(T,K,E,B) bytes, 256-byte aligned,
- * contents need not be initialised and are clobbered.
+ * at least moe_align_sort_workspace_bytes(T,K,E,B) bytes (0 when S <= 4096:
+ * NULL allowed), 256-byte aligned.  Its first 4352 bytes hold the words of a
+ * grid-wide barrier: the workspace must be zero-filled before its first use
+ * (hipMemset, torch.zeros, ...), and every call that completes leaves the
+ * barrier's counters zero again, so one workspace serves any number of calls
+ * in stream order (concurrent calls need separate workspaces).  The rest is
+ * scratch.  Its first int32 is a status word: nonzero means a barrier wait
+ * gave up (the workgroups of the launch could not all run at once, which
+ * needs other work occupying the device for a long time); the results of
+ * that call are then invalid, and the word stays set until the caller
+ * clears it.
  * Limits: 1 <= E <= 1024; 1 <= B <= 1024; S + C < 2^31.
  */
 int64_t moe_align_sort_capacity(int32_t T, int32_t K, int32_t E, int32_t B);
@@ -158,7 +171,7 @@ moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32
  * (minus the workspace), same result bits, same errors, plus
  * MOE_ERR_SCRATCH_LIMIT when moe_align_sort_workspace_bytes(T,K,E,B) exceeds
  * moe_align_sort_noalloc_scratch_bytes() (1088 KiB: for example up to 35M
- * slots over 256 experts, or 4.4M over 1024).
+ * slots over 256 experts, or 4.3M over 1024).
  * Its scratch is a fixed device array inside the library; each device the
  * library runs on holds one copy until the process ends, and the call
  * allocates nothing.  Every call on a device uses that device's copy: calls

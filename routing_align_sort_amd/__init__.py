@@ -183,7 +183,10 @@ def moe_align_sort_workspace_bytes(T, K, E, B) -> int:
 
 def moe_align_sort(topk_ids, E, B, *, sorted_token_ids=None, expert_ids=None,
                    num_tokens_post_padded=None, expert_offsets=None, workspace=None, stream=None):
-    """Align & Sort of int32 ``topk_ids`` [T,K]; returns a dict of device tensors."""
+    """Align & Sort of int32 ``topk_ids`` [T,K]; returns a dict of device tensors.
+
+    A caller-given ``workspace`` must be zero-filled before its first use
+    (every call leaves it so); without one a zeroed tensor is allocated."""
     lib = load_library()
     ids = topk_ids if topk_ids.dim() == 2 else topk_ids.view(-1, 1)
     T, K = ids.shape
@@ -200,7 +203,7 @@ def moe_align_sort(topk_ids, E, B, *, sorted_token_ids=None, expert_ids=None,
         expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     ws_need = moe_align_sort_workspace_bytes(T, K, E, B)
     if workspace is None and ws_need > 0:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(ws_need, dtype=torch.uint8, device=dev)    # zero before its first use
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _need(sorted_token_ids, torch.int32, "sorted_token_ids", C)
     _need(expert_ids, torch.int32, "expert_ids", C // B)
@@ -676,7 +679,7 @@ class MoELayer:
         # where the one-stage schedule reports a wait that gave up (int32, 0 = fine)
         self.status_offset = moe_grouped_ffn_workspace_bytes(
             T, self.KO, self.E_slabs, self.H, self.I, B, w13.dtype, x_dtype, self.rows_sorted) + 32
-        self.ws_align = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
+        self.ws_align = torch.zeros(max(ws_a, 1), dtype=torch.uint8, device=dev)   # zero before first use
         self.ws_ffn = torch.empty(max(ws_f, 1), dtype=torch.uint8, device=dev)
         ny = C if self.rows_sorted else T * self.KO
         self.y_slots = torch.empty((ny, self.H), dtype=torch.float32, device=dev)

@@ -25,12 +25,13 @@ hipError_t launch_route_topk(const RouteArgs& a, hipStream_t stream);
 constexpr int kAlignMaxExperts = 1024;
 
 struct AlignPlan {
-    bool single;               // one workgroup, one launch
-    bool scan;                 // a scan launch merges the counts (many workgroups)
-    int G;                     // workgroups
+    bool single;               // one workgroup, no workspace
+    bool masks;                // stable ranks from per-wave LDS masks (else ballots)
+    bool merge;                // each workgroup merges the [G,E] counts (else column scans)
+    int G;                     // workgroups (1, or a multiple of the 8 XCDs)
     int R;                     // slots per thread (chunk = 1024 * R)
     int64_t chunk;
-    int64_t workspace_bytes;
+    int64_t workspace_bytes;   // barrier words + counts (+ totals)
 };
 AlignPlan align_plan(int64_t S, int E);
 hipError_t launch_align_sort(const int32_t* ids, int64_t S, int E, int B, int64_t C, int32_t* sorted,

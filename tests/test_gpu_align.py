@@ -84,3 +84,42 @@ def test_align_many_experts_large():
     # 4M slots over 1024 experts: the widest chunk that 1024 experts leave room for
     rng = np.random.default_rng(11)
     run_and_compare(rng.integers(0, 1024, size=(524288, 8)).astype(np.int32), 1024, 32, "524288x8/1024")
+
+
+def test_align_workspace_reused_across_paths():
+    # one zeroed workspace serves calls of every path in stream order: the
+    # single workgroup, one launch with the merge, one launch with the column
+    # scans and two barriers, and the count/scan/place launches; the barrier
+    # words are zero again after each call and no wait gave up
+    dev = device()
+    shapes = [(16384, 8, 256, 64), (100, 8, 64, 16), (131072, 8, 256, 64), (1024, 8, 256, 64),
+              (5000, 1, 3, 1), (1_200_000, 8, 256, 64), (16384, 8, 256, 128), (40000, 8, 1024, 32)]
+    need = max(moe.moe_align_sort_workspace_bytes(T, K, E, B) for T, K, E, B in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for T, K, E, B in shapes:
+        ids_np = ms.zipf_topk_ids(T, ms.TAG_IDS, T, K, E, 1.1)
+        ids = torch.from_numpy(ids_np).to(dev)
+        r = moe.moe_align_sort(ids, E, B, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.align_sort(ids_np, E, B)
+        assert np.array_equal(r["sorted_token_ids"].cpu().numpy(), ref["sorted_token_ids"]), (T, K, E, B)
+        assert np.array_equal(r["expert_ids"].cpu().numpy(), ref["expert_ids"]), (T, K, E, B)
+        words = ws[:4352].view(torch.int32).cpu().numpy()
+        counters = np.concatenate([words[[0, 32]], words[64:576:32]])   # status, top, 16 groups
+        assert (counters == 0).all(), (T, K, E, B, counters)    # reset by every call; status 0
+        say(f"shared workspace T={T} K={K} E={E} B={B}: bit-exact, counters zero, "
+            f"generations {words[576:1088:32][:4].tolist()}...")
+
+
+@pytest.mark.parametrize("E", [700, 800])
+def test_align_mask_and_ballot_ranks_near_the_lds_limit(E):
+    # 700 experts still rank with per-wave LDS masks, 800 with ballots
+    rng = np.random.default_rng(E)
+    run_and_compare(rng.integers(0, E, size=(300000, 8)).astype(np.int32), E, 64, f"300000x8/{E}")
+
+
+def test_align_beyond_one_resident_round():
+    # 9.6M slots need more than 256 chunks of 32768: counts, column scans and
+    # placement in three launches
+    ids = ms.zipf_topk_ids(3, ms.TAG_IDS, 1_200_000, 8, 256, 1.1)
+    run_and_compare(ids, 256, 64, "1200000x8/256")
