@@ -942,6 +942,22 @@ def run_cpu_baseline(cfg, B, dev, budget_s=12.0):
     n = int(min(T, max(n0, budget_s / max(t_probe / n0, 1e-9))))
     t_ffn = ffn(np.sort(order[:n]))
     per_token = t_ra / T + t_ffn / n
+    # the same oracle on one core: a smaller seeded sample (about a quarter of the budget)
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        t_one = ffn(np.sort(order[:1]))
+        n1 = int(min(T, max(1, 0.25 * budget_s / max(t_one, 1e-9))))
+        t_ffn1 = ffn(np.sort(order[:n1]))
+    finally:
+        oracle.set_num_threads(threads)
+    per_token1 = t_ra / T + t_ffn1 / n1
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     # the Align & Sort oracle alone (serial C, one core) on the 16384 x top-8 workload
     a16 = ms.CONFIGS["align_16k"]
     ids16 = ms.zipf_topk_ids(0, ms.TAG_IDS, a16["T"], a16["K"], a16["E"], a16["zipf_s"])
@@ -950,8 +966,11 @@ def run_cpu_baseline(cfg, B, dev, budget_s=12.0):
     for _ in range(reps):
         oracle.align_sort(ids16, a16["E"], a16["B"])
     align_ms = (time.perf_counter() - t1) / reps * 1e3
-    return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+    return {"value": round(1.0 / per_token, 2), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "align_sort_16k_single_core_ms": round(align_ms, 3),
+            "single_core_tokens_per_s": round(1.0 / per_token1, 3),
+            "single_core_sample": f"expert FFN + combine for {n1} seeded tokens on one thread ({t_ffn1:.2f} s)",
+            "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
             "sample": f"routing + Align & Sort over all {T} tokens ({t_ra:.3f} s), expert FFN + "
                       f"combine for {n} seeded tokens ({t_ffn:.2f} s), double precision; "
                       f"tokens/s extrapolated per token"}

@@ -92,6 +92,8 @@ def _load():
     lib.oracle_route_backward.argtypes = [i32, i32, i32, i32, i32, f64, i32, P, P, P, P]
     lib.oracle_route_backward.restype = i32
     lib.oracle_num_threads.restype = i32
+    lib.oracle_set_num_threads.argtypes = [i32]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -102,6 +104,11 @@ def _ptr(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (for timing it on one core)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def num_threads() -> int:

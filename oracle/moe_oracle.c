@@ -33,6 +33,7 @@
 
 /* Threads the oracle's parallel loop uses (reported with its timings). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }   /* timing only */
 
 /* ------------------------------------------------------------------------ */
 /* Number formats                                                            */
