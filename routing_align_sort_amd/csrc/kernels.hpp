@@ -28,10 +28,11 @@ struct AlignPlan {
     bool single;               // one workgroup, no workspace
     bool masks;                // stable ranks from per-wave LDS masks (else ballots)
     bool merge;                // each workgroup merges the [G,E] counts (else column scans)
+    bool tagged;               // merge of tagged count words, no grid barrier (few workgroups)
     int G;                     // workgroups (1, or a multiple of the 8 XCDs)
     int R;                     // slots per thread (chunk = 1024 * R)
     int64_t chunk;
-    int64_t workspace_bytes;   // barrier words + counts (+ totals)
+    int64_t workspace_bytes;   // barrier words + counts (+ totals; tagged: 64-bit counts)
 };
 AlignPlan align_plan(int64_t S, int E);
 hipError_t launch_align_sort(const int32_t* ids, int64_t S, int E, int B, int64_t C, int32_t* sorted,

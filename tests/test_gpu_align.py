@@ -123,3 +123,25 @@ def test_align_beyond_one_resident_round():
     # placement in three launches
     ids = ms.zipf_topk_ids(3, ms.TAG_IDS, 1_200_000, 8, 256, 1.1)
     run_and_compare(ids, 256, 64, "1200000x8/256")
+
+
+def test_align_tagged_merge_calls_in_a_row():
+    # 8 and 16 workgroups merge tagged count words without a grid barrier:
+    # calls of different shapes in a row on one workspace (the 16-workgroup
+    # rows 8..15 still hold the first call's words when the third call reads
+    # them), mixed with calls that write plain counts into the same region
+    dev = device()
+    shapes = [(2500, 8, 256, 64), (1024, 8, 256, 16), (2500, 8, 256, 64), (131072, 8, 256, 64),
+              (2100, 8, 200, 32), (600, 8, 32, 1), (2500, 8, 256, 64)]
+    need = max(moe.moe_align_sort_workspace_bytes(T, K, E, B) for T, K, E, B in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for n, (T, K, E, B) in enumerate(shapes):
+        ids_np = ms.zipf_topk_ids(100 + n, ms.TAG_IDS, T, K, E, 1.1)
+        ids = torch.from_numpy(ids_np).to(dev)
+        r = moe.moe_align_sort(ids, E, B, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.align_sort(ids_np, E, B)
+        assert np.array_equal(r["sorted_token_ids"].cpu().numpy(), ref["sorted_token_ids"]), (n, T, K, E, B)
+        assert np.array_equal(r["expert_ids"].cpu().numpy(), ref["expert_ids"]), (n, T, K, E, B)
+        assert int(ws[:4].view(torch.int32).item()) == 0, (n, "a wait gave up")
+        say(f"tagged merge call {n}: T={T} K={K} E={E} B={B} bit-exact")
