@@ -77,7 +77,7 @@ def _mean(v):
 
 
 def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=1, graph=True,
-                    schedule="two_launch"):
+                    schedule="two_launch", slot_rows="fp32"):
     """Generate one workload, run `warmup` + `steps` layer passes with events
     around every kernel; return timings and what the roofline needs.
     rows="sorted": the layer permutes the token rows into the sorted order
@@ -100,7 +100,8 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=
                          w13_scale=s13, w2_scale=s2,
                          x_dtype=L["x"].dtype,
                          out_dtype=torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16,
-                         rows=rows, schedule=schedule)
+                         rows=rows, schedule=schedule,
+                         slot_dtype=torch.bfloat16 if slot_rows == "bf16" else torch.float32)
     x, logits, bias = L["x"], L["logits"], L["bias"]
     inputs = [(x, logits)]
     for j in range(1, rotate):
@@ -320,6 +321,8 @@ def main():
                          "and combine back through the inverse map")
     ap.add_argument("--schedule", default="two_launch", choices=("two_launch", "fused"),
                     help="fused: both GEMMs in one persistent launch")
+    ap.add_argument("--slot-rows", default="fp32", choices=("fp32", "bf16"),
+                    help="type of the slot rows between the FFN and the combine (layers with a combine)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the align-only and secondary-workload figures")
@@ -362,7 +365,8 @@ def main():
     cfg = ms.CONFIGS[args.workload]
     B = args.B or cfg["B"]
 
-    r = run_layer_timed(cfg, B, args.steps, args.warmup, dev, rows=args.rows, schedule=args.schedule)
+    r = run_layer_timed(cfg, B, args.steps, args.warmup, dev, rows=args.rows, schedule=args.schedule,
+                        slot_rows=args.slot_rows)
     summ = summarize(cfg, B, r)
     ab = algorithmic_bytes(cfg, r["ids"], r["E_slabs"])
     ms_per_step = r["wall_s"] / args.steps * 1e3
@@ -389,7 +393,7 @@ def main():
         "config": {"workload": describe(args.workload, cfg, B), "tokens": cfg["T"],
                    "experts": cfg["E"], "top_k": cfg["K"], "hidden": cfg["H"], "inter": cfg["I"],
                    "block_size_m": B, "shared_expert": bool(cfg.get("shared")), "rows": args.rows,
-                   "schedule": args.schedule},
+                   "schedule": args.schedule, "slot_rows": args.slot_rows},
         "layer": summ,
         "roofline": roofline,
     }
@@ -420,6 +424,13 @@ def main():
             b2 = b2 or c2["B"]
             r2 = run_layer_timed(c2, b2, 10, 3, dev)
             extra[name] = {"workload": describe(name, c2, b2), **summarize(c2, b2, r2)}
+            if not r2["layer"].top1:
+                # the same layer with bf16 slot rows between the FFN and the combine
+                del r2
+                r2 = run_layer_timed(c2, b2, 10, 3, dev, graph=False, slot_rows="bf16")
+                s16 = summarize(c2, b2, r2)
+                extra[name]["bf16_slot_rows"] = {"us_per_step": round(s16["us_per_step"], 1),
+                                                 "down_us": s16["us"]["down"], "combine_us": s16["us"]["combine"]}
             if name == "prefill_fp8_uniform":
                 # the pages' figure for this shape, on another machine: context only
                 extra[name]["pages_context"] = {"kernel": "aiter a8w8 fused MoE, block 32x512", "gpu": "MI300",

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 typedef enum {
     MOE_OK = 0,
@@ -201,7 +201,9 @@ moe_status_t moe_align_sort_noalloc(const int32_t *topk_ids, int32_t T, int32_t 
  *   a  = SiLU(x[t] . W13[e, 0:I]^T) * (x[t] . W13[e, I:2I]^T)     [I]
  *   y_slots[r] = a . W2[e]^T                                       [H], fp32
  * Rows holding the sentinel and blocks j >= P/B are skipped; rows of y_slots
- * whose slot is never placed are not written.
+ * whose slot is never placed are not written.  With p->y_dtype = MOE_BF16
+ * the fp32 row is stored rounded to nearest even bf16 (half the bytes the
+ * down GEMM writes and the combine reads; moe_combine_slots reads them).
  *   w_dtype = x_dtype = MOE_F32 : fp32 throughout (a kept in fp32)
  *   w_dtype = x_dtype = MOE_BF16: bf16 inputs, fp32 accumulation, a rounded
  *                                 to bf16 between the two GEMMs
@@ -221,7 +223,11 @@ moe_status_t moe_align_sort_noalloc(const int32_t *topk_ids, int32_t T, int32_t 
  *     and are scaled by the token's (or a's row's) scale only.
  * x device [T,H] (fp32 or bf16); w13 device [E,2I,H]; w2 device [E,H,I];
  * sorted_token_ids / expert_ids / num_tokens_post_padded as produced by
- * moe_align_sort with the same T,K,E,B; y_slots device fp32 [T*K,H] (out);
+ * moe_align_sort with the same T,K,E,B; y_slots device [T*K,H] (out) in
+ * p->y_dtype: MOE_F32 (0), or MOE_BF16 (bf16, fp8 and MXFP4 weights with
+ * MOE_ROWS_BY_TOKEN only; moe_grouped_ffn_train and moe_ffn_backward need
+ * MOE_F32, moe_grouped_ffn_top1 writes no y_slots and ignores it; anything
+ * else is MOE_ERR_UNSUPPORTED);
  * workspace device, at least moe_grouped_ffn_workspace_bytes(p), 256-byte
  * aligned, clobbered.
  * weight_layout MOE_LAYOUT_PACKED means w13 and w2 were rewritten by
@@ -270,13 +276,14 @@ typedef struct {
     int32_t row_layout;        /* moe_row_layout_t of x and y_slots */
     int32_t schedule;          /* moe_schedule_t */
     int32_t grad_dtype;        /* moe_dtype_t of moe_ffn_backward's dw13 and dw2: MOE_F32 (0) or MOE_BF16 */
+    int32_t y_dtype;           /* moe_dtype_t of y_slots: MOE_F32 (0) or MOE_BF16 */
 } moe_ffn_params_t;
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);
 moe_status_t moe_grouped_ffn(const moe_ffn_params_t *p, const void *x, const void *w13,
                              const void *w13_scale, const void *w2, const void *w2_scale,
                              const int32_t *sorted_token_ids, const int32_t *expert_ids,
-                             const int32_t *num_tokens_post_padded, float *y_slots,
+                             const int32_t *num_tokens_post_padded, void *y_slots,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -338,7 +345,7 @@ moe_status_t moe_prepack_block_scales(const moe_ffn_params_t *p, const void *w13
 moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t *p, const void *x, const void *w13,
                                       const void *w13_scale, const void *w2, const void *w2_scale,
                                       const int32_t *sorted_token_ids, const int32_t *expert_ids,
-                                      const int32_t *num_tokens_post_padded, float *y_slots,
+                                      const int32_t *num_tokens_post_padded, void *y_slots,
                                       void *workspace, size_t workspace_bytes, void *stream,
                                       void *const *events);
 
@@ -358,6 +365,16 @@ moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t *p, const void *x, 
 moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float *y_slots,
                          const float *topk_weights, const int32_t *topk_ids, int32_t out_dtype,
                          void *out, void *stream);
+/*
+ * moe_combine_slots: moe_combine with the slot rows in y_dtype.  MOE_F32 is
+ * moe_combine itself; MOE_BF16 reads the bf16 rows that moe_grouped_ffn
+ * writes with p->y_dtype = MOE_BF16, each value widened exactly to fp32
+ * before the same ascending-k fp32 sum.  Limits: H a multiple of 4 (MOE_F32)
+ * or of 8 (MOE_BF16); other y_dtype values are MOE_ERR_UNSUPPORTED.
+ */
+moe_status_t moe_combine_slots(int32_t T, int32_t K, int32_t E, int32_t H, const void *y_slots,
+                               int32_t y_dtype, const float *topk_weights, const int32_t *topk_ids,
+                               int32_t out_dtype, void *out, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Permute / unpermute (the dispatch-side data movement)                     */

@@ -41,13 +41,14 @@ class _FfnParams(ctypes.Structure):
                 ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("B", ctypes.c_int32),
                 ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
                 ("weight_layout", ctypes.c_int32), ("row_layout", ctypes.c_int32),
-                ("schedule", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("y_dtype", ctypes.c_int32)]
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
             "moe_align_sort_workspace_bytes", "moe_align_sort", "moe_grouped_ffn_workspace_bytes",
             "moe_grouped_ffn", "moe_grouped_ffn_profiled", "moe_grouped_ffn_top1", "moe_prepack_weights",
-            "moe_prepack_block_scales", "moe_combine", "moe_permute_rows", "moe_unpermute_combine",
+            "moe_prepack_block_scales", "moe_combine", "moe_combine_slots", "moe_permute_rows", "moe_unpermute_combine",
             "moe_unpermute_combine_backward", "moe_ffn_backward_workspace_bytes", "moe_ffn_backward",
             "moe_grouped_ffn_train", "moe_route_backward", "moe_align_sort_noalloc",
             "moe_align_sort_noalloc_scratch_bytes")
@@ -93,6 +94,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_prepack_block_scales.restype = i32
     lib.moe_combine.argtypes = [i32, i32, i32, i32, P, P, P, i32, P, P]
     lib.moe_combine.restype = i32
+    lib.moe_combine_slots.argtypes = [i32, i32, i32, i32, P, i32, P, P, i32, P, P]
+    lib.moe_combine_slots.restype = i32
     lib.moe_permute_rows.argtypes = [P, i32, i32, i32, i32, i64, P, P, P, P, P, P, P, P]
     lib.moe_permute_rows.restype = i32
     lib.moe_unpermute_combine.argtypes = [i32, i32, i32, P, P, P, i32, P, P]
@@ -265,11 +268,12 @@ MOE_SCHEDULE_TWO_LAUNCH, MOE_SCHEDULE_FUSED = 0, 1
 
 
 def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False, rows_sorted=False, fused=False,
-                grad_dtype=torch.float32):
+                grad_dtype=torch.float32, y_dtype=torch.float32):
     return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype],
                       MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_CANONICAL,
                       MOE_ROWS_SORTED if rows_sorted else MOE_ROWS_BY_TOKEN,
-                      MOE_SCHEDULE_FUSED if fused else MOE_SCHEDULE_TWO_LAUNCH, _DT[grad_dtype])
+                      MOE_SCHEDULE_FUSED if fused else MOE_SCHEDULE_TWO_LAUNCH, _DT[grad_dtype],
+                      _DT[y_dtype])
 
 
 def moe_prepack_weights(w13, w2, *, stream=None):
@@ -313,8 +317,10 @@ def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype, rows_sor
 
 def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, *, K, B,
                     w13_scale=None, w2_scale=None, y_slots=None, workspace=None, stream=None,
-                    stage_events=None, packed=False, T=None, fused=False):
-    """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots fp32 [T*K, H].
+                    stage_events=None, packed=False, T=None, fused=False, y_dtype=None):
+    """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots [T*K, H],
+    fp32, or bf16 (rounded to nearest even) with y_dtype=torch.bfloat16 or a
+    bf16 y_slots given (not with fp32 weights or rows in the sorted order).
 
     With ``T`` given and x of C = capacity rows, x is taken in the sorted row
     order (as moe_permute_rows writes it) and the result is [C, H] in that
@@ -348,10 +354,14 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
         ny = moe_align_sort_capacity(T, K, E, B)
         if Tx != ny:
             raise ValueError(f"x in the sorted row order must have {ny} rows, got {Tx}")
+    if y_dtype is None:
+        y_dtype = y_slots.dtype if y_slots is not None else torch.float32
+    if y_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("y_dtype must be float32 or bfloat16")
     if y_slots is None:
-        y_slots = torch.empty((ny, H), dtype=torch.float32, device=x.device)
-    _need(y_slots, torch.float32, "y_slots", ny * H)
-    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed, rows_sorted, fused)
+        y_slots = torch.empty((ny, H), dtype=y_dtype, device=x.device)
+    _need(y_slots, y_dtype, "y_slots", ny * H)
+    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed, rows_sorted, fused, y_dtype=y_dtype)
     need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype, rows_sorted, fused)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -411,19 +421,27 @@ def moe_grouped_ffn_top1(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_po
 # ------------------------------------------------------------------ combine --
 def moe_combine(y_slots, topk_weights, topk_ids, E, *, out_dtype=torch.bfloat16, out=None,
                 stream=None):
-    """out[t] = sum_k w[t,k] * y_slots[t*K+k] (ascending k, ids outside [0,E) skipped)."""
+    """out[t] = sum_k w[t,k] * y_slots[t*K+k] (ascending k, ids outside [0,E) skipped);
+    y_slots fp32, or bf16 (widened exactly to fp32; moe_combine_slots)."""
     lib = load_library()
     T, K = topk_ids.shape
     H = y_slots.shape[1]
-    _need(y_slots, torch.float32, "y_slots", T * K * H)
+    if y_slots.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("y_slots must be float32 or bfloat16")
+    _need(y_slots, y_slots.dtype, "y_slots", T * K * H)
     _need(topk_weights, torch.float32, "topk_weights", T * K)
     _need(topk_ids, torch.int32, "topk_ids", T * K)
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=y_slots.device)
     _need(out, out_dtype, "out", T * H)
-    _check("moe_combine", lib.moe_combine(T, K, E, H, _ptr(y_slots), _ptr(topk_weights),
-                                          _ptr(topk_ids), _DT[out_dtype], _ptr(out),
-                                          _stream(stream)))
+    if y_slots.dtype == torch.float32:
+        _check("moe_combine", lib.moe_combine(T, K, E, H, _ptr(y_slots), _ptr(topk_weights),
+                                              _ptr(topk_ids), _DT[out_dtype], _ptr(out),
+                                              _stream(stream)))
+    else:
+        _check("moe_combine_slots", lib.moe_combine_slots(
+            T, K, E, H, _ptr(y_slots), _DT[torch.bfloat16], _ptr(topk_weights), _ptr(topk_ids),
+            _DT[out_dtype], _ptr(out), _stream(stream)))
     return out
 
 
@@ -632,13 +650,16 @@ class MoELayer:
     train: the forward keeps the gate/up values (moe_grouped_ffn_train) and the
     backward reads them instead of recomputing.  grad_dtype: the weight
     gradients' type (float32, or bfloat16: rounded once, half the bytes).
+    slot_dtype: the type of the slot rows between the FFN and the combine
+    (float32, or bfloat16: half the bytes written and read back; rows by
+    token, not fp32 weights, no backward).
     """
 
     def __init__(self, w13, w2, *, T, K, B, score="softmax", n_group=1, topk_group=1,
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
                  w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None,
                  rows="by_token", schedule="two_launch", top1="auto", train=False,
-                 grad_dtype=torch.float32):
+                 grad_dtype=torch.float32, slot_dtype=torch.float32):
         dev = w13.device
         if packed is None:
             packed = w13.dtype != torch.float32
@@ -682,7 +703,12 @@ class MoELayer:
         self.ws_align = torch.zeros(max(ws_a, 1), dtype=torch.uint8, device=dev)   # zero before first use
         self.ws_ffn = torch.empty(max(ws_f, 1), dtype=torch.uint8, device=dev)
         ny = C if self.rows_sorted else T * self.KO
-        self.y_slots = torch.empty((ny, self.H), dtype=torch.float32, device=dev)
+        if slot_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("slot_dtype must be float32 or bfloat16")
+        if slot_dtype == torch.bfloat16 and (self.rows_sorted or w13.dtype == torch.float32 or train):
+            raise ValueError("bf16 slot rows need rows by token, matrix-core weights and no training")
+        self.slot_dtype = slot_dtype
+        self.y_slots = torch.empty((ny, self.H), dtype=slot_dtype, device=dev)
         if self.rows_sorted:
             self.x_perm = torch.empty((C, self.H), dtype=x_dtype, device=dev)
             self.row_of_slot = torch.empty(T * self.KO, dtype=torch.int32, device=dev)
@@ -766,6 +792,8 @@ class MoELayer:
         The backward reads the forward's slot rows; after a top-1 forward,
         which does not write them, they are recomputed first.  After a training
         forward it reads the kept gate/up values unless recompute is set."""
+        if self.slot_dtype != torch.float32:
+            raise ValueError("the backward reads fp32 slot rows: build the layer with slot_dtype float32")
         if not self._y_current:
             self.ffn(x)
         dx, dw13, dw2, dwk = moe_ffn_backward(

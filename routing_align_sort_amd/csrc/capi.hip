@@ -125,6 +125,9 @@ static moe_status_t ffn_check(const moe_ffn_params_t* p) {
     if (f32 && p->row_layout == MOE_ROWS_SORTED) return MOE_ERR_UNSUPPORTED;
     if (p->schedule != MOE_SCHEDULE_TWO_LAUNCH && p->schedule != MOE_SCHEDULE_FUSED) return MOE_ERR_INVALID_ARG;
     if (f32 && p->schedule == MOE_SCHEDULE_FUSED) return MOE_ERR_UNSUPPORTED;
+    // bf16 slot rows: the matrix-core paths, rows by slot
+    if (p->y_dtype != MOE_F32 && p->y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->y_dtype == MOE_BF16 && (f32 || p->row_layout != MOE_ROWS_BY_TOKEN)) return MOE_ERR_UNSUPPORTED;
     if (!f32) {
         // the matrix-core kernels address each GEMM's activation operand
         // (x, then the intermediate) with 32-bit byte offsets
@@ -183,7 +186,7 @@ struct Top1Out {
 static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
                                 const void* w13_scale, const void* w2, const void* w2_scale,
                                 const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                                const int32_t* num_tokens_post_padded, float* y_slots, const Top1Out& top1,
+                                const int32_t* num_tokens_post_padded, void* y_slots, const Top1Out& top1,
                                 float* save_gu, void* workspace, size_t workspace_bytes, void* stream,
                                 hipEvent_t const* ev) {
     const moe_status_t st = ffn_check(p);
@@ -204,7 +207,8 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     a.S = S; a.C = C;
     a.x = x; a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
     a.sorted_ids = sorted_token_ids; a.expert_ids = expert_ids; a.post_padded = num_tokens_post_padded;
-    a.y_slots = y_slots;
+    a.y_slots = static_cast<float*>(y_slots);
+    a.y_bf16 = p->y_dtype == MOE_BF16 && !top1.out;
     a.packed = p->weight_layout == MOE_LAYOUT_PACKED;
     a.rows_sorted = p->row_layout == MOE_ROWS_SORTED;
     a.fused = p->schedule == MOE_SCHEDULE_FUSED;
@@ -221,7 +225,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
 moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const void* w13,
                              const void* w13_scale, const void* w2, const void* w2_scale,
                              const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                             const int32_t* num_tokens_post_padded, float* y_slots, void* workspace,
+                             const int32_t* num_tokens_post_padded, void* y_slots, void* workspace,
                              size_t workspace_bytes, void* stream) {
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, y_slots, Top1Out{}, nullptr, workspace, workspace_bytes, stream,
@@ -235,7 +239,7 @@ moe_status_t moe_grouped_ffn_train(const moe_ffn_params_t* p, const void* x, con
     const moe_status_t st = ffn_check(p);
     if (st != MOE_OK) return st;
     if (p->w_dtype != MOE_BF16 || p->x_dtype != MOE_BF16 || p->row_layout != MOE_ROWS_BY_TOKEN ||
-        p->schedule != MOE_SCHEDULE_TWO_LAUNCH)
+        p->schedule != MOE_SCHEDULE_TWO_LAUNCH || p->y_dtype != MOE_F32)
         return MOE_ERR_UNSUPPORTED;
     if ((int64_t)p->T * p->K == 0) return MOE_OK;
     if (!gate_up) return MOE_ERR_INVALID_ARG;
@@ -265,7 +269,7 @@ moe_status_t moe_grouped_ffn_top1(const moe_ffn_params_t* p, const void* x, cons
 moe_status_t moe_grouped_ffn_profiled(const moe_ffn_params_t* p, const void* x, const void* w13,
                                       const void* w13_scale, const void* w2, const void* w2_scale,
                                       const int32_t* sorted_token_ids, const int32_t* expert_ids,
-                                      const int32_t* num_tokens_post_padded, float* y_slots,
+                                      const int32_t* num_tokens_post_padded, void* y_slots,
                                       void* workspace, size_t workspace_bytes, void* stream,
                                       void* const* events) {
     if (!events) return MOE_ERR_INVALID_ARG;
@@ -282,6 +286,7 @@ static moe_status_t bwd_check(const moe_ffn_params_t* p) {
         return MOE_ERR_INVALID_ARG;
     if (p->w_dtype != MOE_BF16 || p->x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->grad_dtype != MOE_F32 && p->grad_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->y_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;     // the forward's fp32 slot rows are read
     if (p->weight_layout != MOE_LAYOUT_CANONICAL || p->row_layout != MOE_ROWS_BY_TOKEN ||
         p->schedule != MOE_SCHEDULE_TWO_LAUNCH)
         return MOE_ERR_UNSUPPORTED;
@@ -401,6 +406,22 @@ moe_status_t moe_combine(int32_t T, int32_t K, int32_t E, int32_t H, const float
     if (!y_slots || !topk_weights || !topk_ids || !out) return MOE_ERR_INVALID_ARG;
     return from_hip(launch_combine(T, K, E, H, y_slots, topk_weights, topk_ids, out_dtype == MOE_BF16, out,
                                    as_stream(stream)));
+}
+
+moe_status_t moe_combine_slots(int32_t T, int32_t K, int32_t E, int32_t H, const void* y_slots, int32_t y_dtype,
+                               const float* topk_weights, const int32_t* topk_ids, int32_t out_dtype, void* out,
+                               void* stream) {
+    if (y_dtype == MOE_F32)
+        return moe_combine(T, K, E, H, static_cast<const float*>(y_slots), topk_weights, topk_ids, out_dtype, out,
+                           stream);
+    if (y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (T < 0 || K < 1 || E < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+    if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (H % 8) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!y_slots || !topk_weights || !topk_ids || !out) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_combine_bf16_slots(T, K, E, H, static_cast<const uint16_t*>(y_slots), topk_weights,
+                                              topk_ids, out_dtype == MOE_BF16, out, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -721,6 +721,11 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
                                 ((float*)a.top1_out)[off + 32 * j] = o;
                             }
                         }
+                    } else if (a.y_bf16) {
+                        // half the bytes for the combine to read back
+                        uint16_t* dst = (uint16_t*)a.y_slots + (int64_t)slot * H + n0 + r32;
+#pragma unroll
+                        for (int j = 0; j < NS; ++j) dst[32 * j] = f32_to_bf16_bits(y[j]);
                     } else {
                         const int64_t yrow = a.rows_sorted ? (int64_t)mb * BM + m : (int64_t)slot;
                         float* dst = a.y_slots + yrow * H + n0 + r32;

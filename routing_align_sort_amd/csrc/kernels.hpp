@@ -57,6 +57,7 @@ struct FfnArgs {
     const int32_t* expert_ids;
     const int32_t* post_padded;
     float* y_slots;            // [S,H] by slot, or [C,H] in the sorted row order
+    int y_bf16;                // y_slots holds bf16 rows (rounded to nearest even), rows by slot
     int packed;                // weights in the layout written by launch_prepack
     int rows_sorted;           // x is [C,H] in the sorted row order, y written in that order
     int fused;                 // both GEMMs in one persistent launch
@@ -150,6 +151,9 @@ hipError_t launch_route_backward(const RouteArgs& a, const float* d_w, float* d_
 // ----------------------------------------------------------------- combine --
 hipError_t launch_combine(int T, int K, int E, int H, const float* y_slots, const float* w,
                           const int32_t* ids, int out_bf16, void* out, hipStream_t stream);
+// The same combine over bf16 slot rows (each widened exactly to fp32).
+hipError_t launch_combine_bf16_slots(int T, int K, int E, int H, const uint16_t* y_slots, const float* w,
+                                     const int32_t* ids, int out_bf16, void* out, hipStream_t stream);
 hipError_t launch_unpermute_combine(int T, int K, int H, const float* y_perm, const float* w,
                                     const int32_t* row_of_slot, int out_bf16, void* out, hipStream_t stream);
 // Gradient of the unpermute-combine in the permuted layout: d_y_perm rows

@@ -122,7 +122,7 @@ def compare_slots(y_rows, toks, ids, yref, dtype, label):
     K = ids.shape[1]
     slots = (np.asarray(toks)[:, None] * K + np.arange(K)[None]).ravel()
     valid = ids[toks].ravel() >= 0
-    got = y_rows[torch.as_tensor(slots[valid], device=y_rows.device)].cpu().numpy()
+    got = y_rows[torch.as_tensor(slots[valid], device=y_rows.device)].float().cpu().numpy()
     err = rel_err(got, yref[valid])
     say(f"{label}: y_slots rel err {err:.3e} over {int(valid.sum())} slots (tol {TOL[dtype]})")
     assert err <= TOL[dtype], (label, err)
@@ -138,9 +138,10 @@ def route_oracle(cfg, L, K=None):
     return ids, w
 
 
-def make_gpu_layer(cfg, L, B=None, packed=None, top1="auto"):
+def make_gpu_layer(cfg, L, B=None, packed=None, top1="auto", slot_dtype=torch.float32, schedule="two_launch"):
     w13, w2, s13, s2 = as_library_weights(L)
     return moe.MoELayer(w13, w2, T=cfg["T"], K=cfg["K"], B=B or cfg["B"], packed=packed, top1=top1,
+                        slot_dtype=slot_dtype, schedule=schedule,
                         score=cfg["score"], n_group=cfg["n_group"], topk_group=cfg["topk_group"],
                         renormalize=cfg["renormalize"], shared=bool(cfg.get("shared")),
                         w13_scale=s13, w2_scale=s2,

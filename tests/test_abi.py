@@ -30,14 +30,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 8
+    assert moe.abi_version() == 9
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -296,3 +296,30 @@ def test_product_sources_do_not_reference_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
                 assert "moe_oracle" not in src, f
+
+
+def test_bf16_slot_rows_are_checked_on_the_host(lib):
+    # y_dtype: fp32 or bf16; bf16 only with matrix-core weights and rows by
+    # slot; the training forward and the backward read fp32 slot rows
+    P = ctypes.c_void_p
+    p = moe._FfnParams(64, 2, 8, 256, 256, 16, moe.MOE_BF16, moe.MOE_BF16, 0, moe.MOE_ROWS_BY_TOKEN, 0, 0,
+                       moe.MOE_BF16)
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(p)) > 0
+    for field, value in (("y_dtype", 7), ("y_dtype", moe.MOE_FP8_E4M3), ("row_layout", moe.MOE_ROWS_SORTED)):
+        q = moe._FfnParams.from_buffer_copy(p)
+        setattr(q, field, value)
+        assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(q)) == -1, (field, value)
+    q = moe._FfnParams.from_buffer_copy(p)
+    q.w_dtype = q.x_dtype = moe.MOE_F32
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(q)) == -1
+    assert lib.moe_ffn_backward_workspace_bytes(ctypes.byref(p)) == -1
+    assert lib.moe_grouped_ffn_train(ctypes.byref(p), *([P(8)] * 8), P(8), 1 << 30, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    # the combine of bf16 slot rows: H a multiple of 8, known dtypes only
+    cs = lib.moe_combine_slots
+    assert cs(4, 2, 8, 12, P(8), moe.MOE_BF16, P(8), P(8), moe.MOE_BF16, P(8), None) == moe.MOE_ERR_UNSUPPORTED
+    assert cs(4, 2, 8, 16, P(8), moe.MOE_FP8_E4M3, P(8), P(8), moe.MOE_BF16, P(8), None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert cs(4, 2, 8, 16, None, moe.MOE_BF16, P(8), P(8), moe.MOE_BF16, P(8), None) == moe.MOE_ERR_INVALID_ARG
+    assert cs(0, 2, 8, 16, None, moe.MOE_BF16, None, None, moe.MOE_BF16, None, None) == moe.MOE_OK
+    assert cs(4, 2, 8, 12, P(8), moe.MOE_F32, P(8), P(8), 5, P(8), None) == moe.MOE_ERR_UNSUPPORTED
