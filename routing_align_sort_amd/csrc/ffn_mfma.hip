@@ -687,6 +687,37 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
 #pragma unroll
     for (int j = 0; j < NS; ++j) sc[j] = F::kChanScale ? ((const float*)a.w2_scale)[(int64_t)e * H + n0 + 32 * j + r32]
                                                        : 1.f;
+    if (a.y_bf16) {
+        // bf16 slot rows, two columns per 4-byte store: accumulator registers
+        // i and i+1 hold rows r and r+1 of column c; neighbouring lanes swap
+        // one value each, so an even lane stores (r, c..c+1) and an odd lane
+        // (r+1, c-1..c) -- half the store instructions of one value per lane
+        const bool odd = lane & 1;
+#pragma unroll
+        for (int mt = 0; mt < TL::MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) {
+                const int m0 = mt * 32 + acc_row(i, lane);
+                const int m = odd ? m0 + 1 : m0;                  // the row this lane stores
+                const float rs0 = F::kQuantA && m0 < BM ? rowscale[m0] : 1.f;
+                const float rs1 = F::kQuantA && m0 + 1 < BM ? rowscale[m0 + 1] : 1.f;
+                const int slot = m < BM ? slots[m] : a.S;
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    float v0 = acc[mt][j][i], v1 = acc[mt][j][i + 1];
+                    if (F::kQuantA) {
+                        v0 = v0 * rs0 * sc[j];
+                        v1 = v1 * rs1 * sc[j];
+                    }
+                    const float x = __shfl_xor(odd ? v0 : v1, 1, kWave);
+                    const uint32_t lo = f32_to_bf16_bits(odd ? x : v0), hi = f32_to_bf16_bits(odd ? v1 : x);
+                    if (slot < a.S)
+                        *(uint32_t*)((uint16_t*)a.y_slots + (int64_t)slot * H + n0 + 32 * j + (r32 & ~1)) =
+                            lo | (hi << 16);
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int mt = 0; mt < TL::MT; ++mt)
 #pragma unroll
@@ -721,11 +752,6 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
                                 ((float*)a.top1_out)[off + 32 * j] = o;
                             }
                         }
-                    } else if (a.y_bf16) {
-                        // half the bytes for the combine to read back
-                        uint16_t* dst = (uint16_t*)a.y_slots + (int64_t)slot * H + n0 + r32;
-#pragma unroll
-                        for (int j = 0; j < NS; ++j) dst[32 * j] = f32_to_bf16_bits(y[j]);
                     } else {
                         const int64_t yrow = a.rows_sorted ? (int64_t)mb * BM + m : (int64_t)slot;
                         float* dst = a.y_slots + yrow * H + n0 + r32;
