@@ -94,6 +94,14 @@ constexpr int kPackScaleStepBytes = 4 * kPackScaleWaveBytes;
 #ifndef MOE_FFN_PIN_LOADS
 #define MOE_FFN_PIN_LOADS 1
 #endif
+// fp32 slot rows stored two columns per lane (8-byte stores) as bf16 ones are
+#ifndef MOE_FFN_PAIR_F32
+#define MOE_FFN_PAIR_F32 1
+#endif
+// the same for the top-1 call's output rows
+#ifndef MOE_FFN_PAIR_TOP1
+#define MOE_FFN_PAIR_TOP1 1
+#endif
 
 // Cache policy of the weight loads.  A tile whose expert has a single M block
 // in the launch is the only reader of its weights: streaming (non-temporal)
@@ -687,11 +695,13 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
 #pragma unroll
     for (int j = 0; j < NS; ++j) sc[j] = F::kChanScale ? ((const float*)a.w2_scale)[(int64_t)e * H + n0 + 32 * j + r32]
                                                        : 1.f;
-    if (a.y_bf16) {
-        // bf16 slot rows, two columns per 4-byte store: accumulator registers
-        // i and i+1 hold rows r and r+1 of column c; neighbouring lanes swap
-        // one value each, so an even lane stores (r, c..c+1) and an odd lane
-        // (r+1, c-1..c) -- half the store instructions of one value per lane
+    if (a.y_bf16 || (a.top1_out ? MOE_FFN_PAIR_TOP1 : MOE_FFN_PAIR_F32)) {
+        // two columns per store: accumulator registers i and i+1 hold rows r
+        // and r+1 of column c; neighbouring lanes swap one value each, so an
+        // even lane stores (r, c..c+1) and an odd lane (r+1, c-1..c) -- half
+        // the store instructions of one value per lane (bf16: 4 bytes, fp32:
+        // 8 bytes).  Top-1: the values are first weighted as the combine
+        // weights them, 0 + w * y in fp32.
         const bool odd = lane & 1;
 #pragma unroll
         for (int mt = 0; mt < TL::MT; ++mt)
@@ -702,6 +712,8 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
                 const float rs0 = F::kQuantA && m0 < BM ? rowscale[m0] : 1.f;
                 const float rs1 = F::kQuantA && m0 + 1 < BM ? rowscale[m0 + 1] : 1.f;
                 const int slot = m < BM ? slots[m] : a.S;
+                const float wt0 = a.top1_out && m0 < BM ? sm.roww[m0] : 0.f;
+                const float wt1 = a.top1_out && m0 + 1 < BM ? sm.roww[m0 + 1] : 0.f;
 #pragma unroll
                 for (int j = 0; j < NS; ++j) {
                     float v0 = acc[mt][j][i], v1 = acc[mt][j][i + 1];
@@ -709,11 +721,34 @@ __device__ __forceinline__ void stage2_tile(const FfnArgs& a, const uint8_t* __r
                         v0 = v0 * rs0 * sc[j];
                         v1 = v1 * rs1 * sc[j];
                     }
+                    if (a.top1_out) {
+                        float o0 = 0.f, o1 = 0.f;
+                        o0 += wt0 * v0;
+                        o1 += wt1 * v1;
+                        v0 = o0;
+                        v1 = o1;
+                    }
                     const float x = __shfl_xor(odd ? v0 : v1, 1, kWave);
-                    const uint32_t lo = f32_to_bf16_bits(odd ? x : v0), hi = f32_to_bf16_bits(odd ? v1 : x);
-                    if (slot < a.S)
-                        *(uint32_t*)((uint16_t*)a.y_slots + (int64_t)slot * H + n0 + 32 * j + (r32 & ~1)) =
-                            lo | (hi << 16);
+                    const float lo = odd ? x : v0, hi = odd ? v1 : x;
+                    if (slot < a.S) {
+                        const int64_t off = (int64_t)slot * H + n0 + 32 * j + (r32 & ~1);
+                        if (a.top1_out) {
+                            // the layer's output is not read again here:
+                            // non-temporal bf16 stores
+                            if (a.top1_bf16)
+                                __builtin_nontemporal_store(
+                                    (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16),
+                                    (uint32_t*)((uint16_t*)a.top1_out + off));
+                            else
+                                *(float2*)((float*)a.top1_out + off) = make_float2(lo, hi);
+                        } else if (a.y_bf16) {
+                            *(uint32_t*)((uint16_t*)a.y_slots + off) =
+                                (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+                        } else {
+                            const int64_t yrow = a.rows_sorted ? (int64_t)mb * BM + m : (int64_t)slot;
+                            *(float2*)(a.y_slots + yrow * H + n0 + 32 * j + (r32 & ~1)) = make_float2(lo, hi);
+                        }
+                    }
                 }
             }
         return;
