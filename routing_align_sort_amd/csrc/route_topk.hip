@@ -19,28 +19,24 @@ namespace moe {
 constexpr int kRouteWaves = 4;
 constexpr int kRouteMaxPerLane = kRouteMaxExperts / kWave;   // 16
 
-struct Cand {
-    float key;
-    int e;          // INT32_MAX = none
-    double s;
-};
-
-__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-    if (a.e == INT32_MAX) return false;
-    if (b.e == INT32_MAX) return true;
-    return a.key > b.key || (a.key == b.key && a.e < b.e);
+// A candidate as one ordered 64-bit word: the fp32 key mapped to an unsigned
+// integer of the same order in the high half, and ~e in the low half, so the
+// largest word is the largest key and, among equal keys, the lowest id.
+// 0 = no candidate (every real word is larger).
+__device__ __forceinline__ uint64_t cand_word(float key, int e) {
+    const uint32_t b = __float_as_uint(key);
+    const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)k << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
+__device__ __forceinline__ int cand_id(uint64_t w) { return (int)(0xFFFFFFFFu - (uint32_t)w); }
 
-__device__ __forceinline__ Cand wave_best(Cand c) {
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        Cand d;
-        d.key = __shfl_xor(c.key, o, kWave);
-        d.e = __shfl_xor(c.e, o, kWave);
-        d.s = __shfl_xor(c.s, o, kWave);
-        if (better(d, c)) c = d;
+        const uint64_t d = __shfl_xor(v, o, kWave);
+        v = d > v ? d : v;
     }
-    return c;
+    return v;
 }
 
 // JT: experts per lane the loops are unrolled for (a power of two with
@@ -101,34 +97,56 @@ route_topk_kernel(RouteArgs a) {
     // 3. group limit
     if (a.n_group > 1) {
         const int gsize = E / a.n_group;
+        float gs = -INFINITY;                       // lane g (< n_group): group g's score
+        if ((gsize & (gsize - 1)) == 0 && gsize <= kWave) {
+            // a group is an aligned run of gsize lanes of one register: its
+            // two largest keys by a butterfly over the run, then each lane g
+            // fetches its group's sum from the run's first lane
+            float gsum[JT];
 #pragma unroll
-        for (int j = 0; j < JT; ++j) {
-            const int e = lane + j * kWave;
-            if (e < E) keys_lds[w][e] = key[j];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lane g scores group g: the sum of its two largest keys
-        Cand g{-INFINITY, INT32_MAX, 0.0};
-        if (lane < a.n_group) {
-            float b1 = -INFINITY, b2 = -INFINITY;
-            int n = 0;
-            for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) {
-                const float k = keys_lds[w][e];
-                if (n == 0 || k > b1) { b2 = b1; b1 = k; }
-                else if (n == 1 || k > b2) { b2 = k; }
-                ++n;
+            for (int j = 0; j < JT; ++j) {
+                float b1 = key[j], b2 = -INFINITY;
+                for (int o = gsize >> 1; o > 0; o >>= 1) {
+                    const float c1 = __shfl_xor(b1, o, kWave), c2 = __shfl_xor(b2, o, kWave);
+                    b2 = fmaxf(fminf(b1, c1), fmaxf(b2, c2));
+                    b1 = fmaxf(b1, c1);
+                }
+                gsum[j] = gsize >= 2 ? b1 + b2 : b1;
             }
-            g.key = (gsize >= 2) ? b1 + b2 : b1;
-            g.e = lane;
+            const int first = lane * gsize;          // group `lane`'s first expert
+#pragma unroll
+            for (int j = 0; j < JT; ++j) {
+                const float v = __shfl(gsum[j], first & (kWave - 1), kWave);
+                if (lane < a.n_group && (first >> 6) == j) gs = v;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < JT; ++j) {
+                const int e = lane + j * kWave;
+                if (e < E) keys_lds[w][e] = key[j];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // lane g scores group g: the sum of its two largest keys
+            if (lane < a.n_group) {
+                float b1 = -INFINITY, b2 = -INFINITY;
+                int n = 0;
+                for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) {
+                    const float k = keys_lds[w][e];
+                    if (n == 0 || k > b1) { b2 = b1; b1 = k; }
+                    else if (n == 1 || k > b2) { b2 = k; }
+                    ++n;
+                }
+                gs = (gsize >= 2) ? b1 + b2 : b1;
+            }
         }
+        // the topk_group best groups (higher score, lower index on ties)
+        uint64_t gw = lane < a.n_group ? cand_word(gs, lane) : 0;
         bool keep = false;
         for (int r = 0; r < a.topk_group; ++r) {
-            Cand c = g;
-            if (keep) c.e = INT32_MAX;
-            const Cand best = wave_best(c);
-            if (best.e == lane) keep = true;
+            const uint64_t best = wave_max_u64(keep ? 0 : gw);
+            if (cand_id(best) == lane) keep = true;
         }
         const uint64_t kept = ballot(keep);
         uint32_t al = 0;
@@ -139,22 +157,28 @@ route_topk_kernel(RouteArgs a) {
         }
         allowed = al;
     }
-    // 4. top-K, one wave-wide argmax per pick (descending order, lower id on ties)
+    // 4. top-K, one wave-wide maximum of candidate words per pick (descending
+    //    order, lower id on ties); the winner's double score comes from its lane
     double my_s = 0.0, sum = 0.0;
     int my_e = 0;
     for (int k = 0; k < a.K; ++k) {
-        Cand c{-INFINITY, INT32_MAX, 0.0};
+        uint64_t c = 0;
 #pragma unroll
-        for (int j = 0; j < JT; ++j) {
+        for (int j = 0; j < JT; ++j)
             if ((allowed >> j) & 1u) {
-                const Cand d{key[j], lane + j * kWave, sc[j]};
-                if (better(d, c)) c = d;
+                const uint64_t d = cand_word(key[j], lane + j * kWave);
+                c = d > c ? d : c;
             }
-        }
-        const Cand best = wave_best(c);
-        if ((best.e & (kWave - 1)) == lane) allowed &= ~(1u << (best.e / kWave));
-        sum += best.s;                            // ascending k, as the definition sums
-        if (lane == k) { my_s = best.s; my_e = best.e; }
+        const int be = cand_id(wave_max_u64(c));
+        const int bj = be / kWave;
+        double s_b = 0.0;
+#pragma unroll
+        for (int j = 0; j < JT; ++j)
+            if (j == bj) s_b = sc[j];
+        s_b = __shfl(s_b, be & (kWave - 1), kWave);
+        if ((be & (kWave - 1)) == lane) allowed &= ~(1u << bj);
+        sum += s_b;                               // ascending k, as the definition sums
+        if (lane == k) { my_s = s_b; my_e = be; }
     }
     // 5. weights
     const int KO = a.K + (a.append_shared ? 1 : 0);
