@@ -57,7 +57,10 @@ def test_route_prefill_assignments_and_shared():
 @pytest.mark.parametrize("E,K,n_group,topk_group,score", [
     (8, 1, 1, 1, "softmax"), (16, 4, 4, 2, "sigmoid"), (64, 6, 1, 1, "sigmoid"),
     (256, 8, 8, 4, "sigmoid"), (256, 8, 1, 1, "softmax"), (1024, 16, 16, 3, "sigmoid"),
-    (160, 6, 1, 1, "softmax"), (64, 64, 1, 1, "softmax"), (96, 5, 32, 4, "sigmoid")])
+    (160, 6, 1, 1, "softmax"), (64, 64, 1, 1, "softmax"), (96, 5, 32, 4, "sigmoid"),
+    # group sizes on both paths of the group scores: 128 lanes (two registers,
+    # a scan), 2 lanes with E not a multiple of 64, 1 expert per group
+    (1024, 8, 8, 2, "sigmoid"), (40, 3, 20, 5, "sigmoid"), (8, 2, 8, 3, "sigmoid")])
 def test_route_random(E, K, n_group, topk_group, score):
     rng = np.random.default_rng(E * 100 + K)
     T = 517
@@ -77,3 +80,23 @@ def test_route_ties_choose_lower_ids():
     gid, _ = compare(logits, 4, score="softmax")
     assert gid[0].tolist() == [0, 1, 2, 3] and gid[3].tolist() == [20, 0, 1, 2]
     assert gid[4].tolist() == [5, 6, 7, 8]
+
+
+@pytest.mark.parametrize("gsize", [4, 32, 24])
+def test_route_group_score_ties_choose_lower_groups(gsize):
+    # every group scores the same, so the kept groups are the lowest indices;
+    # inside them the keys decide (gsize 24 takes the scanning path)
+    n_group = 8
+    E = gsize * n_group
+    T = 64
+    rng = np.random.default_rng(gsize)
+    logits = np.zeros((T, E), np.float32)
+    for t in range(T):
+        for g in range(n_group):
+            # the same two largest keys in every group, different smaller ones
+            base = g * gsize
+            logits[t, base + rng.integers(gsize)] = 3.0
+            rest = [i for i in range(base, base + gsize) if logits[t, i] == 0.0]
+            logits[t, rest[rng.integers(len(rest))]] = 2.0
+    gid, _ = compare(logits, 4, None, score="sigmoid", n_group=n_group, topk_group=3, renormalize=True)
+    assert (gid // gsize < 3).all(), "groups 0..2 must be kept on equal scores"
