@@ -869,6 +869,7 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 }
 
 constexpr int kQuantThreads = 256;
+constexpr int kQuantCache = 4;          // 16-byte chunks of a row a thread keeps in registers
 
 __device__ __forceinline__ float block_max(float v, float* lds4) {
     v = wave_max_f32(v);
@@ -891,21 +892,35 @@ quant_tokens_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__
     for (int64_t r = (int64_t)t * kQuantThreads + tid; r < C; r += (int64_t)gridDim.x * kQuantThreads)
         amax_rows[r] = 0u;
     const uint16_t* row = x + (int64_t)t * H;
+    // rows up to kQuantCache * 8 * kQuantThreads elements stay in registers
+    // between the amax and the encoding (one read of the row); longer rows
+    // are read twice
+    uint4 cache[kQuantCache];
+    const bool cached = H <= kQuantCache * 8 * kQuantThreads;
     float m = 0.f;
-    for (int h = tid * 8; h < H; h += kQuantThreads * 8) {
-        const uint4 v = *(const uint4*)(row + h);
+    auto absmax8 = [&](const uint4 v) {
         const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(wv[j] & 0xFFFF))));
             m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(wv[j] >> 16))));
         }
+    };
+    if (cached) {
+#pragma unroll
+        for (int c = 0; c < kQuantCache; ++c) {
+            const int h = (tid + c * kQuantThreads) * 8;
+            cache[c] = h < H ? *(const uint4*)(row + h) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int c = 0; c < kQuantCache; ++c) absmax8(cache[c]);
+    } else {
+        for (int h = tid * 8; h < H; h += kQuantThreads * 8) absmax8(*(const uint4*)(row + h));
     }
     m = block_max(m, red);
     const float inv = (m > 0.f) ? 448.0f / m : 0.f;
     if (tid == 0) sx[t] = (m > 0.f) ? m / 448.0f : 1.0f;
-    for (int h = tid * 8; h < H; h += kQuantThreads * 8) {
-        const uint4 v = *(const uint4*)(row + h);
+    auto encode8 = [&](const uint4 v, int h) {
         const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
         float f[8];
 #pragma unroll
@@ -920,6 +935,15 @@ quant_tokens_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__
         // faster when this kernel leaves no dirty lines behind (8% at 64
         // tokens per expert)
         __builtin_nontemporal_store(u32x2_t{o.x, o.y}, (u32x2_t*)(xq + (int64_t)t * H + h));
+    };
+    if (cached) {
+#pragma unroll
+        for (int c = 0; c < kQuantCache; ++c) {
+            const int h = (tid + c * kQuantThreads) * 8;
+            if (h < H) encode8(cache[c], h);
+        }
+    } else {
+        for (int h = tid * 8; h < H; h += kQuantThreads * 8) encode8(*(const uint4*)(row + h), h);
     }
 }
 
