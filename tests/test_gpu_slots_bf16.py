@@ -112,3 +112,26 @@ def test_bf16_slot_rows_512_per_expert(name):
     compare_slots(l16.y_slots, toks, ids, yref, cfg["dtype"], f"{name} B=128 bf16 slots")
     del L, l16
     torch.cuda.empty_cache()
+
+
+def test_bf16_slot_rows_with_skipped_ids():
+    # slots whose id is outside [0,E) (experts of another GPU, in an
+    # expert-parallel dispatch) are neither written nor summed
+    dev = device()
+    cfg = ms.scaled("prefill_fp8", T=300, H=512, I=256, E=8)
+    L = ms.make_layer(cfg, device=dev)
+    layers = []
+    for slot_dtype in (torch.float32, torch.bfloat16):
+        layer = make_gpu_layer(cfg, L, 64, top1=False, slot_dtype=slot_dtype)
+        layer.route(L["logits"], L["bias"])
+        ids = layer.topk_ids.cpu().numpy()
+        rng = np.random.default_rng(3)
+        drop = rng.random(ids.shape) < 0.4
+        ids[drop] = np.where(rng.random(ids.shape) < 0.5, -1, layer.E_slabs + 3)[drop]
+        layer.topk_ids.copy_(torch.from_numpy(ids))
+        layer.align()
+        layer.ffn(L["x"])
+        layer.combine()
+        torch.cuda.synchronize()
+        layers.append(layer)
+    check_rounding_and_combine(layers[0], layers[1], "prefill fp8 small, 40% skipped ids")
