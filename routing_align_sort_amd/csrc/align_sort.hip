@@ -228,7 +228,14 @@ constexpr int64_t kAlignMergeMaxInts = 16384;   // a [G,E] matrix up to this is 
 // Up to this many workgroups the merge uses tagged count words instead of a
 // grid barrier: measured at 1024 tokens x 8 (8 workgroups) 7.3 against
 // 8.6 us; at 16384 x 8 (64 workgroups, more polling) 10.8 against 9.9.
-constexpr int kAlignTaggedMaxWg = 16;
+#ifndef MOE_ALIGN_TAGGED_MAX_WG
+#define MOE_ALIGN_TAGGED_MAX_WG 16
+#endif
+constexpr int kAlignTaggedMaxWg = MOE_ALIGN_TAGGED_MAX_WG;
+// Slots per thread of the multi-workgroup path (grown beyond 256 workgroups).
+#ifndef MOE_ALIGN_MIN_R
+#define MOE_ALIGN_MIN_R 2
+#endif
 
 // ------------------------------------------------------------ stable ranks --
 // ev[j] (an expert id, or -1) becomes e | p << 16, p the position of slot j
@@ -640,7 +647,7 @@ AlignPlan align_plan(int64_t S, int E) {
         p.G = 1;
     } else {
         // two slots per thread, or one when eight one-slot chunks cover S
-        r = S <= (int64_t)kNumXcd * kAlignThreads ? 1 : 2;
+        r = S <= (int64_t)kNumXcd * kAlignThreads ? 1 : MOE_ALIGN_MIN_R;
         while (r < rmax && (S + (int64_t)kAlignThreads * r - 1) / ((int64_t)kAlignThreads * r) > kAlignMaxWg) r <<= 1;
         const int64_t g = (S + (int64_t)kAlignThreads * r - 1) / ((int64_t)kAlignThreads * r);
         p.G = (int)((g + kNumXcd - 1) / kNumXcd * kNumXcd);    // whole rounds of the 8 XCDs

@@ -89,6 +89,11 @@ constexpr int kPackScaleStepBytes = 4 * kPackScaleWaveBytes;
 #ifndef MOE_FFN_GROUP_M
 #define MOE_FFN_GROUP_M 8
 #endif
+// 1: a gate/up tile whose last 32-row subtiles are all padding is computed
+// as the smaller tile of its live rows (tiles of 64 and 128 rows).
+#ifndef MOE_FFN_LIVE_TILES
+#define MOE_FFN_LIVE_TILES 1
+#endif
 
 
 #ifndef MOE_FFN_PIN_LOADS
@@ -502,6 +507,40 @@ constexpr int ffn_la() {
     return full ? PF + 1 : 1;
 }
 
+// Live-row gate/up tiles (MOE_FFN_LIVE_TILES): the padding of an M block is a suffix
+// (an expert's slots come first in its run), so a block of BM rows whose
+// last 32-row subtiles are all padding is computed as the smaller tile of
+// its live subtiles, with that tile's weight prefetch depth: the registers
+// of the accumulators it does not need hold more weight K-steps in flight.
+// Such blocks are the lightly loaded experts', whose weights stream from
+// HBM once.
+template <int BM>
+constexpr bool ffn_live_tiles() {
+    return MOE_FFN_LIVE_TILES && (BM == 64 || BM == 128);
+}
+// Rows of the standard tile whose prefetch tuning a live tile of TB rows takes.
+template <int TB>
+constexpr int live_tune_rows() {
+    return TB <= 64 ? 64 : 128;
+}
+template <int kW, int TB>
+constexpr int live_pf() {
+    return ffn_pf<kW, live_tune_rows<TB>()>();
+}
+template <int kW, int BM, int TB, int PF>
+constexpr int live_la() {
+    return ffn_la<kW, (TB < BM ? live_tune_rows<TB>() : BM), PF>();
+}
+// Subtiles of the block whose first row is a row of the block (live(m):
+// row m holds a slot; read after the barrier that staged the rows).
+template <int BM, typename Live>
+__device__ __forceinline__ int live_subtiles(Live live) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < Tile<BM>::MT; ++j) n += live(32 * j) ? 1 : 0;
+    return n;
+}
+
 // LDS of one workgroup: the activation tile and the per-row tables.
 template <int BM>
 struct FfnSmem {
@@ -527,28 +566,20 @@ __device__ __forceinline__ const uint8_t* gate_up_lane_ptr(const uint8_t* slab, 
                                         lane);
 }
 
-// One gate/up tile: M block mb, intermediate columns [nt*64*NS, (nt+1)*64*NS).
-template <int kW, bool kPacked, int BM, int PF, int NS = 2>
-__device__ __forceinline__ void stage1_tile(const FfnArgs& a, uint16_t* __restrict__ h_out, const Fp8Ws& q,
+// The gate/up tile after its rows are staged: TB rows of the MFMA tile
+// (TB < BM: the rows of the block past TB are padding and are not computed;
+// the intermediate's rows past TB are left as they are).
+template <int kW, bool kPacked, int BM, int TB, int PF, int NS>
+__device__ __forceinline__ void stage1_body(const FfnArgs& a, uint16_t* __restrict__ h_out, const Fp8Ws& q,
                                             int mb, int nt, FfnSmem<BM>& sm) {
-    using TL = Tile<BM>;
+    using TL = Tile<TB>;
     using F = Fmt<kW>;
     uint8_t* lds = sm.lds;
-    int* arow = sm.arow;
-    float* rowscale = sm.rowscale;
+    const int* arow = sm.arow;
+    const float* rowscale = sm.rowscale;
     const int e = a.expert_ids[mb];
     const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
     const int H = a.H, I = a.I;
-    if (tid < BM) {
-        const int slot = a.sorted_ids[(int64_t)mb * BM + tid];
-        const bool ok = slot < a.S;
-        // row of x: the token, or (x already in the sorted order) the row itself
-        const int t = ok ? (a.rows_sorted ? mb * BM + tid : slot / a.K) : 0;
-        arow[tid] = ok ? t : -1;                          // -1 = padding
-        if (F::kQuantA) rowscale[tid] = ok ? q.sx[t] : 0.f;
-    }
-    __syncthreads();
-
     static_assert(NS == 2 || (NS == 4 && kW != kWFp4), "E2M1 scale words pair two row sets");
     const int n0 = nt * 64 * NS + w * 16 * NS;              // this wave's intermediate columns
     const int r32 = lane & 31;
@@ -568,10 +599,11 @@ __device__ __forceinline__ void stage1_tile(const FfnArgs& a, uint16_t* __restri
     zero_acc(acc);
     const uint8_t* xs = F::kQuantA ? (const uint8_t*)q.xq : (const uint8_t*)a.x;
     const int64_t xrow = F::kQuantA ? (int64_t)H : (int64_t)H * 2;
+    constexpr int LA = live_la<kW, BM, TB, PF>();
     if (stream_weights(a, mb, BM, e))
-        kloop<kW, kPacked, true, BM, NS, PF, ffn_la<kW, BM, PF>()>(xs, arow, xrow, brow, srow, nk, lds, acc);
+        kloop<kW, kPacked, true, TB, NS, PF, LA>(xs, arow, xrow, brow, srow, nk, lds, acc);
     else
-        kloop<kW, kPacked, false, BM, NS, PF, ffn_la<kW, BM, PF>()>(xs, arow, xrow, brow, srow, nk, lds, acc);
+        kloop<kW, kPacked, false, TB, NS, PF, LA>(xs, arow, xrow, brow, srow, nk, lds, acc);
 
 #pragma unroll
     for (int sub = 0; sub < NS / 2; ++sub) {
@@ -617,6 +649,37 @@ __device__ __forceinline__ void stage1_tile(const FfnArgs& a, uint16_t* __restri
                 }
             }
     }
+}
+
+// One gate/up tile: M block mb, intermediate columns [nt*64*NS, (nt+1)*64*NS).
+template <int kW, bool kPacked, int BM, int PF, int NS = 2>
+__device__ __forceinline__ void stage1_tile(const FfnArgs& a, uint16_t* __restrict__ h_out, const Fp8Ws& q,
+                                            int mb, int nt, FfnSmem<BM>& sm) {
+    using F = Fmt<kW>;
+    int* arow = sm.arow;
+    float* rowscale = sm.rowscale;
+    const int tid = threadIdx.x;
+    if (tid < BM) {
+        const int slot = a.sorted_ids[(int64_t)mb * BM + tid];
+        const bool ok = slot < a.S;
+        // row of x: the token, or (x already in the sorted order) the row itself
+        const int t = ok ? (a.rows_sorted ? mb * BM + tid : slot / a.K) : 0;
+        arow[tid] = ok ? t : -1;                          // -1 = padding
+        if (F::kQuantA) rowscale[tid] = ok ? q.sx[t] : 0.f;
+    }
+    __syncthreads();
+    // a tile whose block ends in whole 32-row subtiles of padding runs the
+    // smaller tile over its rows (the training forward saves every row's
+    // gate/up values, so it keeps the whole tile)
+    if constexpr (ffn_live_tiles<BM>()) {
+        const int live = a.save_gu ? Tile<BM>::MT : live_subtiles<BM>([&](int m) { return arow[m] >= 0; });
+        if (live <= 1) return stage1_body<kW, kPacked, BM, 32, live_pf<kW, 32>(), NS>(a, h_out, q, mb, nt, sm);
+        if constexpr (BM >= 128) {
+            if (live == 2) return stage1_body<kW, kPacked, BM, 64, live_pf<kW, 64>(), NS>(a, h_out, q, mb, nt, sm);
+            if (live == 3) return stage1_body<kW, kPacked, BM, 96, live_pf<kW, 96>(), NS>(a, h_out, q, mb, nt, sm);
+        }
+    }
+    stage1_body<kW, kPacked, BM, BM, PF, NS>(a, h_out, q, mb, nt, sm);
 }
 
 // Four row sets per wave hold 256 accumulator registers (all AGPRs) at the

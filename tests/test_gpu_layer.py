@@ -102,6 +102,28 @@ def test_layer_small_mxfp4_grouped_sigmoid():
         check_layer(cfg, L, np.arange(cfg["T"]), B=B, label=f"small mxfp4 decode B={B}")
 
 
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_fp8", "prefill_fp4"])
+def test_layer_blocks_ending_in_padding(name):
+    """Experts with 1, 33, 65, 97, 128 and 160 tokens: at block 128 their
+    blocks hold 1, 2, 3, 4, 4 and (4, 1) subtiles of 32 rows with a slot, at
+    block 64 (1, 2), ...; a block whose last subtiles are all padding is
+    computed as the smaller tile of its rows.  Every token against the oracle,
+    and the slot rows bit-identical to block 16's."""
+    dev = device()
+    counts = [1, 33, 65, 97, 128, 160]
+    cfg = ms.scaled(name, T=sum(counts), H=512, I=256, E=len(counts))
+    L = ms.make_layer(cfg, device=dev)
+    assign = np.repeat(np.arange(len(counts)), counts)[np.random.default_rng(7).permutation(cfg["T"])]
+    logits = torch.zeros(cfg["T"], cfg["E"], dtype=torch.float32)
+    logits[torch.arange(cfg["T"]), torch.from_numpy(assign)] = 8.0
+    L["logits"] = logits.to(dev)
+    ref_layer, _ = run_layer(cfg, L, 16)
+    y16 = ref_layer.y_slots.clone()
+    for B in (64, 128):
+        layer, _ = check_layer(cfg, L, None, B=B, label=f"{name} padded blocks B={B}")
+        assert torch.equal(layer.y_slots, y16), f"{name} B={B}: slot rows differ from block 16's"
+
+
 def test_ffn_output_is_block_size_invariant():
     dev = device()
     for name in ("decode_bf16", "prefill_fp8", "prefill_fp4"):

@@ -41,9 +41,13 @@ def check_rounding_and_combine(l32, l16, label):
     T, K = l16.topk_ids.shape
     ids = l16.topk_ids.cpu().numpy()
     w = l16.topk_weights.cpu().numpy().astype(np.float64)
-    y = l16.y_slots.float().cpu().numpy().astype(np.float64).reshape(T, K, -1)
     keep = ((ids >= 0) & (ids < l16.E_slabs)).astype(np.float64)
-    ref = np.einsum("tk,tkh->th", w * keep, np.where(keep[:, :, None] > 0, y, 0.0))
+    # rows of skipped slots are never written: only placed rows are read
+    yk = torch.zeros(T * K, l16.y_slots.shape[-1], dtype=torch.float32, device=l16.y_slots.device)
+    rows16 = placed_slots(l16)
+    yk[rows16] = l16.y_slots[rows16].float()
+    y = yk.cpu().numpy().astype(np.float64).reshape(T, K, -1)
+    ref = np.einsum("tk,tkh->th", w * keep, y)
     err = np.abs(out32.cpu().numpy() - ref).max() / max(np.abs(ref).max(), 1e-30)
     say(f"{label}: bf16 slot rows exact, combine rel err {err:.2e} against float64")
     assert err <= 1e-6, (label, err)
