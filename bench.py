@@ -678,9 +678,11 @@ def copy_probe(dev, reps=3):
 
 
 def hbm_probe(dev, nbytes=4 << 30, reps=10):
-    """Bandwidth a plain kernel reaches: a 16-byte-per-thread copy (reads and
-    writes nbytes/2 each) and a read-only stream of nbytes, event-timed,
-    best of `reps`."""
+    """Bandwidth plain kernels reach: a 16-byte-per-thread copy (reads and
+    writes nbytes/2 each), a grid-strided read of nbytes, and a read of nbytes
+    shaped like the GEMMs' weight stream (1 KB per wave load, 8 in flight,
+    non-temporal, a contiguous slab per workgroup) at several grid sizes;
+    event-timed, best of `reps`."""
     import ctypes
 
     import torch
@@ -692,6 +694,8 @@ def hbm_probe(dev, nbytes=4 << 30, reps=10):
     lib = ctypes.CDLL(hip_build.PROBE_LIB)
     for f in (lib.moe_probe_copy, lib.moe_probe_read):
         f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.moe_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.c_void_p]
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     half = nbytes // 2
     out = torch.empty(4096, dtype=torch.int32, device=dev)
@@ -704,7 +708,13 @@ def hbm_probe(dev, nbytes=4 << 30, reps=10):
              2 * half),
             ("read", lambda: lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()),
                                                 ctypes.c_void_p(out.data_ptr()), nbytes, stream),
-             nbytes)):
+             nbytes),
+            # 1 KB per wave load instruction, 8 in flight, non-temporal, one
+            # contiguous slab per workgroup (the GEMMs' weight stream)
+            *[(f"stream_{g}wg", (lambda g=g: lib.moe_probe_stream(ctypes.c_void_p(buf.data_ptr()),
+                                                                   ctypes.c_void_p(out.data_ptr()), nbytes, g,
+                                                                   stream)),
+               nbytes) for g in (512, 1024, 2048, 4096)]):
         call()
         torch.cuda.synchronize()
         for i in range(reps):

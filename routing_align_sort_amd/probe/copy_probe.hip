@@ -30,6 +30,42 @@ __global__ void __launch_bounds__(256) read_probe_kernel(const uint4* __restrict
     }
 }
 
+// Reads `n` 16-byte chunks once the way the grouped GEMMs stream their
+// weights: every load instruction of a wave reads 1 KB of consecutive bytes
+// (64 lanes x 16), each wave keeps 8 of them in flight, the loads are
+// non-temporal, and workgroup b walks the b-th contiguous slab.  Writes one
+// word per workgroup (an xor of everything read).
+typedef unsigned int u32x4_probe_t __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) stream_probe_kernel(const uint4* __restrict__ src,
+                                                           uint32_t* __restrict__ out, int64_t n) {
+    constexpr int kUnroll = 8;
+    constexpr int64_t kStep = 4 * kUnroll * 64;           // chunks per workgroup step
+    const int64_t per = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t slab = (per + kStep - 1) / kStep * kStep;
+    const int64_t begin = (int64_t)blockIdx.x * slab;
+    const int64_t end = begin + slab < n ? begin + slab : n;
+    const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+    uint32_t acc = 0;
+    for (int64_t i = begin + (int64_t)w * kUnroll * 64 + lane; i < end; i += kStep) {
+        u32x4_probe_t v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = i + u * 64;
+            v[u] = j < end ? __builtin_nontemporal_load((const u32x4_probe_t*)(src + j)) : u32x4_probe_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int t = 0; t < 256; ++t) r ^= red[t];
+        out[blockIdx.x] = r;
+    }
+}
+
 extern "C" int moe_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
     if (!src || !dst || bytes % 16) return 1;
     const int64_t n = (int64_t)(bytes / 16);
@@ -43,6 +79,15 @@ extern "C" int moe_probe_read(const void* src, void* out, size_t bytes, void* st
     if (!src || !out || bytes % 16) return 1;
     const int64_t n = (int64_t)(bytes / 16);
     hipLaunchKernelGGL(read_probe_kernel, dim3(4096), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       (const uint4*)src, (uint32_t*)out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+// out must hold `blocks` words (blocks <= 65536).
+extern "C" int moe_probe_stream(const void* src, void* out, size_t bytes, int blocks, void* stream) {
+    if (!src || !out || bytes % 16 || blocks <= 0 || blocks > 65536) return 1;
+    const int64_t n = (int64_t)(bytes / 16);
+    hipLaunchKernelGGL(stream_probe_kernel, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                        (const uint4*)src, (uint32_t*)out, n);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
