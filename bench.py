@@ -131,6 +131,23 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=
             layer.combine()
         torch.cuda.synchronize()
         wall_sep = time.perf_counter() - t0
+    # with E4M3 / MXFP4 weights the forward routes and quantises x in one
+    # launch; the same steps with the quantisation inside the FFN call
+    wall_quant_in_ffn = float("nan")
+    if layer.route_quant:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            xs, ls = inputs[s % rotate]
+            layer.route(ls, bias)
+            layer.align()
+            if layer.top1:
+                layer.ffn_top1(xs)
+            else:
+                layer.ffn(xs)
+                layer.combine()
+        torch.cuda.synchronize()
+        wall_quant_in_ffn = time.perf_counter() - t0
     # 2. the same four calls captured once in a HIP graph and replayed
     wall_graph = float("nan")
     if graph:
@@ -179,6 +196,7 @@ def run_layer_timed(cfg, B, steps, warmup, dev, seed=0, rows="by_token", rotate=
     res = {
         "wall_s": wall,
         "wall_sep_s": wall_sep,
+        "wall_quant_in_ffn_s": wall_quant_in_ffn,
         "wall_graph_s": wall_graph,
         "us": {n: _mean(v) for n, v in per.items()},
         "us_step_events": _mean(total),
@@ -207,6 +225,10 @@ def summarize(cfg, B, r):
         "graph_us_per_step": r["wall_graph_s"] / steps * 1e6 if r["wall_graph_s"] == r["wall_graph_s"] else None,
         "us_per_step_ffn_then_combine": (r["wall_sep_s"] / steps * 1e6 if r["wall_sep_s"] == r["wall_sep_s"]
                                          else None),
+        # E4M3 / MXFP4: the steps with the activation quantisation in the FFN
+        # call instead of in the routing launch
+        "us_per_step_quant_in_ffn": (r["wall_quant_in_ffn_s"] / steps * 1e6
+                                     if r["wall_quant_in_ffn_s"] == r["wall_quant_in_ffn_s"] else None),
         "event_timed_us_per_step": r["us_step_events"],
         "us": {k: round(v, 2) for k, v in us.items()},
         "experts_hit": ab["experts_hit"],
@@ -313,7 +335,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_bf16")
     ap.add_argument("--B", type=int, default=None)
     ap.add_argument("--rows", default="by_token", choices=("by_token", "sorted"),

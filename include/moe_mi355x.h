@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 typedef enum {
     MOE_OK = 0,
@@ -277,6 +277,9 @@ typedef struct {
     int32_t schedule;          /* moe_schedule_t */
     int32_t grad_dtype;        /* moe_dtype_t of moe_ffn_backward's dw13 and dw2: MOE_F32 (0) or MOE_BF16 */
     int32_t y_dtype;           /* moe_dtype_t of y_slots: MOE_F32 (0) or MOE_BF16 */
+    int32_t x_quantized;       /* 1: the workspace already holds x's E4M3 codes and
+                                  scales, written by moe_route_topk_quantize with
+                                  these same parameters; 0: quantised here */
 } moe_ffn_params_t;
 
 int64_t moe_grouped_ffn_workspace_bytes(const moe_ffn_params_t *p);
@@ -285,6 +288,31 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t *p, const void *x, const voi
                              const int32_t *sorted_token_ids, const int32_t *expert_ids,
                              const int32_t *num_tokens_post_padded, void *y_slots,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_route_topk and the per-token activation quantisation of moe_grouped_ffn
+ * (E4M3 and E2M1 weights) in one launch.  The two steps are independent: the
+ * routing reads the logits, the quantisation reads x.  Launched together they
+ * run side by side, and the FFN call then starts with its gate/up GEMM.  The
+ * quantisation is the one moe_grouped_ffn runs: per token,
+ *   s[t] = max_h |x[t,h]| / 448 (1 when the row is zero),
+ *   code = E4M3 nearest-even of x[t,h] * (448 / max_h |x[t,h]|), saturated,
+ * the a8w8 per-token activation mode of the aiter issue ("[Feature]: Add more
+ * configuration options for MoE assembly kernels", "Suggestion Description").
+ * rp, logits, bias, topk_ids, topk_weights as for moe_route_topk.  fp, x,
+ * workspace as for the moe_grouped_ffn (or moe_grouped_ffn_top1) call that
+ * follows, which must pass the same fp with fp->x_quantized = 1 and the same
+ * workspace, and must run after this call (same stream, or ordered by the
+ * caller).  Requires fp->w_dtype MOE_FP8_E4M3 or MOE_FP4_E2M1, fp->x_dtype
+ * MOE_BF16, MOE_ROWS_BY_TOKEN and fp->T == rp->T (else MOE_ERR_INVALID_ARG);
+ * workspace at least moe_grouped_ffn_workspace_bytes(fp) (else
+ * MOE_ERR_WORKSPACE).  The codes, scales and the FFN's cleared row-amax
+ * buffer go to the workspace; nothing else is written there.  T = 0 is a
+ * no-op.
+ */
+moe_status_t moe_route_topk_quantize(const moe_route_params_t *rp, const float *logits, const float *bias,
+                                     int32_t *topk_ids, float *topk_weights, const moe_ffn_params_t *fp,
+                                     const void *x, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * moe_grouped_ffn followed by moe_combine for top-1 routing, in one call.  The

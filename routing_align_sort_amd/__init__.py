@@ -42,7 +42,7 @@ class _FfnParams(ctypes.Structure):
                 ("w_dtype", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
                 ("weight_layout", ctypes.c_int32), ("row_layout", ctypes.c_int32),
                 ("schedule", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
-                ("y_dtype", ctypes.c_int32)]
+                ("y_dtype", ctypes.c_int32), ("x_quantized", ctypes.c_int32)]
 
 
 EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align_sort_capacity",
@@ -51,7 +51,7 @@ EXPORTED = ("moe_abi_version", "moe_status_string", "moe_route_topk", "moe_align
             "moe_prepack_block_scales", "moe_combine", "moe_combine_slots", "moe_permute_rows", "moe_unpermute_combine",
             "moe_unpermute_combine_backward", "moe_ffn_backward_workspace_bytes", "moe_ffn_backward",
             "moe_grouped_ffn_train", "moe_route_backward", "moe_align_sort_noalloc",
-            "moe_align_sort_noalloc_scratch_bytes")
+            "moe_align_sort_noalloc_scratch_bytes", "moe_route_topk_quantize")
 
 
 def load_library(path: str = LIB_PATH):
@@ -68,6 +68,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_route_topk.argtypes = [ctypes.POINTER(_RouteParams), P, P, P, P, P]
     lib.moe_route_topk.restype = i32
+    lib.moe_route_topk_quantize.argtypes = [ctypes.POINTER(_RouteParams), P, P, P, P, ctypes.POINTER(_FfnParams),
+                                            P, P, sz, P]
+    lib.moe_route_topk_quantize.restype = i32
     lib.moe_align_sort_capacity.argtypes = [i32, i32, i32, i32]
     lib.moe_align_sort_capacity.restype = i64
     lib.moe_align_sort_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -166,6 +169,42 @@ def moe_route_topk(logits, K, *, score="softmax", bias=None, n_group=1, topk_gro
                      int(bool(renormalize)), float(routed_scaling), int(bool(append_shared)))
     _check("moe_route_topk", lib.moe_route_topk(ctypes.byref(p), _ptr(logits), _ptr(bias),
                                                 _ptr(topk_ids), _ptr(topk_weights), _stream(stream)))
+    return topk_ids, topk_weights
+
+
+def moe_route_topk_quantize(logits, K, x, workspace, *, w13, B, K_ffn=None, score="softmax", bias=None,
+                            n_group=1, topk_group=1, renormalize=True, routed_scaling=1.0,
+                            append_shared=False, fused=False, topk_ids=None, topk_weights=None, stream=None):
+    """moe_route_topk, plus the per-token E4M3 quantisation of bf16 ``x`` into
+    ``workspace`` (the moe_grouped_ffn workspace of E4M3 or MXFP4 weights
+    ``w13`` at block size B), in one launch.  The FFN call that follows passes
+    the same workspace with x_quantized=True.  K_ffn: slots per token of that
+    FFN call (K, plus one with append_shared).  Returns (topk_ids, topk_weights)."""
+    lib = load_library()
+    T, E = logits.shape
+    _need(logits, torch.float32, "logits")
+    _need(x, torch.bfloat16, "x")
+    if bias is not None:
+        _need(bias, torch.float32, "bias", E)
+    KO = K + (1 if append_shared else 0)
+    if K_ffn is None:
+        K_ffn = KO
+    if topk_ids is None:
+        topk_ids = torch.empty((T, KO), dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, KO), dtype=torch.float32, device=logits.device)
+    _need(topk_ids, torch.int32, "topk_ids", T * KO)
+    _need(topk_weights, torch.float32, "topk_weights", T * KO)
+    Ew, I, H = weight_dims(w13)
+    if tuple(x.shape) != (T, H):
+        raise ValueError("x must be [T, H]")
+    rp = _RouteParams(T, E, K, {"softmax": 0, "sigmoid": 1}[score], n_group, topk_group,
+                      int(bool(renormalize)), float(routed_scaling), int(bool(append_shared)))
+    fp = _ffn_params(T, K_ffn, Ew, H, I, B, w13.dtype, torch.bfloat16, fused=fused, x_quantized=True)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("moe_route_topk_quantize", lib.moe_route_topk_quantize(
+        ctypes.byref(rp), _ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(topk_weights), ctypes.byref(fp),
+        _ptr(x), _ptr(workspace), ws_bytes, _stream(stream)))
     return topk_ids, topk_weights
 
 
@@ -268,12 +307,12 @@ MOE_SCHEDULE_TWO_LAUNCH, MOE_SCHEDULE_FUSED = 0, 1
 
 
 def _ffn_params(T, K, E, H, I, B, w_dtype, x_dtype, packed=False, rows_sorted=False, fused=False,
-                grad_dtype=torch.float32, y_dtype=torch.float32):
+                grad_dtype=torch.float32, y_dtype=torch.float32, x_quantized=False):
     return _FfnParams(T, K, E, H, I, B, _DT[w_dtype], _DT[x_dtype],
                       MOE_LAYOUT_PACKED if packed else MOE_LAYOUT_CANONICAL,
                       MOE_ROWS_SORTED if rows_sorted else MOE_ROWS_BY_TOKEN,
                       MOE_SCHEDULE_FUSED if fused else MOE_SCHEDULE_TWO_LAUNCH, _DT[grad_dtype],
-                      _DT[y_dtype])
+                      _DT[y_dtype], int(bool(x_quantized)))
 
 
 def moe_prepack_weights(w13, w2, *, stream=None):
@@ -317,7 +356,7 @@ def moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w_dtype, x_dtype, rows_sor
 
 def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, *, K, B,
                     w13_scale=None, w2_scale=None, y_slots=None, workspace=None, stream=None,
-                    stage_events=None, packed=False, T=None, fused=False, y_dtype=None):
+                    stage_events=None, packed=False, T=None, fused=False, y_dtype=None, x_quantized=False):
     """Grouped SwiGLU expert FFN over the sorted layout; returns y_slots [T*K, H],
     fp32, or bf16 (rounded to nearest even) with y_dtype=torch.bfloat16 or a
     bf16 y_slots given (not with fp32 weights or rows in the sorted order).
@@ -327,7 +366,9 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     order (row layout MOE_ROWS_SORTED).
     fused: both GEMMs in one persistent launch (schedule MOE_SCHEDULE_FUSED).
     stage_events: optional 5 raw hipEvent_t handles (ints) recorded at the stage
-    boundaries (the profiling entry point)."""
+    boundaries (the profiling entry point).
+    x_quantized: the workspace already holds x's E4M3 codes and scales from
+    moe_route_topk_quantize (E4M3 / MXFP4 weights, rows by token)."""
     lib = load_library()
     rows_sorted = T is not None
     Tx, H = x.shape
@@ -361,7 +402,8 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
     if y_slots is None:
         y_slots = torch.empty((ny, H), dtype=y_dtype, device=x.device)
     _need(y_slots, y_dtype, "y_slots", ny * H)
-    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed, rows_sorted, fused, y_dtype=y_dtype)
+    p = _ffn_params(T, K, E, H, I, B, w13.dtype, x.dtype, packed, rows_sorted, fused, y_dtype=y_dtype,
+                    x_quantized=x_quantized)
     need = moe_grouped_ffn_workspace_bytes(T, K, E, H, I, B, w13.dtype, x.dtype, rows_sorted, fused)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -379,7 +421,7 @@ def moe_grouped_ffn(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_pa
 
 def moe_grouped_ffn_top1(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_post_padded, topk_ids,
                          topk_weights, *, B, w13_scale=None, w2_scale=None, out_dtype=torch.bfloat16,
-                         out=None, workspace=None, stream=None, packed=False):
+                         out=None, workspace=None, stream=None, packed=False, x_quantized=False):
     """moe_grouped_ffn + moe_combine for top-1 routing in one call: out[t] =
     w[t] * FFN(x[t]) (zero rows for ids outside [0,E)); same bits as the two calls."""
     lib = load_library()
@@ -406,7 +448,7 @@ def moe_grouped_ffn_top1(x, w13, w2, sorted_token_ids, expert_ids, num_tokens_po
     if out is None:
         out = torch.empty((T, H), dtype=out_dtype, device=x.device)
     _need(out, out_dtype, "out", T * H)
-    p = _ffn_params(T, 1, E, H, I, B, w13.dtype, x.dtype, packed, False, False)
+    p = _ffn_params(T, 1, E, H, I, B, w13.dtype, x.dtype, packed, False, False, x_quantized=x_quantized)
     need = moe_grouped_ffn_workspace_bytes(T, 1, E, H, I, B, w13.dtype, x.dtype, False, False)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -659,7 +701,7 @@ class MoELayer:
                  renormalize=True, routed_scaling=1.0, shared=False, w13_scale=None,
                  w2_scale=None, x_dtype=torch.bfloat16, out_dtype=torch.bfloat16, packed=None,
                  rows="by_token", schedule="two_launch", top1="auto", train=False,
-                 grad_dtype=torch.float32, slot_dtype=torch.float32):
+                 grad_dtype=torch.float32, slot_dtype=torch.float32, route_quant="auto"):
         dev = w13.device
         if packed is None:
             packed = w13.dtype != torch.float32
@@ -729,10 +771,25 @@ class MoELayer:
                 raise ValueError("train needs bf16 weights, rows by token and two launches")
             self.gate_up = torch.empty((C, 2 * I), dtype=torch.float32, device=dev)
         self._gu_current = False
+        # E4M3 / MXFP4 weights with token rows: the forward routes and
+        # quantises the activations in one launch (moe_route_topk_quantize)
+        quant_ok = w13.dtype in (torch.float8_e4m3fn, FP4) and not self.rows_sorted and x_dtype == torch.bfloat16
+        if route_quant not in ("auto", True, False):
+            raise ValueError("route_quant must be 'auto', True or False")
+        if route_quant is True and not quant_ok:
+            raise ValueError("route_quant needs E4M3 or MXFP4 weights, bf16 x and rows by token")
+        self.route_quant = quant_ok and route_quant is not False
+        self.w_dtype = w13.dtype
 
     def route(self, logits, bias=None):
         return moe_route_topk(logits, self.K, bias=bias, topk_ids=self.topk_ids,
                               topk_weights=self.topk_weights, **self.route_kw)
+
+    def route_quantize(self, x, logits, bias=None):
+        """Routing and the activation quantisation of x into the FFN workspace, one launch."""
+        return moe_route_topk_quantize(logits, self.K, x, self.ws_ffn, w13=self.w13, B=self.B, K_ffn=self.KO,
+                                       bias=bias, fused=self.fused, topk_ids=self.topk_ids,
+                                       topk_weights=self.topk_weights, **self.route_kw)
 
     def align(self):
         return moe_align_sort(self.topk_ids, self.E_slabs, self.B, sorted_token_ids=self.sorted,
@@ -743,7 +800,7 @@ class MoELayer:
         return moe_permute_rows(x, self.topk_ids, self.sorted, self.ntpp, self.E_slabs, self.B,
                                 x_perm=self.x_perm, row_of_slot=self.row_of_slot)
 
-    def ffn(self, x, stage_events=None):
+    def ffn(self, x, stage_events=None, x_quantized=False):
         self._y_current = True
         self._gu_current = False
         if self.rows_sorted:
@@ -755,7 +812,8 @@ class MoELayer:
         return moe_grouped_ffn(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
                                K=self.KO, B=self.B, w13_scale=self.w13_scale,
                                w2_scale=self.w2_scale, y_slots=self.y_slots, workspace=self.ws_ffn,
-                               stage_events=stage_events, packed=self.packed, fused=self.fused)
+                               stage_events=stage_events, packed=self.packed, fused=self.fused,
+                               x_quantized=x_quantized)
 
     def fused_status(self):
         """The one-stage schedule's status word (0 = every wait was satisfied); syncs."""
@@ -778,14 +836,14 @@ class MoELayer:
                                      B=self.B, y_slots=self.y_slots, gate_up=self.gate_up,
                                      workspace=self.ws_ffn, packed=self.packed)
 
-    def ffn_top1(self, x):
+    def ffn_top1(self, x, x_quantized=False):
         """The FFN and the combine of a top-1 layer in one call (into self.out)."""
         self._y_current = False
         self._gu_current = False
         return moe_grouped_ffn_top1(x, self.w13, self.w2, self.sorted, self.expert_ids, self.ntpp,
                                     self.topk_ids, self.topk_weights, B=self.B, w13_scale=self.w13_scale,
                                     w2_scale=self.w2_scale, out_dtype=self.out_dtype, out=self.out,
-                                    workspace=self.ws_ffn, packed=self.packed)
+                                    workspace=self.ws_ffn, packed=self.packed, x_quantized=x_quantized)
 
     def backward(self, x, logits, d_out, workspace=None, recompute=False):
         """Gradients after forward(x, logits): (dx, dw13, dw2, d_logits), fp32.
@@ -808,16 +866,19 @@ class MoELayer:
         return dx, dw13, dw2, d_logits, dwk
 
     def forward(self, x, logits, bias=None):
-        self.route(logits, bias)
+        if self.route_quant:
+            self.route_quantize(x, logits, bias)
+        else:
+            self.route(logits, bias)
         self.align()
         if self.rows_sorted:
             self.permute(x)
         if self.top1:
-            return self.ffn_top1(x)
+            return self.ffn_top1(x, x_quantized=self.route_quant)
         if self.train:
             self.ffn_train(x)
         else:
-            self.ffn(x)
+            self.ffn(x, x_quantized=self.route_quant)
         return self.combine()
 
 

@@ -42,23 +42,34 @@ const char* moe_status_string(int32_t s) {
     }
 }
 
-moe_status_t moe_route_topk(const moe_route_params_t* p, const float* logits, const float* bias,
-                            int32_t* topk_ids, float* topk_weights, void* stream) {
+static moe_status_t route_check(const moe_route_params_t* p) {
     if (!p) return MOE_ERR_INVALID_ARG;
     if (p->T < 0 || p->E < 1 || p->K < 1 || p->n_group < 1 || p->topk_group < 1 ||
         p->topk_group > p->n_group || p->E % p->n_group != 0 ||
         p->K > p->topk_group * (p->E / p->n_group) || (p->score != MOE_SCORE_SOFTMAX && p->score != MOE_SCORE_SIGMOID))
         return MOE_ERR_INVALID_ARG;
     if (p->E > kRouteMaxExperts || p->K > kRouteMaxK || p->n_group > kRouteMaxGroups) return MOE_ERR_UNSUPPORTED;
-    if (p->T == 0) return MOE_OK;
-    if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+static RouteArgs route_args(const moe_route_params_t* p, const float* logits, const float* bias,
+                            int32_t* topk_ids, float* topk_weights) {
     RouteArgs a;
     a.T = p->T; a.E = p->E; a.K = p->K; a.score = p->score;
     a.n_group = p->n_group; a.topk_group = p->topk_group;
     a.renormalize = p->renormalize != 0; a.append_shared = p->append_shared != 0;
     a.routed_scaling = p->routed_scaling;
     a.logits = logits; a.bias = bias; a.topk_ids = topk_ids; a.topk_weights = topk_weights;
-    return from_hip(launch_route_topk(a, as_stream(stream)));
+    return a;
+}
+
+moe_status_t moe_route_topk(const moe_route_params_t* p, const float* logits, const float* bias,
+                            int32_t* topk_ids, float* topk_weights, void* stream) {
+    const moe_status_t st = route_check(p);
+    if (st != MOE_OK) return st;
+    if (p->T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARG;
+    return from_hip(launch_route_topk(route_args(p, logits, bias, topk_ids, topk_weights), as_stream(stream)));
 }
 
 int64_t moe_align_sort_capacity(int32_t T, int32_t K, int32_t E, int32_t B) {
@@ -128,6 +139,9 @@ static moe_status_t ffn_check(const moe_ffn_params_t* p) {
     // bf16 slot rows: the matrix-core paths, rows by slot
     if (p->y_dtype != MOE_F32 && p->y_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->y_dtype == MOE_BF16 && (f32 || p->row_layout != MOE_ROWS_BY_TOKEN)) return MOE_ERR_UNSUPPORTED;
+    // activations quantised by moe_route_topk_quantize: E4M3 codes of x by token
+    if (p->x_quantized != 0 && p->x_quantized != 1) return MOE_ERR_INVALID_ARG;
+    if (p->x_quantized && (!(fp8 || fp4) || p->row_layout != MOE_ROWS_BY_TOKEN)) return MOE_ERR_INVALID_ARG;
     if (!f32) {
         // the matrix-core kernels address each GEMM's activation operand
         // (x, then the intermediate) with 32-bit byte offsets
@@ -194,7 +208,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     const int64_t S = (int64_t)p->T * p->K;
     const int64_t C = capacity(S, p->E, p->B);
     if (S == 0) return MOE_OK;
-    if (!x || !w13 || !w2 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded ||
+    if ((!x && !p->x_quantized) || !w13 || !w2 || !sorted_token_ids || !expert_ids || !num_tokens_post_padded ||
         (!y_slots && !top1.out))
         return MOE_ERR_INVALID_ARG;
     if ((p->w_dtype == MOE_FP8_E4M3 || p->w_dtype == MOE_FP4_E2M1) && (!w13_scale || !w2_scale))
@@ -214,6 +228,7 @@ static moe_status_t grouped_ffn(const moe_ffn_params_t* p, const void* x, const 
     a.fused = p->schedule == MOE_SCHEDULE_FUSED;
     a.top1_w = top1.w; a.top1_ids = top1.ids; a.top1_out = top1.out; a.top1_bf16 = top1.bf16;
     a.save_gu = save_gu;
+    a.x_quantized = p->x_quantized;
     hipError_t e;
     if (p->w_dtype == MOE_F32) e = launch_ffn_f32(a, workspace, as_stream(stream), ev);
     else if (p->w_dtype == MOE_BF16) e = launch_ffn_bf16(a, workspace, as_stream(stream), ev);
@@ -230,6 +245,25 @@ moe_status_t moe_grouped_ffn(const moe_ffn_params_t* p, const void* x, const voi
     return grouped_ffn(p, x, w13, w13_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                        num_tokens_post_padded, y_slots, Top1Out{}, nullptr, workspace, workspace_bytes, stream,
                        nullptr);
+}
+
+moe_status_t moe_route_topk_quantize(const moe_route_params_t* rp, const float* logits, const float* bias,
+                                     int32_t* topk_ids, float* topk_weights, const moe_ffn_params_t* fp,
+                                     const void* x, void* workspace, size_t workspace_bytes, void* stream) {
+    moe_status_t st = route_check(rp);
+    if (st != MOE_OK) return st;
+    if ((st = ffn_check(fp)) != MOE_OK) return st;
+    if ((fp->w_dtype != MOE_FP8_E4M3 && fp->w_dtype != MOE_FP4_E2M1) || fp->row_layout != MOE_ROWS_BY_TOKEN ||
+        fp->T != rp->T)
+        return MOE_ERR_INVALID_ARG;
+    if (rp->T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights || !x) return MOE_ERR_INVALID_ARG;
+    const int64_t C = capacity((int64_t)fp->T * fp->K, fp->E, fp->B);
+    const int64_t need = ffn_workspace_bytes(fp->w_dtype, fp->T, fp->H, fp->I, C, fp->schedule == MOE_SCHEDULE_FUSED);
+    if (!workspace || (int64_t)workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    const QuantArgs q = ffn_quant_args(workspace, x, fp->T, fp->H, fp->I, C);
+    return from_hip(
+        launch_route_quant(route_args(rp, logits, bias, topk_ids, topk_weights), q, as_stream(stream)));
 }
 
 moe_status_t moe_grouped_ffn_train(const moe_ffn_params_t* p, const void* x, const void* w13, const void* w2,

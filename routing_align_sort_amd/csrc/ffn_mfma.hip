@@ -44,6 +44,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "quant.hpp"
 
 namespace moe {
 
@@ -975,94 +976,11 @@ ffn_stage2(FfnArgs a, const uint8_t* __restrict__ h_in, const float* __restrict_
 }
 
 // --------------------------------------------------------- fp8 quantisation --
-// E4M3 code of v (OCP, nearest even); |v| <= 448 by construction (clamped).
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
-    a = fminf(fmaxf(a, -448.f), 448.f);
-    b = fminf(fmaxf(b, -448.f), 448.f);
-    c = fminf(fmaxf(c, -448.f), 448.f);
-    d = fminf(fmaxf(d, -448.f), 448.f);
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
-    return (uint32_t)r;
-}
-
-constexpr int kQuantThreads = 256;
-constexpr int kQuantCache = 4;          // 16-byte chunks of a row a thread keeps in registers
-
-__device__ __forceinline__ float block_max(float v, float* lds4) {
-    v = wave_max_f32(v);
-    const int w = threadIdx.x / kWave;
-    if (lane_id() == 0) lds4[w] = v;
-    __syncthreads();
-    float m = lds4[0];
-#pragma unroll
-    for (int i = 1; i < kQuantThreads / kWave; ++i) m = fmaxf(m, lds4[i]);
-    return m;
-}
-
-// One workgroup per token: x bf16 row -> E4M3 codes + scale.  Also clears the
-// per-row amax of the intermediate for stage 1.
+// One workgroup per token: x bf16 row -> E4M3 codes + scale (quant.hpp).
 __global__ void __launch_bounds__(kQuantThreads)
 quant_tokens_kernel(const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq, float* __restrict__ sx,
                     uint32_t* __restrict__ amax_rows, int64_t C) {
-    __shared__ float red[kQuantThreads / kWave];
-    const int t = blockIdx.x, tid = threadIdx.x;
-    for (int64_t r = (int64_t)t * kQuantThreads + tid; r < C; r += (int64_t)gridDim.x * kQuantThreads)
-        amax_rows[r] = 0u;
-    const uint16_t* row = x + (int64_t)t * H;
-    // rows up to kQuantCache * 8 * kQuantThreads elements stay in registers
-    // between the amax and the encoding (one read of the row); longer rows
-    // are read twice
-    uint4 cache[kQuantCache];
-    const bool cached = H <= kQuantCache * 8 * kQuantThreads;
-    float m = 0.f;
-    auto absmax8 = [&](const uint4 v) {
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(wv[j] & 0xFFFF))));
-            m = fmaxf(m, fabsf(bf16_bits_to_f32((uint16_t)(wv[j] >> 16))));
-        }
-    };
-    if (cached) {
-#pragma unroll
-        for (int c = 0; c < kQuantCache; ++c) {
-            const int h = (tid + c * kQuantThreads) * 8;
-            cache[c] = h < H ? *(const uint4*)(row + h) : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int c = 0; c < kQuantCache; ++c) absmax8(cache[c]);
-    } else {
-        for (int h = tid * 8; h < H; h += kQuantThreads * 8) absmax8(*(const uint4*)(row + h));
-    }
-    m = block_max(m, red);
-    const float inv = (m > 0.f) ? 448.0f / m : 0.f;
-    if (tid == 0) sx[t] = (m > 0.f) ? m / 448.0f : 1.0f;
-    auto encode8 = [&](const uint4 v, int h) {
-        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-        float f[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[2 * j] = bf16_bits_to_f32((uint16_t)(wv[j] & 0xFFFF)) * inv;
-            f[2 * j + 1] = bf16_bits_to_f32((uint16_t)(wv[j] >> 16)) * inv;
-        }
-        uint2 o;
-        o.x = e4m3_pack4(f[0], f[1], f[2], f[3]);
-        o.y = e4m3_pack4(f[4], f[5], f[6], f[7]);
-        // non-temporal: the gate/up GEMM that reads the codes next streams
-        // faster when this kernel leaves no dirty lines behind (8% at 64
-        // tokens per expert)
-        __builtin_nontemporal_store(u32x2_t{o.x, o.y}, (u32x2_t*)(xq + (int64_t)t * H + h));
-    };
-    if (cached) {
-#pragma unroll
-        for (int c = 0; c < kQuantCache; ++c) {
-            const int h = (tid + c * kQuantThreads) * 8;
-            if (h < H) encode8(cache[c], h);
-        }
-    } else {
-        for (int h = tid * 8; h < H; h += kQuantThreads * 8) encode8(*(const uint4*)(row + h), h);
-    }
+    quant_token_row(x, H, xq, sx, amax_rows, C, blockIdx.x, gridDim.x);
 }
 
 // Row r of the fp32 intermediate -> E4M3 codes + scale, by a workgroup of
@@ -1333,6 +1251,11 @@ static Fp8Ws fp8_ws(void* ws, int64_t T, int64_t H, int64_t I, int64_t C) {
     return q;
 }
 
+QuantArgs ffn_quant_args(void* ws, const void* x, int64_t T, int64_t H, int64_t I, int64_t C) {
+    const Fp8Ws q = fp8_ws(ws, T, H, I, C);
+    return QuantArgs{static_cast<const uint16_t*>(x), (int)H, q.xq, q.sx, q.amax, C};
+}
+
 template <int kW, bool kPacked, int BM>
 static hipError_t launch_fused_bm(const FfnArgs& a, void* ws, hipStream_t stream, hipEvent_t const* ev,
                                   int w_dtype) {
@@ -1346,7 +1269,7 @@ static hipError_t launch_fused_bm(const FfnArgs& a, void* ws, hipStream_t stream
     if ((err = record_stage(ev, 0, stream)) != hipSuccess) return err;
     if (kQuant) {
         q = fp8_ws(ws, xrows, a.H, a.I, a.C);
-        if (xrows > 0)
+        if (xrows > 0 && !a.x_quantized)
             hipLaunchKernelGGL(quant_tokens_kernel, dim3((unsigned)xrows), dim3(kQuantThreads), 0, stream,
                                (const uint16_t*)a.x, a.H, q.xq, q.sx, q.amax, a.C);
         if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1405,7 +1328,7 @@ static hipError_t launch_two_stage(const FfnArgs& a, void* ws, hipStream_t strea
     if (kQuant) {
         const int64_t xrows = a.rows_sorted ? a.C : a.T;         // rows of x
         q = fp8_ws(ws, xrows, a.H, a.I, a.C);
-        if (xrows > 0)
+        if (xrows > 0 && !a.x_quantized)
             hipLaunchKernelGGL(quant_tokens_kernel, dim3((unsigned)xrows), dim3(kQuantThreads), 0, stream,
                                (const uint16_t*)a.x, a.H, q.xq, q.sx, q.amax, a.C);
         if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -20,6 +20,18 @@ struct RouteArgs {
     float* topk_weights;
 };
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t stream);
+// Per-token E4M3 quantisation of x into the FFN's workspace (codes, scales),
+// with the per-row amax of the intermediate cleared (C rows).
+struct QuantArgs {
+    const uint16_t* x;         // bf16 [T,H]
+    int H;
+    uint8_t* xq;               // [T,H]
+    float* sx;                 // [T]
+    uint32_t* amax;            // [C]
+    int64_t C;
+};
+// Routing and the quantisation of the same T tokens in one launch.
+hipError_t launch_route_quant(const RouteArgs& a, const QuantArgs& q, hipStream_t stream);
 
 // ------------------------------------------------------------- align&sort --
 constexpr int kAlignMaxExperts = 1024;
@@ -73,7 +85,12 @@ struct FfnArgs {
     // sorted row r are written to save_gu[r*2I + j] and [r*2I + I + j] for
     // rows below num_tokens_post_padded, for the backward; null otherwise.
     float* save_gu;
+    // the workspace already holds x's codes and scales and a cleared row
+    // amax (launch_route_quant): no quantisation launch
+    int x_quantized;
 };
+// The quantisation targets of an E4M3 / E2M1 FFN's workspace for T token rows.
+QuantArgs ffn_quant_args(void* ws, const void* x, int64_t T, int64_t H, int64_t I, int64_t C);
 // Largest activation operand (bytes of x, or of the intermediate, as one
 // GEMM reads it) of the matrix-core kernels: they address it with 32-bit
 // offsets.

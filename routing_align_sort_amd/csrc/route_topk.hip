@@ -13,6 +13,7 @@
 // double scores.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "quant.hpp"
 
 namespace moe {
 
@@ -43,12 +44,11 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // 64*JT >= E), so a token of E experts does E/64 lanes' worth of work, not
 // the 1024-expert maximum's.
 template <int JT>
-__global__ void __launch_bounds__(kRouteWaves* kWave)
-route_topk_kernel(RouteArgs a) {
+__device__ __forceinline__ void route_token_block(const RouteArgs& a, int block) {
     __shared__ float keys_lds[kRouteWaves][kRouteMaxExperts];
     const int w = threadIdx.x / kWave;
     const int lane = lane_id();
-    const int t = blockIdx.x * kRouteWaves + w;
+    const int t = block * kRouteWaves + w;
     if (t >= a.T) return;                       // whole wave leaves; no block barriers below
     const int E = a.E;
     static_assert(JT <= kRouteMaxPerLane && JT <= 32, "experts per lane");
@@ -193,6 +193,41 @@ route_topk_kernel(RouteArgs a) {
         a.topk_ids[(int64_t)t * KO + a.K] = E;
         a.topk_weights[(int64_t)t * KO + a.K] = 1.0f;
     }
+}
+
+template <int JT>
+__global__ void __launch_bounds__(kRouteWaves* kWave)
+route_topk_kernel(RouteArgs a) {
+    route_token_block<JT>(a, blockIdx.x);
+}
+
+// Routing and the per-token activation quantisation in one launch: the
+// first ceil(T/4) workgroups route four tokens each, the next T quantise one
+// token row each.  The two jobs are independent (both read their own inputs
+// only), so one launch runs them side by side instead of one after the other.
+static_assert(kQuantThreads == kRouteWaves * kWave, "one workgroup size for both jobs");
+template <int JT>
+__global__ void __launch_bounds__(kRouteWaves* kWave)
+route_quant_kernel(RouteArgs a, QuantArgs q) {
+    const int nr = (a.T + kRouteWaves - 1) / kRouteWaves;
+    if ((int)blockIdx.x < nr)
+        route_token_block<JT>(a, blockIdx.x);
+    else
+        quant_token_row(q.x, q.H, q.xq, q.sx, q.amax, q.C, (int)blockIdx.x - nr, (int)gridDim.x - nr);
+}
+
+hipError_t launch_route_quant(const RouteArgs& a, const QuantArgs& q, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    const int blocks = (a.T + kRouteWaves - 1) / kRouteWaves + a.T;
+    const int J = (a.E + kWave - 1) / kWave;
+    const dim3 g(blocks), b(kRouteWaves * kWave);
+    if (J <= 1) hipLaunchKernelGGL(route_quant_kernel<1>, g, b, 0, stream, a, q);
+    else if (J <= 2) hipLaunchKernelGGL(route_quant_kernel<2>, g, b, 0, stream, a, q);
+    else if (J <= 4) hipLaunchKernelGGL(route_quant_kernel<4>, g, b, 0, stream, a, q);
+    else if (J <= 8) hipLaunchKernelGGL(route_quant_kernel<8>, g, b, 0, stream, a, q);
+    else if (J <= kRouteMaxPerLane) hipLaunchKernelGGL(route_quant_kernel<kRouteMaxPerLane>, g, b, 0, stream, a, q);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t stream) {

@@ -30,14 +30,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     assert set(names) == set(moe.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 9
+    assert moe.abi_version() == 10
     assert moe.status_string(0) == "ok"
     assert "workspace" in moe.status_string(3)
     assert moe.status_string(99) == "unknown status"
@@ -323,3 +323,40 @@ def test_bf16_slot_rows_are_checked_on_the_host(lib):
     assert cs(4, 2, 8, 16, None, moe.MOE_BF16, P(8), P(8), moe.MOE_BF16, P(8), None) == moe.MOE_ERR_INVALID_ARG
     assert cs(0, 2, 8, 16, None, moe.MOE_BF16, None, None, moe.MOE_BF16, None, None) == moe.MOE_OK
     assert cs(4, 2, 8, 12, P(8), moe.MOE_F32, P(8), P(8), 5, P(8), None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_route_quantize_is_checked_on_the_host(lib):
+    # routing plus the activation quantisation of an E4M3 / MXFP4 FFN: the
+    # FFN's parameters must be a quantised-activation path with token rows
+    # and the routing's T, the workspace the FFN's; x_quantized is 0 or 1 and
+    # only for those paths
+    P = ctypes.c_void_p
+    rp = moe._RouteParams(64, 8, 2, 0, 1, 1, 1, 1.0, 0)
+    fp = moe._FfnParams(64, 2, 8, 256, 256, 16, moe.MOE_FP8_E4M3, moe.MOE_BF16, 0, moe.MOE_ROWS_BY_TOKEN, 0, 0,
+                        moe.MOE_F32, 1)
+    need = lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(fp))
+    assert need > 0
+    rq = lib.moe_route_topk_quantize
+    assert rq(ctypes.byref(rp), P(8), None, P(8), P(8), ctypes.byref(fp), P(8), P(8), need - 1, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert rq(ctypes.byref(rp), P(8), None, P(8), P(8), ctypes.byref(fp), None, P(8), need, None) == \
+        moe.MOE_ERR_INVALID_ARG                     # x missing
+    for field, value in (("T", 32), ("row_layout", moe.MOE_ROWS_SORTED)):
+        q = moe._FfnParams.from_buffer_copy(fp)
+        setattr(q, field, value)
+        assert rq(ctypes.byref(rp), P(8), None, P(8), P(8), ctypes.byref(q), P(8), P(8), 1 << 30, None) != \
+            moe.MOE_OK, (field, value)
+    q = moe._FfnParams.from_buffer_copy(fp)
+    q.w_dtype = q.x_dtype = moe.MOE_BF16
+    q.x_quantized = 0
+    assert rq(ctypes.byref(rp), P(8), None, P(8), P(8), ctypes.byref(q), P(8), P(8), 1 << 30, None) == \
+        moe.MOE_ERR_INVALID_ARG                     # bf16 weights read x as it is
+    q.x_quantized = 1
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(q)) == -1
+    q = moe._FfnParams.from_buffer_copy(fp)
+    q.x_quantized = 2
+    assert lib.moe_grouped_ffn_workspace_bytes(ctypes.byref(q)) == -1
+    rp0 = moe._RouteParams(0, 8, 2, 0, 1, 1, 1, 1.0, 0)
+    fp0 = moe._FfnParams.from_buffer_copy(fp)
+    fp0.T = 0
+    assert rq(ctypes.byref(rp0), None, None, None, None, ctypes.byref(fp0), None, None, 0, None) == moe.MOE_OK
