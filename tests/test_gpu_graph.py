@@ -20,9 +20,11 @@ def eager(layer, x, logits, bias):
     return out, layer.y_slots.clone(), layer.sorted.clone()
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8", "prefill_bf16"])
+@pytest.mark.parametrize("name", ["decode_bf16", "prefill_fp8", "prefill_bf16", "prefill_fp4"])
 def test_layer_graph_replays_match_eager(name):
-    # prefill_bf16 is top-1: its FFN and combine run as one call, with no slot rows
+    # prefill_bf16 and prefill_fp4 are top-1: their FFN and combine run as one
+    # call, with no slot rows; the fp8 and MXFP4 layers route and quantise x
+    # in one launch
     dev = device()
     if name == "decode_bf16":
         cfg = ms.scaled(name, T=96, H=512, I=256, E=16, K=4, n_group=4, topk_group=2)
