@@ -34,6 +34,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "e2m1": 5000.0, "f32": 157.3
 ESZ = {"f32": 4, "bf16": 2, "e4m3": 1, "e2m1": 0.5}
 DTYPE_NAME = {"f32": "f32", "bf16": "bf16", "e4m3": "fp8_e4m3", "e2m1": "fp8_e4m3 x mxfp4"}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+NUM_XCD = 8                                             # XCDs of an MI355X (one GRBM instance each)
 
 
 def layer_flops(slots: int, hidden: int, inter: int) -> int:
@@ -358,7 +359,14 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-probe run into the traffic record under profiles/ and exit")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PMC_DIR", "OUT_JSON"),
+                    help="reduce one rocprofv3 --pmc --kernel-trace output directory to per-kernel "
+                         "medians of every counter (moe:: kernels) with per-dispatch durations, "
+                         "write them as JSON and exit")
     args = ap.parse_args()
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq)
+        return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.workload,
                            args.B or None)
@@ -853,6 +861,46 @@ def _counter_rows(path):
     import csv
     with open(path) as f:
         return list(csv.DictReader(f))
+
+
+def summarize_sq(pmc_dir, out_json):
+    """Per-kernel medians over the dispatches of every counter in a rocprofv3
+    --pmc --kernel-trace run (counters summed over their instances), each
+    dispatch's duration from the kernel trace and its cycle count
+    (GRBM_GUI_ACTIVE is one instance per XCD, so cycles = its sum / 8)."""
+    import statistics
+    names, per, dur = {}, {}, {}
+    for r in _counter_rows(os.path.join(pmc_dir, "run_counter_collection.csv")):
+        name = r["Kernel_Name"].replace("void ", "", 1).split("(")[0]
+        if not name.startswith("moe::"):
+            continue
+        did = r["Dispatch_Id"]
+        names[did] = name
+        c = per.setdefault(did, {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    trace = os.path.join(pmc_dir, "run_kernel_trace.csv")
+    if os.path.exists(trace):
+        for r in _counter_rows(trace):
+            if r.get("Dispatch_Id") in names:
+                dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    by_kernel = {}
+    for did, name in names.items():
+        by_kernel.setdefault(name, []).append(did)
+    out = {}
+    for name, ids in by_kernel.items():
+        rec = {"dispatches": len(ids)}
+        for c in per[ids[0]]:
+            rec[c] = statistics.median(per[i][c] for i in ids)
+        timed = [i for i in ids if i in dur]
+        if timed:
+            rec["us_median"] = statistics.median(dur[i] for i in timed)
+            rec["per_dispatch_us_cycles"] = [(round(dur[i], 1), per[i].get("GRBM_GUI_ACTIVE", 0.0) / NUM_XCD)
+                                             for i in timed]
+        out[name] = rec
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"{out_json}: {sorted(out)}")
+
 
 
 def summarize_counters(fetch_csv, write_csv, workload, B):
