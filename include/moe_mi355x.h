@@ -178,6 +178,11 @@ moe_status_t moe_align_sort(const int32_t *topk_ids, int32_t T, int32_t K, int32
  * that overlap in time on one device (on different streams, or from
  * different host threads onto one device without ordering) race on it and
  * give wrong results; calls ordered on one stream are safe.
+ * The barrier status word of moe_align_sort lives in that array, where the
+ * caller cannot read it: a call whose barrier wait gives up returns MOE_OK
+ * with invalid results.  The barrier's counters still end at zero (every
+ * workgroup arrives at every phase whether or not its wait gave up), so the
+ * calls after it are unaffected.
  */
 int64_t moe_align_sort_noalloc_scratch_bytes(void);
 moe_status_t moe_align_sort_noalloc(const int32_t *topk_ids, int32_t T, int32_t K, int32_t E, int32_t B,
