@@ -360,8 +360,9 @@ def main():
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-probe run into the traffic record under profiles/ and exit")
     ap.add_argument("--summarize-sq", nargs=2, metavar=("PMC_DIR", "OUT_JSON"),
-                    help="reduce one rocprofv3 --pmc --kernel-trace output directory to per-kernel "
-                         "medians of every counter (moe:: kernels) with per-dispatch durations, "
+                    help="reduce one rocprofv3 --pmc output directory to per-kernel medians of every "
+                         "counter (the library's kernels and the copy probe), with per-dispatch "
+                         "durations when it also holds a kernel trace, "
                          "write them as JSON and exit")
     args = ap.parse_args()
     if args.summarize_sq:
@@ -865,14 +866,15 @@ def _counter_rows(path):
 
 def summarize_sq(pmc_dir, out_json):
     """Per-kernel medians over the dispatches of every counter in a rocprofv3
-    --pmc --kernel-trace run (counters summed over their instances), each
+    --pmc run (counters summed over their instances; the library's kernels and
+    the copy probe), and, when the run also took a kernel trace, each
     dispatch's duration from the kernel trace and its cycle count
     (GRBM_GUI_ACTIVE is one instance per XCD, so cycles = its sum / 8)."""
     import statistics
     names, per, dur = {}, {}, {}
     for r in _counter_rows(os.path.join(pmc_dir, "run_counter_collection.csv")):
         name = r["Kernel_Name"].replace("void ", "", 1).split("(")[0]
-        if not name.startswith("moe::"):
+        if not (name.startswith("moe::") or name.startswith("copy_probe_kernel")):
             continue
         did = r["Dispatch_Id"]
         names[did] = name
